@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 GEMM library on one MI355X.
+
+Headline (the step that is timed): one W4A16 GEMM at the decode workload
+M=1, N=17408, K=5120, group 128 (bf16 activations, packed int4 weights,
+fp32 accumulation, bf16 output), reported as effective weight bandwidth:
+(N*K/2 packed bytes + N*K/128*2 scale bytes) per step / time per step.
+
+All inputs are synthetic (seeded, see synth/gen.py) and resident in HBM
+before the timed region. Weights and scales are rotated over enough copies
+(>= 512 MB) that the 256 MB Infinity Cache cannot serve them from one step
+to the next. The other workloads (small-batch split-K decode, deep prefill,
+grouped) are measured the same way and reported under "workloads".
+
+Output: one JSON line on stdout. `--gpus N` with N > 1 exits with a message:
+the library is single-GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective weight GB/s at M=1 decode; TFLOP/s at M=1322 prefill (1x MI355X)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+ROTATE_BYTES = 512 << 20
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def eff_weight_bytes(N, K, G=1):
+    return G * (N * K // 2 + N * (K // 128) * 2)
+
+
+class Dev:
+    """Device copies of a workload, with `copies` rotated weight/scale sets."""
+
+    def __init__(self, c, copies=1):
+        import torch
+        import bf16_activation_quantized_amd as w4
+        d = torch.device("cuda:0")
+        self.x = torch.from_numpy(c.x.view(np.int16)).to(d).view(torch.bfloat16)
+        s = torch.from_numpy(c.s.view(np.int16)).to(d).view(torch.bfloat16)
+        q = torch.from_numpy(c.q).to(d)
+        w = w4.w4a16_pack_int4(q)
+        del q
+        self.w = [w] + [w.clone() for _ in range(copies - 1)]
+        self.s = [s] + [s.clone() for _ in range(copies - 1)]
+        self.m_sizes = None if c.m_sizes is None else torch.from_numpy(c.m_sizes).to(d)
+        torch.cuda.synchronize()
+
+
+def time_steps(step, steps, warmup):
+    """Runs `warmup` untimed steps, then `steps` timed steps, each bracketed
+    by events on the launch stream. Returns (total seconds, per-step
+    seconds list)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1) / 1e3
+    per = [a.elapsed_time(b) / 1e3 for a, b in ev]
+    return total, per
+
+
+def bench_decode(name, steps, warmup, split_k=0, path=None, variant=None):
+    import torch
+    import bf16_activation_quantized_amd as w4
+    from synth import make_config, CONFIGS
+    cfg = CONFIGS[name]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    wb = eff_weight_bytes(N, K)
+    copies = max(1, math.ceil(ROTATE_BYTES / wb))
+    c = make_config(name)
+    d = Dev(c, copies)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    need = w4.w4a16_gemm_workspace_bytes(M, N, K, split_k, path=path, variant=variant)
+    ws = torch.empty(max(need // 4, 1) + 4, dtype=torch.float32, device="cuda")
+    sk = split_k if split_k else w4.w4a16_gemm_auto_split_k(M, N, K)
+
+    def step(i):
+        j = i % copies
+        w4.w4a16_gemm(d.x, d.w[j], d.s[j], y=y, split_k=split_k, workspace=ws, path=path, variant=variant)
+
+    total, per = time_steps(step, steps, warmup)
+    t = total / steps
+    return dict(M=M, N=N, K=K, split_k=sk, weight_copies=copies, eff_weight_bytes=wb,
+                us_per_step=t * 1e6, us_per_launch_events=float(np.mean(per)) * 1e6,
+                gbs=wb / t / 1e9, frac_hbm=wb / t / 1e9 / HBM_PEAK_GBS), d, y
+
+
+def bench_prefill(name, steps, warmup, variant=None):
+    import torch
+    import bf16_activation_quantized_amd as w4
+    from synth import make_config, CONFIGS
+    cfg = CONFIGS[name]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    c = make_config(name)
+    d = Dev(c, 1)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    need = w4.w4a16_gemm_workspace_bytes(M, N, K, 0, path=None if variant is None else w4.PATH_TILE, variant=variant)
+    ws = torch.empty(max(need // 4, 1) + 4, dtype=torch.float32, device="cuda")
+    path = None if variant is None else w4.PATH_TILE
+
+    def step(i):
+        w4.w4a16_gemm(d.x, d.w[0], d.s[0], y=y, workspace=ws, path=path, variant=variant)
+
+    total, per = time_steps(step, steps, warmup)
+    t = total / steps
+    flops = 2.0 * M * N * K
+    return dict(M=M, N=N, K=K, us_per_step=t * 1e6, us_per_launch_events=float(np.mean(per)) * 1e6,
+                tflops=flops / t / 1e12, frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS), d, y
+
+
+def bench_grouped(name, steps, warmup, variant=None):
+    import torch
+    import bf16_activation_quantized_amd as w4
+    from synth import make_config, CONFIGS
+    cfg = CONFIGS[name]
+    G, Mt, N, K = cfg["G"], cfg["M_total"], cfg["N"], cfg["K"]
+    c = make_config(name)
+    d = Dev(c, 1)
+    y = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(w4.w4a16_gemm_grouped_workspace_bytes(G, Mt, N, K) // 4 + 4, dtype=torch.float32, device="cuda")
+
+    def step(i):
+        w4.w4a16_gemm_grouped(d.x, d.w[0], d.s[0], d.m_sizes, y=y, workspace=ws, variant=variant)
+
+    total, per = time_steps(step, steps, warmup)
+    t = total / steps
+    flops = 2.0 * Mt * N * K
+    return dict(G=G, M_total=Mt, N=N, K=K, m_sizes=[int(v) for v in c.m_sizes], us_per_step=t * 1e6,
+                us_per_launch_events=float(np.mean(per)) * 1e6, tflops=flops / t / 1e12,
+                frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS), d, y
+
+
+def bench_pack(steps, warmup):
+    import torch
+    import bf16_activation_quantized_amd as w4
+    from synth import CONFIGS
+    N, K = CONFIGS["decode_gemv"]["N"], CONFIGS["decode_gemv"]["K"]
+    q = torch.randint(0, 16, (N, K), dtype=torch.uint8, device="cuda")
+    out = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        w4.w4a16_pack_int4(q, out=out)
+
+    total, _ = time_steps(step, steps, warmup)
+    t = total / steps
+    return dict(rows=N, K=K, us_per_step=t * 1e6, gbs=(N * K * 1.5) / t / 1e9)
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle (unpack + dequant + fp64 GEMV) on the decode workload, timed
+    on the host cores."""
+    import oracle
+    from synth import make_config, CONFIGS
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cfg = CONFIGS["decode_gemv"]
+    c = make_config("decode_gemv")
+    p = oracle.pack_int4(c.q)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm(c.x, p, c.s)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 20:
+            break
+    t = float(np.median(times))
+    wb = eff_weight_bytes(cfg["N"], cfg["K"])
+    return dict(value=wb / t / 1e9, unit="GB/s", cores=int(blas_threads), kind="oracle",
+                sample=f"full decode workload M=1 N={cfg['N']} K={cfg['K']} (unpack + dequant + fp64 GEMV), "
+                       f"{len(times)} runs, median {t * 1e3:.1f} ms; numpy element-wise steps single-threaded, "
+                       f"BLAS with {blas_threads} threads",
+                host_cpus=os.cpu_count(), affinity_cpus=len(os.sched_getaffinity(0)),
+                cpu_model=_cpu_model())
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", default=None,
+                    choices=["decode_gemv", "decode_splitk", "prefill", "grouped", "pack", "tiny"],
+                    help="measure one workload only and print its record (for profiling)")
+    ap.add_argument("--split-k", type=int, default=0)
+    ap.add_argument("--variant", type=int, default=None)
+    ap.add_argument("--path", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="headline workload only")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this W4A16 GEMM library runs on one GPU only; --gpus must be 1 "
+              "(the multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bf16_activation_quantized_amd as w4
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w4._lib()   # fails loudly if the HIP library is not built
+
+    if args.only:
+        if args.only in ("decode_gemv", "decode_splitk", "tiny"):
+            r, _, _ = bench_decode(args.only, args.steps, args.warmup, args.split_k, args.path, args.variant)
+        elif args.only == "prefill":
+            r, _, _ = bench_prefill("prefill", args.steps, args.warmup, args.variant)
+        elif args.only == "grouped":
+            r, _, _ = bench_grouped("grouped", args.steps, args.warmup, args.variant)
+        else:
+            r = bench_pack(args.steps, args.warmup)
+        print(json.dumps({"workload": args.only, **r}), flush=True)
+        return
+
+    log("bench: decode_gemv (headline)")
+    head, _, _ = bench_decode("decode_gemv", args.steps, args.warmup)
+    wb = head["eff_weight_bytes"]
+    ms_per_step = head["us_per_step"] / 1e3
+    # dominant kernel of the step: the decode GEMV (one launch per step at split_k 1)
+    kern_s = head["us_per_launch_events"] / 1e6
+    achieved = wb / kern_s / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="w4a16::gemv_m1_kernel", bytes_per_launch=wb,
+                    launch_us_events=round(head["us_per_launch_events"], 3))
+
+    workloads = {}
+    if not args.no_extras:
+        steps2 = max(20, args.steps // 2)
+        log("bench: tiny")
+        workloads["tiny"], _, _ = bench_decode("tiny", steps2, args.warmup)
+        for sk in (0, 1, 2, 4, 8):
+            log(f"bench: decode_splitk sk={sk}")
+            workloads[f"decode_splitk_sk{sk if sk else 'auto'}"], _, _ = bench_decode(
+                "decode_splitk", steps2, args.warmup, split_k=sk)
+        log("bench: prefill")
+        workloads["prefill"], _, _ = bench_prefill("prefill", steps2, args.warmup)
+        log("bench: grouped")
+        workloads["grouped"], _, _ = bench_grouped("grouped", steps2, args.warmup)
+        log("bench: pack")
+        workloads["pack_int4"] = bench_pack(steps2, args.warmup)
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        cpu = cpu_baseline()
+
+    out = {
+        "metric": METRIC,
+        "value": round(head["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV M=1 N=17408 K=5120 group=128 (bf16 x packed int4, fp32 acc, bf16 out)",
+                   "M": 1, "N": 17408, "K": 5120, "split_k": head["split_k"],
+                   "weight_copies_rotated": head["weight_copies"], "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "workloads": workloads,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

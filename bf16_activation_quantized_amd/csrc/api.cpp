@@ -1,0 +1,302 @@
+// C-ABI entry points: argument validation on the host (before anything is
+// enqueued), path and split-K selection, workspace layout and launches.
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/w4a16.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kGroup = 128;
+constexpr int64_t kMaxDim = 0x7FFFFFFFLL;
+constexpr uint64_t kMaxBytes = 0xFFFFFFFFULL;   // one buffer resource extent
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+bool valid_split(int32_t sk) { return sk == 0 || sk == 1 || sk == 2 || sk == 4 || sk == 8 || sk == 16; }
+
+// Which kernel family runs a plain GEMM at this shape.
+enum Path { kPathAuto = 0, kPathGemv = 1, kPathSkinny = 2, kPathTile = 3 };
+
+int32_t pow2_at_least(int64_t v) {
+  int32_t p = 1;
+  while (p < v && p < 16) p <<= 1;
+  return p;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// GEMV default variant: 1000 * layout (0 = flat 1 KiB runs) + 100 * non-temporal
+// + 10 * prefetch depth + row blocks per wave.
+constexpr int kGemvDefaultVariant = 24;
+// Skinny defaults: column tiles per wave and waves per workgroup.
+constexpr int kSkinnyNT = 4;
+constexpr int kSkinnyWaves = 4;
+
+Path auto_path(int64_t M, int64_t K, int32_t sk) {
+  const int64_t Gk = K / kGroup;
+  if (M == 1) {
+    // the GEMV keeps a lane's x in registers: at most 64 groups per slice
+    const int64_t s = sk > 0 ? sk : 16;
+    return ceil_div(Gk, s) <= 64 ? kPathGemv : kPathSkinny;
+  }
+  if (M <= 16) return kPathSkinny;
+  return kPathTile;
+}
+
+int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg) {
+  const int64_t Gk = K / kGroup;
+  int32_t sk = 1;
+  if (M >= 512) return 1;   // split-K only for small M ("Split-K without atomics")
+  switch (path) {
+    case kPathGemv: {
+      sk = pow2_at_least(ceil_div(Gk, 64));           // register budget for x
+      while (sk < 16 && N * sk < 16384 && ceil_div(Gk, sk * 2) >= 1 && sk * 2 <= Gk) sk <<= 1;
+      break;
+    }
+    case kPathSkinny: {
+      const int64_t wgs = ceil_div(N, 16 * kSkinnyNT);
+      while (sk < 16 && wgs * sk < 512 && ceil_div(Gk, (int64_t)sk * 2) >= kSkinnyWaves) sk <<= 1;
+      break;
+    }
+    case kPathTile: {
+      const int64_t tiles = ceil_div(M, w4a16::tile_bm(tile_cfg)) * ceil_div(N, w4a16::tile_bn(tile_cfg));
+      while (sk < 16 && tiles * sk < 256 && sk * 2 <= Gk) sk <<= 1;
+      break;
+    }
+    default:
+      break;
+  }
+  return sk;
+}
+
+struct Plan {
+  Path path;
+  int32_t sk;        // effective split-K
+  int32_t gps;       // groups per slice
+  int variant;       // kernel variant of the path
+  uint64_t ws_split; // bytes of the [SK, M, N] fp32 partials
+  uint64_t ws_sx;    // bytes of the [K/128, ld] fp32 row sums (tile path)
+  int64_t ld;        // row stride of the row sums
+};
+
+int default_tile_cfg(int64_t M, int64_t N) {
+  (void)M;
+  return N >= 4096 ? 0 : 1;
+}
+
+w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg, Plan* p) {
+  const int64_t Gk = K / kGroup;
+  Path path = auto_path(M, K, split_k);
+  int variant = -1;
+  if (cfg != nullptr) {
+    if (cfg->path < 0 || cfg->path > 3) return W4A16_ERR_SHAPE;
+    if (cfg->path != 0) path = (Path)cfg->path;
+    variant = cfg->variant;
+  }
+  if (path == kPathGemv && M != 1) return W4A16_ERR_SHAPE;
+  if (path == kPathSkinny && M > 16) return W4A16_ERR_SHAPE;
+  int tile_cfg = 0;
+  if (path == kPathTile) {
+    tile_cfg = variant >= 0 ? variant : default_tile_cfg(M, N);
+    if (tile_cfg >= w4a16::tile_num_cfgs()) return W4A16_ERR_SHAPE;
+  }
+  int32_t sk = split_k > 0 ? split_k : auto_split(path, M, N, K, tile_cfg);
+  if (sk > Gk && split_k == 0) sk = 1;
+  if (path == kPathGemv && ceil_div(Gk, sk) > 64) {
+    if (split_k != 0) return W4A16_ERR_SPLIT_K;   // explicit split too small for the GEMV path
+    sk = pow2_at_least(ceil_div(Gk, 64));
+  }
+  p->path = path;
+  p->sk = sk;
+  p->gps = (int32_t)ceil_div(Gk, sk);
+  p->variant = path == kPathTile ? tile_cfg : variant;
+  p->ws_split = sk > 1 ? (uint64_t)sk * (uint64_t)M * (uint64_t)N * 4u : 0u;
+  p->ld = (int64_t)round_up((uint64_t)M, 4);
+  p->ws_sx = path == kPathTile ? (uint64_t)Gk * (uint64_t)p->ld * 4u : 0u;
+  return W4A16_OK;
+}
+
+uint64_t plan_bytes(const Plan& p) { return round_up(p.ws_split, 256) + p.ws_sx; }
+
+w4a16_status check_dims(int64_t M, int64_t N, int64_t K, int32_t group_size) {
+  if (M < 0 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return W4A16_ERR_SHAPE;
+  if (group_size != kGroup || K % kGroup != 0) return W4A16_ERR_GROUP_SIZE;
+  // buffer extents of one resource
+  if ((uint64_t)N * (uint64_t)K / 2u > kMaxBytes) return W4A16_ERR_SHAPE;
+  if ((uint64_t)M * (uint64_t)K * 2u > kMaxBytes) return W4A16_ERR_SHAPE;
+  if ((uint64_t)M * (uint64_t)N * 4u > kMaxBytes) return W4A16_ERR_SHAPE;
+  return W4A16_OK;
+}
+
+w4a16_status launched(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
+
+w4a16_status run_gemm(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, int64_t M, int64_t N,
+                      int64_t K, int32_t group_size, int32_t split_k, float* workspace, size_t workspace_bytes,
+                      void* stream, const w4a16_config* cfg) {
+  if (!valid_split(split_k)) return W4A16_ERR_SPLIT_K;
+  w4a16_status st = check_dims(M, N, K, group_size);
+  if (st != W4A16_OK) return st;
+  if (M == 0) return W4A16_OK;   // empty problem: nothing to read or write
+  if (x == nullptr || w == nullptr || s == nullptr || y == nullptr) return W4A16_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(y)) return W4A16_ERR_ALIGN;
+  Plan p;
+  st = make_plan(M, N, K, split_k, cfg, &p);
+  if (st != W4A16_OK) return st;
+  if (p.ws_split > kMaxBytes) return W4A16_ERR_SHAPE;
+  const uint64_t need = plan_bytes(p);
+  if (need > 0) {
+    if (workspace == nullptr) return W4A16_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
+    if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+  }
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  float* ws_split = p.sk > 1 ? workspace : nullptr;
+  float* ws_sx = p.ws_sx ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + round_up(p.ws_split, 256))
+                         : nullptr;
+  const int iM = (int)M, iN = (int)N, iK = (int)K;
+  hipError_t e = hipSuccess;
+  switch (p.path) {
+    case kPathGemv: {
+      const int v = p.variant > 0 ? p.variant : kGemvDefaultVariant;
+      e = w4a16::launch_gemv_m1(x, w, s, y, ws_split, iN, iK, p.gps, p.sk, v, strm);
+      break;
+    }
+    case kPathSkinny: {
+      int nt = kSkinnyNT, waves = kSkinnyWaves;
+      if (p.variant > 0) { nt = p.variant % 10; waves = p.variant / 10; }
+      e = w4a16::launch_skinny(x, w, s, y, ws_split, iM, iN, iK, p.gps, p.sk, nt, waves, strm);
+      break;
+    }
+    case kPathTile: {
+      e = w4a16::launch_rowsum_neg136(x, ws_sx, iM, iK, (int)p.ld, strm);
+      if (e == hipSuccess)
+        e = w4a16::launch_tile(x, w, s, ws_sx, y, ws_split, nullptr, iM, iN, iK, 1, (int)p.ld, p.gps, p.sk,
+                               p.variant, strm);
+      break;
+    }
+    default:
+      return W4A16_ERR_SHAPE;
+  }
+  if (e != hipSuccess) return W4A16_ERR_LAUNCH;
+  if (p.sk > 1) return launched(w4a16::launch_splitk_reduce(ws_split, y, (uint64_t)M * (uint64_t)N, p.sk, strm));
+  return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a16_status_string(int status) {
+  switch (status) {
+    case W4A16_OK: return "W4A16_OK";
+    case W4A16_ERR_NULL: return "W4A16_ERR_NULL: a required pointer is NULL";
+    case W4A16_ERR_SHAPE: return "W4A16_ERR_SHAPE: invalid dimension or size limit exceeded";
+    case W4A16_ERR_GROUP_SIZE: return "W4A16_ERR_GROUP_SIZE: group_size must be 128 and divide K";
+    case W4A16_ERR_SPLIT_K: return "W4A16_ERR_SPLIT_K: split_k must be 0, 1, 2, 4, 8 or 16";
+    case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE: workspace missing or too small";
+    case W4A16_ERR_ALIGN: return "W4A16_ERR_ALIGN: pointers must be 16-byte aligned";
+    case W4A16_ERR_LAUNCH: return "W4A16_ERR_LAUNCH: kernel launch failed";
+    default: return "W4A16: unknown status";
+  }
+}
+
+w4a16_status w4a16_pack_int4(const uint8_t* q, uint8_t* w_packed, int64_t rows, int64_t K, void* stream) {
+  if (rows < 0 || K < 2 || K % 2 != 0) return W4A16_ERR_SHAPE;
+  if (q == nullptr || w_packed == nullptr) return W4A16_ERR_NULL;
+  if (!aligned16(q) || !aligned16(w_packed)) return W4A16_ERR_ALIGN;
+  if (rows == 0) return W4A16_OK;
+  if ((uint64_t)rows > (uint64_t)INT64_MAX / (uint64_t)K) return W4A16_ERR_SHAPE;
+  return launched(w4a16::launch_pack_int4(q, w_packed, (uint64_t)rows * (uint64_t)K, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int32_t w4a16_gemm_auto_split_k(int64_t M, int64_t N, int64_t K) {
+  if (check_dims(M, N, K, 128) != W4A16_OK || M == 0) return 0;
+  Plan p;
+  if (make_plan(M, N, K, 0, nullptr, &p) != W4A16_OK) return 0;
+  return p.sk;
+}
+
+size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t split_k) {
+  return w4a16_gemm_workspace_bytes_ex(M, N, K, split_k, nullptr);
+}
+
+size_t w4a16_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg) {
+  if (!valid_split(split_k) || check_dims(M, N, K, 128) != W4A16_OK || M == 0) return 0;
+  Plan p;
+  if (make_plan(M, N, K, split_k, cfg, &p) != W4A16_OK) return 0;
+  return (size_t)plan_bytes(p);
+}
+
+w4a16_status w4a16_gemm(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales, uint16_t* y, int64_t M,
+                        int64_t N, int64_t K, int32_t group_size, int32_t split_k, float* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return run_gemm(x, w_packed, scales, y, M, N, K, group_size, split_k, workspace, workspace_bytes, stream, nullptr);
+}
+
+w4a16_status w4a16_gemm_ex(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales, uint16_t* y,
+                           int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t split_k, float* workspace,
+                           size_t workspace_bytes, void* stream, const w4a16_config* cfg) {
+  return run_gemm(x, w_packed, scales, y, M, N, K, group_size, split_k, workspace, workspace_bytes, stream, cfg);
+}
+
+size_t w4a16_gemm_grouped_workspace_bytes(int32_t G, int64_t M_total, int64_t N, int64_t K) {
+  if (G < 1 || M_total <= 0 || check_dims(M_total, N, K, 128) != W4A16_OK) return 0;
+  return (size_t)((uint64_t)(K / kGroup) * round_up((uint64_t)M_total, 4) * 4u);
+}
+
+w4a16_status w4a16_gemm_grouped(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales,
+                                const int32_t* m_sizes, uint16_t* y, int32_t G, int64_t M_total, int64_t N, int64_t K,
+                                int32_t group_size, float* workspace, size_t workspace_bytes, void* stream) {
+  return w4a16_gemm_grouped_ex(x, w_packed, scales, m_sizes, y, G, M_total, N, K, group_size, workspace,
+                               workspace_bytes, stream, nullptr);
+}
+
+w4a16_status w4a16_gemm_grouped_ex(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales,
+                                   const int32_t* m_sizes, uint16_t* y, int32_t G, int64_t M_total, int64_t N,
+                                   int64_t K, int32_t group_size, float* workspace, size_t workspace_bytes,
+                                   void* stream, const w4a16_config* cfg) {
+  if (G < 1 || M_total < 0) return W4A16_ERR_SHAPE;
+  w4a16_status st = check_dims(M_total, N, K, group_size);
+  if (st != W4A16_OK) return st;
+  if ((uint64_t)N * (uint64_t)K / 2u * (uint64_t)G > (uint64_t)INT64_MAX / 2) return W4A16_ERR_SHAPE;
+  if (M_total == 0) return W4A16_OK;   // empty problem: nothing to read or write
+  if (x == nullptr || w_packed == nullptr || scales == nullptr || m_sizes == nullptr || y == nullptr)
+    return W4A16_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_packed) || !aligned16(scales) || !aligned16(y)) return W4A16_ERR_ALIGN;
+  if (((uintptr_t)m_sizes & 3u) != 0) return W4A16_ERR_ALIGN;
+  int tile_cfg = default_tile_cfg(M_total, N);
+  if (cfg != nullptr) {
+    if (cfg->path != 0 && cfg->path != kPathTile) return W4A16_ERR_SHAPE;
+    if (cfg->variant >= 0) tile_cfg = cfg->variant;
+    if (tile_cfg >= w4a16::tile_num_cfgs()) return W4A16_ERR_SHAPE;
+  }
+  const uint64_t need = w4a16_gemm_grouped_workspace_bytes(G, M_total, N, K);
+  if (workspace == nullptr) return W4A16_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
+  if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  const int ld = (int)round_up((uint64_t)M_total, 4);
+  const int Gk = (int)(K / kGroup);
+  hipError_t e = w4a16::launch_rowsum_neg136(x, workspace, (int)M_total, (int)K, ld, strm);
+  if (e != hipSuccess) return W4A16_ERR_LAUNCH;
+  return launched(w4a16::launch_tile(x, w_packed, scales, workspace, y, nullptr, m_sizes, (int)M_total, (int)N,
+                                     (int)K, G, ld, Gk, 1, tile_cfg, strm));
+}
+
+w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y, int32_t split_k, int64_t M, int64_t N,
+                                 void* stream) {
+  if (split_k < 1 || split_k > 64 || M < 0 || N < 0) return W4A16_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4A16_OK;
+  if (workspace == nullptr || y == nullptr) return W4A16_ERR_NULL;
+  if (!aligned16(workspace) || !aligned16(y)) return W4A16_ERR_ALIGN;
+  if ((uint64_t)M > (uint64_t)INT64_MAX / (uint64_t)N / 64u) return W4A16_ERR_SHAPE;
+  return launched(w4a16::launch_splitk_reduce(workspace, y, (uint64_t)M * (uint64_t)N, split_k,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

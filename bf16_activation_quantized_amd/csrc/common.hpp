@@ -1,0 +1,122 @@
+// Device helpers shared by the W4A16 kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kGroup = 128;            // K elements per scale group
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+
+// ---------------------------------------------------------------- buffers
+// A buffer resource with an exact byte extent: loads past `bytes` return 0
+// and stores past it are dropped by the hardware, so tails need no guards
+// ("[ROCm][Kernel] W4A16 skinny GEMM: hand-asm kernel for gfx1151", section 3
+// "Exact buffer-descriptor sizing").
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint16_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ void st128(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ void st64(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ void st32(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ void st16(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
+}
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint16_t to_bf16(float v) {
+  return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+}
+
+// ---------------------------------------------------------------- dequant
+// Magic-constant int4 -> bf16 ("[ROCm][Kernel] W4A16 skinny GEMM ...",
+// section 1): a nibble n OR-ed into the low mantissa bits of the bf16 pattern
+// 0x4300 (= 128.0, whose ulp is 1) reads as bf16(128 + n), exactly. The
+// contraction then sees (128 + n); the "- 136" of the page's (128 + n) - 136
+// = n - 8 is applied outside the dot, once per group, as -136 * sum(x).
+constexpr uint32_t kMagicPair = 0x43004300u;
+constexpr uint32_t kNibblePairMask = 0x000F000Fu;
+
+// Word w holds the nibbles of 8 consecutive k (k0 in bits 0-3 ... k7 in
+// bits 28-31). Pair j (0..3) = (bf16(128+q[j]), bf16(128+q[j+4])), i.e. the
+// k order inside the 8-block becomes (0,4,1,5,2,6,3,7).
+__device__ __forceinline__ uint32_t magic_pair_interleaved(uint32_t w, int j) {
+  return ((w >> (4 * j)) & kNibblePairMask) | kMagicPair;
+}
+
+// (a & m) | o in one VOP3 instruction. gfx950 VOP3 cannot encode literal
+// constants, so the compiler would split a literal-mask and-or into two VOP2
+// instructions; here the mask comes from an SGPR and `o` from a VGPR.
+__device__ __forceinline__ uint32_t and_or_sv(uint32_t a, uint32_t m_sgpr, uint32_t o_vgpr) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m_sgpr), "v"(o_vgpr));
+  return r;
+}
+// An opaque VGPR copy of a constant, so that it stays in one register.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+  return r;
+}
+
+// Natural k order: pair j (0..3) = (bf16(128+q[2j]), bf16(128+q[2j+1])).
+// v_perm puts byte j of w into byte 0 and byte j of (w >> 4) into byte 2.
+__device__ __forceinline__ uint32_t magic_pair_natural(uint32_t w, uint32_t w4, int j) {
+  // selector: byte0 <- src1.byte j (w), byte2 <- src0.byte j (w4); bytes 1, 3 unused (masked)
+  const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 16) | 0x0C000C00u;
+  return (__builtin_amdgcn_perm(w4, w, sel) & kNibblePairMask) | kMagicPair;
+}
+
+// ---------------------------------------------------------------- XCD mapping
+// Workgroups are dispatched to the 8 XCDs round robin (blockIdx % 8). Remap so
+// that each XCD owns a contiguous run of logical tile ids: neighbouring tiles
+// (which share weight columns) then share one XCD's L2 ("Add Triton
+// BF16xINT4 rowwise GEMM for ROCm gfx942/gfx950", Implementation "XCD
+// remapping").
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int per = (nblocks + kNumXcd - 1) / kNumXcd;
+  const int xcd = bid % kNumXcd;
+  const int idx = bid / kNumXcd;
+  // XCDs with index < rem own `per` tiles, the others `per - 1`
+  const int rem = nblocks - (per - 1) * kNumXcd;
+  int base;
+  if (xcd < rem) base = xcd * per;
+  else base = rem * per + (xcd - rem) * (per - 1);
+  return base + idx;
+}
+
+}  // namespace w4a16

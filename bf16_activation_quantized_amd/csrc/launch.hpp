@@ -1,0 +1,33 @@
+// Host-side launchers of the device kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+hipError_t launch_pack_int4(const uint8_t* q, uint8_t* out, uint64_t total_in, hipStream_t stream);
+hipError_t launch_splitk_reduce(const float* ws, uint16_t* y, uint64_t mn, int sk, hipStream_t stream);
+
+// M = 1 decode GEMV; gps = 128-groups per split-K slice (<= 64), sk slices;
+// ws == nullptr writes bf16 y, else fp32 partials ws[s, 0, :].
+hipError_t launch_gemv_m1(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
+                          int N, int K, int gps, int sk, int variant, hipStream_t stream);
+
+// 1 <= M <= 16 decode on MFMA 16x16x32; nt column tiles of 16 per wave, `waves` per workgroup.
+hipError_t launch_skinny(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
+                         int M, int N, int K, int gps, int sk, int nt, int waves, hipStream_t stream);
+
+// out[g * ld + m] = -136 * sum_{k in group g} x[m, k]
+hipError_t launch_rowsum_neg136(const uint16_t* x, float* out, int M, int K, int ld, hipStream_t stream);
+
+// Tile GEMM (plain when m_sizes == nullptr, grouped otherwise). With ws != nullptr
+// (plain only) slice s of gridDim.y = sk writes fp32 partials ws[s, :, :].
+hipError_t launch_tile(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
+                       float* ws, const int32_t* m_sizes, int M_total, int N, int K, int G, int ld, int gps,
+                       int sk, int cfg, hipStream_t stream);
+int tile_bm(int cfg);
+int tile_bn(int cfg);
+int tile_num_cfgs();
+
+}  // namespace w4a16

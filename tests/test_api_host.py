@@ -1,0 +1,158 @@
+"""Host-side checks of the C-ABI library (CPU only: no kernel is launched).
+
+Every call here either only queries host logic (workspace sizes, split-K
+choice, status strings) or carries an argument error that the library must
+reject before anything is enqueued.
+"""
+import ctypes
+import os
+
+import pytest
+
+import bf16_activation_quantized_amd as w4
+
+LIB_MISSING = not os.path.exists(w4.LIB_PATH)
+pytestmark = pytest.mark.skipif(LIB_MISSING, reason="libw4a16.so not built")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_SPLIT, ERR_WS, ERR_ALIGN = 0, 1, 2, 3, 4, 5, 6
+
+
+def L():
+    return w4._lib()
+
+
+def test_exports_every_declared_symbol():
+    names = w4.header_functions()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(w4.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(8):
+        txt = w4.status_string(s)
+        assert txt.startswith("W4A16_")
+    assert "unknown" in w4.status_string(99)
+
+
+# fake but 16-byte aligned device pointers: never dereferenced, because every
+# call below fails validation first
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+C = ctypes.c_void_p(0x30000)
+D = ctypes.c_void_p(0x40000)
+MIS = ctypes.c_void_p(0x10004)
+
+
+def gemm(x=A, w=B, s=C, y=D, M=1, N=64, K=128, g=128, sk=0, ws=None, wsb=0):
+    return L().w4a16_gemm(x, w, s, y, M, N, K, g, sk, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(M=-1), ERR_SHAPE), (dict(N=0), ERR_SHAPE), (dict(K=0), ERR_SHAPE),
+    (dict(K=100), ERR_GROUP), (dict(K=192), ERR_GROUP), (dict(g=64), ERR_GROUP),
+    (dict(g=32, K=128), ERR_GROUP),
+    (dict(sk=3), ERR_SPLIT), (dict(sk=-1), ERR_SPLIT), (dict(sk=32), ERR_SPLIT),
+    (dict(x=None), ERR_NULL), (dict(w=None), ERR_NULL), (dict(s=None), ERR_NULL), (dict(y=None), ERR_NULL),
+    (dict(x=MIS), ERR_ALIGN), (dict(y=MIS), ERR_ALIGN), (dict(w=MIS), ERR_ALIGN), (dict(s=MIS), ERR_ALIGN),
+    (dict(M=4, N=1 << 20, K=1 << 14), ERR_SHAPE),            # W larger than 4 GiB (one resource)
+    (dict(M=1 << 22, N=64, K=1 << 10), ERR_SHAPE),           # X larger than 4 GiB
+    (dict(M=1 << 31, N=64, K=128), ERR_SHAPE),               # dimension limit
+    (dict(M=1, N=64, K=128, sk=2), ERR_WS),                  # split-K needs a workspace
+    (dict(M=64, N=64, K=256), ERR_WS),                       # tile path needs the row-sum workspace
+    (dict(M=64, N=64, K=256, ws=A, wsb=16), ERR_WS),         # too small
+    (dict(M=64, N=64, K=256, ws=MIS, wsb=1 << 20), ERR_ALIGN),
+    (dict(M=0), OK),                                         # empty: nothing enqueued
+    (dict(M=0, x=None, y=None), OK),                         # empty: pointers unused
+])
+def test_gemm_argument_errors(kw, want):
+    assert gemm(**kw) == want
+
+
+def test_gemm_m0_ok_even_without_workspace():
+    assert gemm(M=0, N=1000, K=1024, sk=8) == OK
+
+
+def grouped(x=A, w=B, s=C, ms=A, y=D, G=2, Mt=10, N=64, K=128, g=128, ws=A, wsb=1 << 20):
+    return L().w4a16_gemm_grouped(x, w, s, ms, y, G, Mt, N, K, g, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(G=0), ERR_SHAPE), (dict(G=-3), ERR_SHAPE), (dict(Mt=-1), ERR_SHAPE),
+    (dict(K=130), ERR_GROUP), (dict(g=256), ERR_GROUP),
+    (dict(ms=None), ERR_NULL), (dict(x=None), ERR_NULL), (dict(y=None), ERR_NULL),
+    (dict(ms=ctypes.c_void_p(0x10002)), ERR_ALIGN), (dict(x=MIS), ERR_ALIGN),
+    (dict(ws=None), ERR_WS), (dict(wsb=8), ERR_WS),
+    (dict(Mt=0), OK),
+    (dict(Mt=0, x=None, ms=None), OK),                      # empty: pointers unused
+])
+def test_grouped_argument_errors(kw, want):
+    assert grouped(**kw) == want
+
+
+def test_pack_argument_errors():
+    f = L().w4a16_pack_int4
+    assert f(A, B, 4, 3, None) == ERR_SHAPE          # odd K
+    assert f(A, B, -1, 4, None) == ERR_SHAPE
+    assert f(A, B, 4, 0, None) == ERR_SHAPE
+    assert f(None, B, 4, 4, None) == ERR_NULL
+    assert f(A, MIS, 4, 4, None) == ERR_ALIGN
+    assert f(A, B, 0, 4, None) == OK                 # nothing to do
+
+
+def test_reduce_argument_errors():
+    f = L().w4a16_splitk_reduce
+    assert f(A, B, 0, 4, 4, None) == ERR_SHAPE
+    assert f(A, B, 65, 4, 4, None) == ERR_SHAPE
+    assert f(A, B, 2, -1, 4, None) == ERR_SHAPE
+    assert f(None, B, 2, 4, 4, None) == ERR_NULL
+    assert f(MIS, B, 2, 4, 4, None) == ERR_ALIGN
+    assert f(A, B, 2, 0, 4, None) == OK
+
+
+def test_explicit_path_errors():
+    cfg = w4._Config(1, -1)   # GEMV path forced at M=2
+    st = L().w4a16_gemm_ex(A, B, C, D, 2, 64, 128, 128, 0, None, 0, None, ctypes.byref(cfg))
+    assert st == ERR_SHAPE
+    cfg = w4._Config(2, -1)   # skinny path forced at M=17
+    st = L().w4a16_gemm_ex(A, B, C, D, 17, 64, 128, 128, 0, None, 0, None, ctypes.byref(cfg))
+    assert st == ERR_SHAPE
+    cfg = w4._Config(7, -1)
+    st = L().w4a16_gemm_ex(A, B, C, D, 2, 64, 128, 128, 0, None, 0, None, ctypes.byref(cfg))
+    assert st == ERR_SHAPE
+
+
+def test_auto_split_rule():
+    # split-K is used only below M = 512 ("Split-K without atomics")
+    for M in (512, 1322, 4096):
+        assert w4.w4a16_gemm_auto_split_k(M, 64, 8192) == 1
+    for M in (1, 2, 16, 100):
+        sk = w4.w4a16_gemm_auto_split_k(M, 256, 8192)
+        assert sk in (1, 2, 4, 8, 16)
+    # the decode GEMV holds at most 64 groups of x per lane: K = 32768 forces SK >= 4
+    assert w4.w4a16_gemm_auto_split_k(1, 65536, 32768) >= 4
+    assert w4.w4a16_gemm_auto_split_k(0, 64, 128) == 0
+    assert w4.w4a16_gemm_auto_split_k(1, 64, 100) == 0
+
+
+def test_workspace_sizes():
+    # split-K partials [SK, M, N] fp32
+    assert w4.w4a16_gemm_workspace_bytes(16, 8192, 8192, 8) == 8 * 16 * 8192 * 4
+    assert w4.w4a16_gemm_workspace_bytes(16, 8192, 8192, 1) == 0
+    assert w4.w4a16_gemm_workspace_bytes(1, 17408, 5120, 1) == 0
+    # tile path: row sums [K/128, round_up(M, 4)] fp32
+    assert w4.w4a16_gemm_workspace_bytes(1322, 19456, 2560, 1) == 20 * 1324 * 4
+    sk2 = w4.w4a16_gemm_workspace_bytes(100, 64, 256, 2)
+    assert sk2 == ((2 * 100 * 64 * 4 + 255) // 256) * 256 + 2 * 100 * 4
+    assert w4.w4a16_gemm_grouped_workspace_bytes(8, 2048, 2048, 4096) == 32 * 2048 * 4
+    assert w4.w4a16_gemm_grouped_workspace_bytes(8, 2047, 2048, 4096) == 32 * 2048 * 4
+    assert w4.w4a16_gemm_grouped_workspace_bytes(0, 2048, 2048, 4096) == 0
+    assert w4.w4a16_gemm_workspace_bytes(16, 64, 100, 1) == 0     # invalid K
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(w4, "_lib_handle", None)
+    monkeypatch.setattr(w4, "LIB_PATH", "/nonexistent/libw4a16.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        w4._lib()

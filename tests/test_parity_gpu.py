@@ -1,0 +1,292 @@
+"""GPU parity: the HIP library (called through its C ABI) against the CPU
+oracle, on the same seeded inputs.
+
+Floating-point results must pass the gate max|y - y_ref| <= 4e-3 * max|y_ref|
++ 1e-3 and cos >= 0.99999 against the float64 oracle; integer work (packing)
+and the reduce step (float32 sum in slice order, then round to nearest even,
+decided in the same precision on both sides) must be bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bf16_activation_quantized_amd as w4
+import oracle
+from synth import make_inputs, make_workspace
+from gpu_util import DevCase, bf16_dev, bits_host, check_gate, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w4._lib()   # raises if the HIP library is missing: no fallback
+
+
+def _run(case, sk=0, path=None, variant=None, M=None):
+    y = w4.w4a16_gemm(case.x, case.w, case.s, split_k=sk, path=path, variant=variant)
+    torch.cuda.synchronize()
+    return bits_host(y)
+
+
+# ------------------------------------------------------------------ packing
+
+@pytest.mark.parametrize("rows,K", [(3, 18), (7, 10), (256, 512), (1000, 1280), (5, 4098), (1, 2)])
+def test_pack_bit_exact(rows, K):
+    rng = np.random.default_rng(rows * 7 + K)
+    q = rng.integers(0, 256, (rows, K), dtype=np.uint8)   # high bits must be ignored
+    out = w4.w4a16_pack_int4(u8_dev(q))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle.pack_int4(q & 0x0F))
+
+
+# ------------------------------------------------------------------ decode GEMV (M = 1)
+
+GEMV_CASES = [
+    # N, K, split_k, variant (1000 * layout [0 flat, 1 half-wave] + 100 * non-temporal
+    #                         + 10 * prefetch depth + row blocks (rows) per wave)
+    (256, 512, 0, None),      # the tiny workload (flat, 4-row blocks)
+    (17408, 5120, 1, None),   # the decode workload (flat, 2-row blocks)
+    (1001, 5120, 1, 131),     # odd N: last 2-row block half outside
+    (999, 8192, 1, 22),       # flat, 1-row blocks, 4 runs of 1 KiB
+    (777, 4096, 1, 113),      # flat, 1-row blocks, 2 runs
+    (1003, 2560, 1, 24),      # flat, 4-row blocks, 5 runs
+    (1002, 1024, 1, 21),      # flat, 2-row blocks, 1 run
+    (1000, 1280, 1, 1011),    # half-wave layout (flat does not fit 40 chunks/row)
+    (1000, 1280, 1, 1022),
+    (1001, 1280, 1, 1134),
+    (999, 640, 1, 1149),
+    (1003, 5120, 1, 1037),    # half-wave layout forced
+    (37, 128, 1, None),
+    (513, 2560, 2, None),
+    (300, 9216, 0, None),     # 72 groups: auto split so that a slice holds <= 64
+    (300, 1024, 16, None),    # more slices than groups: empty slices write zeros
+    (64, 384, 4, None),       # 3 groups over 4 slices
+    (1, 8192, 1, None),       # single row, 64 groups in one slice
+    (3, 5120, 1, None),       # fewer rows than one wave's blocks
+    (40, 10240, 2, 24),       # flat with split-K: 40 groups per slice
+    (41, 7680, 2, None),      # 30 groups per slice -> half-wave fallback
+]
+
+
+@pytest.mark.parametrize("N,K,sk,variant", GEMV_CASES)
+def test_gemv_parity(N, K, sk, variant):
+    c = make_inputs(1, N, K, seed=N + K + sk)
+    d = DevCase(c)
+    assert d.packed_matches_oracle()
+    y = _run(d, sk=sk, path=w4.PATH_GEMV, variant=variant)
+    check_gate(y, oracle.gemm(c.x, d.p_host, c.s), f"gemv N={N} K={K} sk={sk} v={variant}")
+
+
+# ------------------------------------------------------------------ skinny MFMA (M <= 16)
+
+SKINNY_CASES = [
+    # M, N, K, split_k, variant (10 * waves + column tiles per wave)
+    (1, 256, 512, 1, 44),
+    (2, 1000, 1024, 1, 44),
+    (3, 17, 384, 1, 41),
+    (5, 64, 128, 1, 42),
+    (15, 1000, 1024, 2, 84),
+    (16, 513, 2048, 4, 81),
+    (16, 256, 1024, 8, 82),
+    (16, 100, 384, 16, 44),   # more slices than groups
+    (7, 300, 640, 1, 82),
+    (16, 8192, 1024, 0, None),
+]
+
+
+@pytest.mark.parametrize("M,N,K,sk,variant", SKINNY_CASES)
+def test_skinny_parity(M, N, K, sk, variant):
+    c = make_inputs(M, N, K, seed=M * 1000 + N + K)
+    d = DevCase(c)
+    y = _run(d, sk=sk, path=w4.PATH_SKINNY, variant=variant)
+    check_gate(y, oracle.gemm(c.x, d.p_host, c.s), f"skinny M={M} N={N} K={K} sk={sk} v={variant}")
+
+
+# ------------------------------------------------------------------ tile MFMA (prefill)
+
+TILE_CASES = [
+    # M, N, K, split_k, tile config
+    (17, 100, 128, 1, 0),
+    (130, 256, 256, 1, 0),
+    (300, 1000, 640, 1, 1),
+    (129, 513, 384, 2, 0),
+    (64, 64, 1024, 4, 1),
+    (257, 300, 256, 8, 1),    # more slices than groups
+    (1, 256, 256, 1, 0),      # one row through the tile kernel (M tail)
+    (255, 129, 512, 0, 0),
+    (600, 700, 1280, 0, 1),
+]
+
+
+@pytest.mark.parametrize("M,N,K,sk,cfg", TILE_CASES)
+def test_tile_parity(M, N, K, sk, cfg):
+    c = make_inputs(M, N, K, seed=M + N * 3 + K)
+    d = DevCase(c)
+    y = _run(d, sk=sk, path=w4.PATH_TILE, variant=cfg)
+    check_gate(y, oracle.gemm(c.x, d.p_host, c.s), f"tile M={M} N={N} K={K} sk={sk} cfg={cfg}")
+
+
+# ------------------------------------------------------------------ grouped
+
+GROUPED_CASES = [
+    # m_sizes, N, K, tile config
+    ([37], 256, 384, None),
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 0),
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 1),
+    ([0, 0, 0, 50], 128, 128, None),
+    ([128, 128, 128], 256, 512, 1),
+    ([1, 1, 1, 1, 1], 64, 128, 0),
+]
+
+
+@pytest.mark.parametrize("ms,N,K,cfg", GROUPED_CASES)
+def test_grouped_parity(ms, N, K, cfg):
+    c = make_inputs(sum(ms), N, K, seed=len(ms) * 31 + N + K, G=len(ms), m_sizes=ms)
+    d = DevCase(c)
+    assert d.packed_matches_oracle()
+    y = w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, variant=cfg)
+    torch.cuda.synchronize()
+    check_gate(bits_host(y), oracle.gemm_grouped(c.x, d.p_host, c.s, c.m_sizes), f"grouped {ms} N={N} K={K}")
+
+
+def test_grouped_empty_total_is_noop():
+    c = make_inputs(0, 64, 128, seed=5, G=3, m_sizes=[0, 0, 0])
+    d = DevCase(c)
+    y = torch.full((0, 64), 1.0, dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, y=y)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ split-K partials and reduce
+
+@pytest.mark.parametrize("path,M,N,K,sk", [
+    (w4.PATH_GEMV, 1, 300, 1280, 4),
+    (w4.PATH_SKINNY, 16, 256, 1024, 8),
+    (w4.PATH_SKINNY, 5, 100, 384, 4),
+    (w4.PATH_TILE, 130, 256, 640, 2),
+])
+def test_splitk_workspace_slices(path, M, N, K, sk):
+    c = make_inputs(M, N, K, seed=sk * 100 + M)
+    d = DevCase(c)
+    need = w4.w4a16_gemm_workspace_bytes(M, N, K, sk, path=path)
+    ws = torch.empty(need // 4 + 4, dtype=torch.float32, device="cuda")
+    y = w4.w4a16_gemm(d.x, d.w, d.s, split_k=sk, workspace=ws, path=path)
+    torch.cuda.synchronize()
+    part = ws[: sk * M * N].view(sk, M, N).cpu().numpy().astype(np.float64)
+    ref = oracle.gemm_splitk_partials(c.x, d.p_host, c.s, sk)
+    # fp32 accumulation bound: the kernels accumulate x * (128 + q) against
+    # -136 * sum(x), so the error scales with 143 * sum |x| * s per slice
+    x = np.abs(oracle.bf16_to_f64(c.x))
+    srep = np.repeat(oracle.bf16_to_f64(c.s), 128, axis=1) * 143.0
+    for s, (g0, g1) in enumerate(oracle.splitk_group_ranges(K // 128, sk)):
+        k0, k1 = g0 * 128, g1 * 128
+        mag = x[:, k0:k1] @ srep[:, k0:k1].T if k1 > k0 else np.zeros((M, N))
+        err = np.abs(part[s] - ref[s])
+        assert np.all(err <= 4e-6 * mag + 1e-30), (s, float(err.max()), float(mag.max()))
+    # and the final output is the reduce of exactly these partials
+    assert np.array_equal(bits_host(y), oracle.splitk_reduce_bf16(ws[: sk * M * N].view(sk, M, N).cpu().numpy()))
+
+
+@pytest.mark.parametrize("sk,M,N", [(1, 3, 37), (2, 16, 64), (3, 5, 7), (8, 16, 8192), (16, 1, 17408), (64, 2, 6)])
+def test_splitk_reduce_bit_exact(sk, M, N):
+    ws = make_workspace(sk, M, N, seed=sk + M + N)
+    y = w4.w4a16_splitk_reduce(torch.from_numpy(ws).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_host(y), oracle.splitk_reduce_bf16(ws))
+
+
+# ------------------------------------------------------------------ degenerate inputs
+
+@pytest.mark.parametrize("path,M", [(w4.PATH_GEMV, 1), (w4.PATH_SKINNY, 4), (w4.PATH_TILE, 40)])
+def test_degenerate_zero_outputs(path, M):
+    N, K = 200, 384
+    c = make_inputs(M, N, K, seed=9)
+    # q == 8 everywhere: the oracle gives exactly 0; the MFMA paths form
+    # -136 * sum(x) + sum(136 * x) in two fp32 summation orders, so only a
+    # rounding residue (far below the gate's absolute term) may remain
+    zero_q = DevCase(type(c)(x=c.x, q=np.full_like(c.q, 8), s=c.s))
+    check_gate(_run(zero_q, path=path), np.zeros((M, N)), "q == 8")
+    zero_s = DevCase(type(c)(x=c.x, q=c.q, s=np.zeros_like(c.s)))
+    assert np.all((_run(zero_s, path=path) & 0x7FFF) == 0)       # s == 0 -> +-0
+    zero_x = DevCase(type(c)(x=np.zeros_like(c.x), q=c.q, s=c.s))
+    assert np.all((_run(zero_x, path=path) & 0x7FFF) == 0)
+
+
+def test_n1_and_k128():
+    for M in (1, 3, 20):
+        c = make_inputs(M, 1, 128, seed=M)
+        d = DevCase(c)
+        check_gate(_run(d), oracle.gemm(c.x, d.p_host, c.s), f"N=1 M={M}")
+
+
+def test_m0_leaves_output_untouched():
+    c = make_inputs(1, 64, 256, seed=3)
+    d = DevCase(c)
+    x0 = d.x[:0]
+    y = torch.full((0, 64), 2.0, dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_gemm(x0, d.w, d.s, y=y)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ determinism and graphs
+
+@pytest.mark.parametrize("path,M,N,K,sk", [
+    (w4.PATH_GEMV, 1, 1000, 2560, 1),
+    (w4.PATH_SKINNY, 16, 1024, 2048, 4),
+    (w4.PATH_TILE, 300, 512, 1024, 1),
+])
+def test_repeat_bitwise_and_graph_replay(path, M, N, K, sk):
+    c = make_inputs(M, N, K, seed=77)
+    d = DevCase(c)
+    need = w4.w4a16_gemm_workspace_bytes(M, N, K, sk, path=path)
+    ws = torch.empty(max(need // 4, 1) + 4, dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_gemm(d.x, d.w, d.s, y=y, split_k=sk, workspace=ws, path=path)
+    torch.cuda.synchronize()
+    ref = bits_host(y)
+    check_gate(ref, oracle.gemm(c.x, d.p_host, c.s), "eager")
+    for _ in range(3):
+        w4.w4a16_gemm(d.x, d.w, d.s, y=y, split_k=sk, workspace=ws, path=path)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_host(y), ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            w4.w4a16_gemm(d.x, d.w, d.s, y=y, split_k=sk, workspace=ws, path=path)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(3):
+        y.fill_(0)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_host(y), ref), f"replay {i}"
+
+
+def test_grouped_graph_replay():
+    ms = [3, 0, 129, 5, 0, 255, 1, 64]
+    c = make_inputs(sum(ms), 300, 256, seed=12, G=len(ms), m_sizes=ms)
+    d = DevCase(c)
+    y = torch.empty((sum(ms), 300), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(w4.w4a16_gemm_grouped_workspace_bytes(len(ms), sum(ms), 300, 256) // 4,
+                     dtype=torch.float32, device="cuda")
+    w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    ref = bits_host(y)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, y=y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(3):
+        y.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_host(y), ref), f"replay {i}"
