@@ -35,6 +35,16 @@ METRIC = "effective weight GB/s at M=1 decode; TFLOP/s at M=1322 prefill (1x MI3
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROTATE_BYTES = 512 << 20
+# HBM bytes per launch of the decode GEMV from rocprofv3 --pmc (FETCH_SIZE and
+# WRITE_SIZE, KiB per dispatch), scaled by the factors a plain copy kernel of
+# known size reads from the same counters (FETCH x2.00, WRITE x1.00); None
+# when the kernel has changed since the counters were taken
+TRAFFIC_DECODE_GEMV = {
+    "kernel": "w4a16::gemv_m1_kernel<5, 2, 2>",
+    "fetch_kib_counter": 22564.12, "fetch_factor": 2.00,
+    "write_kib_counter": 68.0, "write_factor": 1.00,
+    "bytes": int((22564.12 * 2.00 + 68.0 * 1.00) * 1024),
+}
 
 
 def log(msg):
@@ -64,28 +74,32 @@ class Dev:
 
 
 def time_steps(step, steps, warmup):
-    """Runs `warmup` untimed steps, then `steps` timed steps, each bracketed
-    by events on the launch stream. Returns (total seconds, per-step
-    seconds list)."""
+    """W untimed eager warmup steps; then the K steps are captured once in a
+    HIP graph on a side stream (the library enqueues only kernels, so the
+    capture is exact), replayed once untimed (graph upload), and the timed
+    region is one replay of exactly K steps bracketed by synchronisations and
+    HIP events on that stream. Returns (total seconds, seconds per step)."""
     import torch
-    stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(s)
+        g.replay()
+        t1.record(s)
+        torch.cuda.synchronize()
     total = t0.elapsed_time(t1) / 1e3
-    per = [a.elapsed_time(b) / 1e3 for a, b in ev]
-    return total, per
+    return total, total / steps
 
 
 def bench_decode(name, steps, warmup, split_k=0, path=None, variant=None):
@@ -107,11 +121,9 @@ def bench_decode(name, steps, warmup, split_k=0, path=None, variant=None):
         j = i % copies
         w4.w4a16_gemm(d.x, d.w[j], d.s[j], y=y, split_k=split_k, workspace=ws, path=path, variant=variant)
 
-    total, per = time_steps(step, steps, warmup)
-    t = total / steps
+    total, t = time_steps(step, steps, warmup)
     return dict(M=M, N=N, K=K, split_k=sk, weight_copies=copies, eff_weight_bytes=wb,
-                us_per_step=t * 1e6, us_per_launch_events=float(np.mean(per)) * 1e6,
-                gbs=wb / t / 1e9, frac_hbm=wb / t / 1e9 / HBM_PEAK_GBS), d, y
+                us_per_step=t * 1e6, gbs=wb / t / 1e9, frac_hbm=wb / t / 1e9 / HBM_PEAK_GBS), d, y
 
 
 def bench_prefill(name, steps, warmup, variant=None):
@@ -130,10 +142,9 @@ def bench_prefill(name, steps, warmup, variant=None):
     def step(i):
         w4.w4a16_gemm(d.x, d.w[0], d.s[0], y=y, workspace=ws, path=path, variant=variant)
 
-    total, per = time_steps(step, steps, warmup)
-    t = total / steps
+    total, t = time_steps(step, steps, warmup)
     flops = 2.0 * M * N * K
-    return dict(M=M, N=N, K=K, us_per_step=t * 1e6, us_per_launch_events=float(np.mean(per)) * 1e6,
+    return dict(M=M, N=N, K=K, us_per_step=t * 1e6,
                 tflops=flops / t / 1e12, frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS), d, y
 
 
@@ -151,12 +162,10 @@ def bench_grouped(name, steps, warmup, variant=None):
     def step(i):
         w4.w4a16_gemm_grouped(d.x, d.w[0], d.s[0], d.m_sizes, y=y, workspace=ws, variant=variant)
 
-    total, per = time_steps(step, steps, warmup)
-    t = total / steps
+    total, t = time_steps(step, steps, warmup)
     flops = 2.0 * Mt * N * K
     return dict(G=G, M_total=Mt, N=N, K=K, m_sizes=[int(v) for v in c.m_sizes], us_per_step=t * 1e6,
-                us_per_launch_events=float(np.mean(per)) * 1e6, tflops=flops / t / 1e12,
-                frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS), d, y
+                tflops=flops / t / 1e12, frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS), d, y
 
 
 def bench_pack(steps, warmup):
@@ -170,8 +179,7 @@ def bench_pack(steps, warmup):
     def step(i):
         w4.w4a16_pack_int4(q, out=out)
 
-    total, _ = time_steps(step, steps, warmup)
-    t = total / steps
+    total, t = time_steps(step, steps, warmup)
     return dict(rows=N, K=K, us_per_step=t * 1e6, gbs=(N * K * 1.5) / t / 1e9)
 
 
@@ -261,13 +269,18 @@ def main():
     head, _, _ = bench_decode("decode_gemv", args.steps, args.warmup)
     wb = head["eff_weight_bytes"]
     ms_per_step = head["us_per_step"] / 1e3
-    # dominant kernel of the step: the decode GEMV (one launch per step at split_k 1)
-    kern_s = head["us_per_launch_events"] / 1e6
+    # dominant kernel of the step: the decode GEMV, one launch per step at
+    # split_k 1; its average launch duration is the graph replay time / K
+    # (HIP events on the launch stream), so it includes the dispatch gap
+    # between consecutive graph nodes
+    kern_s = head["us_per_step"] / 1e6
     achieved = wb / kern_s / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel="w4a16::gemv_m1_kernel", bytes_per_launch=wb,
-                    launch_us_events=round(head["us_per_launch_events"], 3))
+                    frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=TRAFFIC_DECODE_GEMV["bytes"] if TRAFFIC_DECODE_GEMV else None,
+                    traffic_detail=TRAFFIC_DECODE_GEMV,
+                    kernel="w4a16::gemv_m1_kernel<5, 2, 2>", bytes_per_launch=wb,
+                    launch_us=round(head["us_per_step"], 3))
 
     workloads = {}
     if not args.no_extras:

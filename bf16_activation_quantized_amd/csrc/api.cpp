@@ -32,7 +32,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // GEMV default variant: 1000 * layout (0 = flat 1 KiB runs) + 100 * non-temporal
 // + 10 * prefetch depth + row blocks per wave.
-constexpr int kGemvDefaultVariant = 24;
+constexpr int kGemvDefaultVariant = 1124;
 // Skinny defaults: column tiles per wave and waves per workgroup.
 constexpr int kSkinnyNT = 4;
 constexpr int kSkinnyWaves = 4;

@@ -52,6 +52,11 @@ __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v <
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
+// A 32-bit word as a bf16 pair. Taken by value on purpose: clang's
+// __builtin_bit_cast applied directly to an ext-vector element (v.y) reads the
+// vector's first element instead (observed with ROCm 7.2 clang).
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
 // Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 r = {(__bf16)lo, (__bf16)hi};

@@ -109,8 +109,8 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           t = __builtin_amdgcn_fdot2_f32_bf16(
-              __builtin_bit_cast(bf16x2, magic_pair_interleaved(wd[d], j)),
-              __builtin_bit_cast(bf16x2, xp[i][4 * d + j]), t, false);
+              as_bf16x2(magic_pair_interleaved(wd[d], j)),
+              as_bf16x2(xp[i][4 * d + j]), t, false);
         }
       }
       acc = fmaf(bf16f(sb[i]), t, acc);
@@ -188,6 +188,8 @@ __device__ __forceinline__ void wave_reduce_rows(float (&acc)[R], int lane, floa
   }
 }
 
+constexpr int kMaxChunks = 256;   // 32-k chunks per row-slice (64 groups)
+
 template <int R, int I, int D, int AUX>
 __global__ __launch_bounds__(256) void gemv_flat_kernel(const uint16_t* __restrict__ x,
                                                         const uint8_t* __restrict__ w,
@@ -212,9 +214,22 @@ __global__ __launch_bounds__(256) void gemv_flat_kernel(const uint16_t* __restri
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, (uint32_t)N * (uint32_t)G * 2u);
   const uint32_t rowb = (uint32_t)(K / 2);
 
+  // ---- x of the slice, prepared once per workgroup in LDS: each 32-k chunk
+  // as 16 dwords in the magic-constant pair order plus -136 * its sum
+  __shared__ u32x4 xprep[kMaxChunks * 4];
+  __shared__ float cinl[kMaxChunks];
+  const int tid = threadIdx.x;
+  constexpr int kPrepPer = (kMaxChunks * 4 + 255) / 256;
+  u32x4 xv[kPrepPer];
+#pragma unroll
+  for (int k = 0; k < kPrepPer; ++k) {
+    const int p = tid + 256 * k;   // 16-byte piece p = 4 * chunk + d
+    xv[k] = p < cps * 4 ? ld128(rx, (uint32_t)(g0 * kGroup) * 2u + 16u * (uint32_t)p) : u32x4{0u, 0u, 0u, 0u};
+  }
+
   // static per-lane mapping, identical for every block
   uint32_t woff[I], soff[I];
-  int rib[I];
+  int rib[I], chi[I];
   bool valid[I];
 #pragma unroll
   for (int i = 0; i < I; ++i) {
@@ -223,6 +238,7 @@ __global__ __launch_bounds__(256) void gemv_flat_kernel(const uint16_t* __restri
     const int r = valid[i] ? c / cps : 0;
     const int ch = valid[i] ? c - r * cps : 0;
     rib[i] = r;
+    chi[i] = ch;
     woff[i] = (uint32_t)r * rowb + (uint32_t)g0 * 64u + (uint32_t)ch * 16u;
     soff[i] = ((uint32_t)r * (uint32_t)G + (uint32_t)g0 + (uint32_t)(ch >> 2)) * 2u;
   }
@@ -248,7 +264,29 @@ __global__ __launch_bounds__(256) void gemv_flat_kernel(const uint16_t* __restri
 #pragma unroll
   for (int j = 0; j < D; ++j) issue(wbuf[j], sbuf[j], j);
 
-  // x of this lane's chunks, pair-interleaved, -136 * chunk sum, row masks
+  const uint32_t ones = 0x3F803F80u;   // bf16 (1, 1)
+#pragma unroll
+  for (int k = 0; k < kPrepPer; ++k) {
+    const int p = tid + 256 * k;
+    if (p < cps * 4) {   // whole quads of a chunk are active together (cps * 4 % 4 == 0)
+      const u32x4 v = xv[k];
+      u32x4 o;
+      o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);   // (x0, x4)
+      o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);   // (x1, x5)
+      o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);   // (x2, x6)
+      o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);   // (x3, x7)
+      xprep[p] = o;
+      float sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(ones), 0.0f, false);
+      sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(ones), sx, false);
+      sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), as_bf16x2(ones), sx, false);
+      sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), as_bf16x2(ones), sx, false);
+      sx += __shfl_xor(sx, 1, 4);
+      sx += __shfl_xor(sx, 2, 4);
+      if ((p & 3) == 0) cinl[p >> 2] = -136.0f * sx;
+    }
+  }
+  __syncthreads();
+
   const uint32_t magic = vgpr_const(kMagicPair);
   const uint32_t mask = __builtin_amdgcn_readfirstlane(kNibblePairMask);
   uint32_t xp[I][16];
@@ -256,21 +294,15 @@ __global__ __launch_bounds__(256) void gemv_flat_kernel(const uint16_t* __restri
   float rmask[I][R];
 #pragma unroll
   for (int i = 0; i < I; ++i) {
-    const int c = 64 * i + lane;
-    const int ch = valid[i] ? c - rib[i] * cps : 0;
-    const uint32_t kb = (uint32_t)(g0 * kGroup + 32 * ch) * 2u;
-    float sx = 0.0f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const u32x4 v = valid[i] ? ld128(rx, kb + 16u * d) : u32x4{0u, 0u, 0u, 0u};
-      sx += (bf16lo(v.x) + bf16hi(v.x)) + (bf16lo(v.y) + bf16hi(v.y)) +
-            (bf16lo(v.z) + bf16hi(v.z)) + (bf16lo(v.w) + bf16hi(v.w));
-      xp[i][4 * d + 0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-      xp[i][4 * d + 1] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-      xp[i][4 * d + 2] = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-      xp[i][4 * d + 3] = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+      const u32x4 o = valid[i] ? xprep[4 * chi[i] + d] : u32x4{0u, 0u, 0u, 0u};
+      xp[i][4 * d + 0] = o.x;
+      xp[i][4 * d + 1] = o.y;
+      xp[i][4 * d + 2] = o.z;
+      xp[i][4 * d + 3] = o.w;
     }
-    cinit[i] = -136.0f * sx;
+    cinit[i] = valid[i] ? cinl[chi[i]] : 0.0f;
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) rmask[i][rr] = (valid[i] && rib[i] == rr) ? 1.0f : 0.0f;
   }
@@ -286,14 +318,14 @@ __global__ __launch_bounds__(256) void gemv_flat_kernel(const uint16_t* __restri
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const uint32_t w0 = wd[d], w1 = wd[d] >> 4, w2 = wd[d] >> 8, w3 = wd[d] >> 12;
-        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, and_or_sv(w0, mask, magic)),
-                                           __builtin_bit_cast(bf16x2, xp[i][4 * d + 0]), t, false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, and_or_sv(w1, mask, magic)),
-                                           __builtin_bit_cast(bf16x2, xp[i][4 * d + 1]), t, false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, and_or_sv(w2, mask, magic)),
-                                           __builtin_bit_cast(bf16x2, xp[i][4 * d + 2]), t, false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, and_or_sv(w3, mask, magic)),
-                                           __builtin_bit_cast(bf16x2, xp[i][4 * d + 3]), t, false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or_sv(w0, mask, magic)),
+                                           as_bf16x2(xp[i][4 * d + 0]), t, false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or_sv(w1, mask, magic)),
+                                           as_bf16x2(xp[i][4 * d + 1]), t, false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or_sv(w2, mask, magic)),
+                                           as_bf16x2(xp[i][4 * d + 2]), t, false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or_sv(w3, mask, magic)),
+                                           as_bf16x2(xp[i][4 * d + 3]), t, false);
       }
       const float v = bf16f(sb[i]) * t;
 #pragma unroll

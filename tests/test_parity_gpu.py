@@ -207,8 +207,11 @@ def test_degenerate_zero_outputs(path, M):
     # q == 8 everywhere: the oracle gives exactly 0; the MFMA paths form
     # -136 * sum(x) + sum(136 * x) in two fp32 summation orders, so only a
     # rounding residue (far below the gate's absolute term) may remain
+    # (the gate's cosine is undefined for an all-zero reference, so only its
+    # absolute term, 1e-3, is checked)
     zero_q = DevCase(type(c)(x=c.x, q=np.full_like(c.q, 8), s=c.s))
-    check_gate(_run(zero_q, path=path), np.zeros((M, N)), "q == 8")
+    y8 = oracle.bf16_to_f64(_run(zero_q, path=path))
+    assert np.all(np.isfinite(y8)) and float(np.max(np.abs(y8))) <= 1e-3
     zero_s = DevCase(type(c)(x=c.x, q=c.q, s=np.zeros_like(c.s)))
     assert np.all((_run(zero_s, path=path) & 0x7FFF) == 0)       # s == 0 -> +-0
     zero_x = DevCase(type(c)(x=np.zeros_like(c.x), q=c.q, s=c.s))
