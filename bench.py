@@ -35,15 +35,18 @@ METRIC = "effective weight GB/s at M=1 decode; TFLOP/s at M=1322 prefill (1x MI3
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROTATE_BYTES = 512 << 20
+# the decode GEMV at M=1, N=17408, K=5120, split_k 1 (40 groups per slice ->
+# 2-row blocks, 5 instructions per block; one block in flight; 4 waves with x in LDS)
+DECODE_KERNEL = "w4a16::gemv_mfma_kernel<2, 5, 1, 4, true>"
 # HBM bytes per launch of the decode GEMV from rocprofv3 --pmc (FETCH_SIZE and
 # WRITE_SIZE, KiB per dispatch), scaled by the factors a plain copy kernel of
 # known size reads from the same counters (FETCH x2.00, WRITE x1.00); None
 # when the kernel has changed since the counters were taken
 TRAFFIC_DECODE_GEMV = {
-    "kernel": "w4a16::gemv_m1_kernel<5, 2, 2>",
-    "fetch_kib_counter": 22564.12, "fetch_factor": 2.00,
-    "write_kib_counter": 68.0, "write_factor": 1.00,
-    "bytes": int((22564.12 * 2.00 + 68.0 * 1.00) * 1024),
+    "kernel": DECODE_KERNEL,
+    "fetch_kib_counter": 22537.02, "fetch_factor": 2.00,
+    "write_kib_counter": 68.01, "write_factor": 1.00,
+    "bytes": int((22537.02 * 2.00 + 68.01 * 1.00) * 1024),
 }
 
 
@@ -279,7 +282,7 @@ def main():
                     frac=round(achieved / HBM_PEAK_GBS, 4),
                     traffic=TRAFFIC_DECODE_GEMV["bytes"] if TRAFFIC_DECODE_GEMV else None,
                     traffic_detail=TRAFFIC_DECODE_GEMV,
-                    kernel="w4a16::gemv_m1_kernel<5, 2, 2>", bytes_per_launch=wb,
+                    kernel=DECODE_KERNEL, bytes_per_launch=wb,
                     launch_us=round(head["us_per_step"], 3))
 
     workloads = {}

@@ -21,6 +21,9 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
 
 SOURCES = ["api.cpp", "pack_reduce.hip", "gemv.hip", "skinny.hip", "tile.hip"]
+# the decode kernels keep their small MFMA accumulators in VGPRs (the default
+# heuristic moved them through AGPRs with extra copies)
+EXTRA_FLAGS = {"gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 
@@ -38,6 +41,7 @@ def _flags(src: str):
         common += ["-x", "hip", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
     else:
         common += ["-x", "hip"]  # host-only code that includes hip_runtime.h
+    common += EXTRA_FLAGS.get(src, [])
     return common
 
 

@@ -30,9 +30,10 @@ int32_t pow2_at_least(int64_t v) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// GEMV default variant: 1000 * layout (0 = flat 1 KiB runs) + 100 * non-temporal
-// + 10 * prefetch depth + row blocks per wave.
-constexpr int kGemvDefaultVariant = 1124;
+// GEMV default variant: layout 2 (MFMA diagonal contraction), 4-wave
+// workgroups with x staged in LDS, one weight block in flight per wave, three
+// row blocks per wave (encoding in the dispatcher of gemv.hip).
+constexpr int kGemvDefaultVariant = 2213;
 // Skinny defaults: column tiles per wave and waves per workgroup.
 constexpr int kSkinnyNT = 4;
 constexpr int kSkinnyWaves = 4;

@@ -105,6 +105,34 @@ __device__ __forceinline__ uint32_t magic_pair_natural(uint32_t w, uint32_t w4, 
   return (__builtin_amdgcn_perm(w4, w, sel) & kNibblePairMask) | kMagicPair;
 }
 
+// ---------------------------------------------------------------- DPP sums
+// Cross-lane sums on the VALU with DPP (a few cycles per step) instead of
+// ds_bpermute round trips through the LDS unit.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
+}
+// Sum over each row of 16 lanes; every lane of the row gets the row's sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);   // row_half_mirror
+  v += dpp_f<0x140>(v);   // row_mirror
+  return v;
+}
+// Sum over each half-wave (32 lanes): valid in lanes 16..31 and 48..63.
+__device__ __forceinline__ float half32_sum(float v) {
+  v = row16_sum(v);
+  v += dpp_f<0x142, 0xA>(v);   // row_bcast15 into rows 1 and 3
+  return v;
+}
+// Sum over the whole wave: valid in lanes 48..63.
+__device__ __forceinline__ float wave64_sum(float v) {
+  v = half32_sum(v);
+  v += dpp_f<0x143, 0xC>(v);   // row_bcast31 into rows 2 and 3
+  return v;
+}
+
 // ---------------------------------------------------------------- XCD mapping
 // Workgroups are dispatched to the 8 XCDs round robin (blockIdx % 8). Remap so
 // that each XCD owns a contiguous run of logical tile ids: neighbouring tiles

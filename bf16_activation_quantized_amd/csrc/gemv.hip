@@ -115,14 +115,10 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t* __restrict
       }
       acc = fmaf(bf16f(sb[i]), t, acc);
     }
-    // half-wave reduction (xor offsets stay within 32 lanes)
-    acc += __shfl_xor(acc, 16, 32);
-    acc += __shfl_xor(acc, 8, 32);
-    acc += __shfl_xor(acc, 4, 32);
-    acc += __shfl_xor(acc, 2, 32);
-    acc += __shfl_xor(acc, 1, 32);
+    // half-wave reduction (DPP): the sum lands in lanes 31 and 63
+    acc = half32_sum(acc);
     const int n = hw + r * H;
-    if (hl == 0 && r < nrows) {
+    if (hl == 31 && r < nrows) {
       if (ws == nullptr) y[n] = to_bf16(acc);
       else ws[(size_t)slice * N + n] = acc;
     }
@@ -146,46 +142,13 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t* __restrict
 // 1 KiB run: in instruction i lane l takes 16-byte chunk c = 64 i + l of the
 // block, i.e. row c / cps, chunk c % cps (cps = chunks per row-slice).
 // R = 64 / gcd(cps, 64) rows make the block a whole number I of 1 KiB runs.
-// A lane keeps R row partials; the R sums are formed with a wave-wide
-// reduce-scatter (exchange halves, then tree) and written by lanes 0, 32, ...
+// A lane keeps R row partials; each row is summed over the wave with DPP and
+// written by lane 63.
 template <int R>
-__device__ __forceinline__ void wave_reduce_rows(float (&acc)[R], int lane, float* out_rows) {
-  if (R == 4) {
-    // offset 32: lanes < 32 keep rows 0,1; lanes >= 32 keep rows 2,3
-    const bool hi = lane & 32;
-    float k0 = hi ? acc[2] : acc[0], k1 = hi ? acc[3] : acc[1];
-    float s0 = hi ? acc[0] : acc[2], s1 = hi ? acc[1] : acc[3];
-    k0 += __shfl_xor(s0, 32);
-    k1 += __shfl_xor(s1, 32);
-    // offset 16: lanes with bit 16 keep the second
-    const bool h16 = lane & 16;
-    float k = h16 ? k1 : k0, sv = h16 ? k0 : k1;
-    k += __shfl_xor(sv, 16);
-    k += __shfl_xor(k, 8);
-    k += __shfl_xor(k, 4);
-    k += __shfl_xor(k, 2);
-    k += __shfl_xor(k, 1);
-    out_rows[0] = k;   // lane 0: row 0, lane 16: row 1, lane 32: row 2, lane 48: row 3
-  } else if (R == 2) {
-    const bool hi = lane & 32;
-    float k = hi ? acc[1] : acc[0], sv = hi ? acc[0] : acc[1];
-    k += __shfl_xor(sv, 32);
-    k += __shfl_xor(k, 16);
-    k += __shfl_xor(k, 8);
-    k += __shfl_xor(k, 4);
-    k += __shfl_xor(k, 2);
-    k += __shfl_xor(k, 1);
-    out_rows[0] = k;   // lane 0: row 0, lane 32: row 1
-  } else {
-    float k = acc[0];
-    k += __shfl_xor(k, 32);
-    k += __shfl_xor(k, 16);
-    k += __shfl_xor(k, 8);
-    k += __shfl_xor(k, 4);
-    k += __shfl_xor(k, 2);
-    k += __shfl_xor(k, 1);
-    out_rows[0] = k;
-  }
+__device__ __forceinline__ void wave_reduce_rows(float (&acc)[R]) {
+  // every row's sum over the 64 lanes, valid in lane 63 (DPP, no LDS trips)
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) acc[rr] = wave64_sum(acc[rr]);
 }
 
 constexpr int kMaxChunks = 256;   // 32-k chunks per row-slice (64 groups)
@@ -280,8 +243,8 @@ __global__ __launch_bounds__(256) void gemv_flat_kernel(const uint16_t* __restri
       sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(ones), sx, false);
       sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), as_bf16x2(ones), sx, false);
       sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), as_bf16x2(ones), sx, false);
-      sx += __shfl_xor(sx, 1, 4);
-      sx += __shfl_xor(sx, 2, 4);
+      sx += dpp_f<0xB1>(sx);   // quad_perm [1,0,3,2]
+      sx += dpp_f<0x4E>(sx);   // quad_perm [2,3,0,1]
       if ((p & 3) == 0) cinl[p >> 2] = -136.0f * sx;
     }
   }
@@ -331,13 +294,16 @@ __global__ __launch_bounds__(256) void gemv_flat_kernel(const uint16_t* __restri
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) acc[rr] = fmaf(rmask[i][rr], v, acc[rr]);
     }
-    float red[1];
-    wave_reduce_rows<R>(acc, lane, red);
-    const int rr = R == 4 ? (lane >> 4) : (R == 2 ? (lane >> 5) : 0);
-    const int n = (wv + j * W) * R + rr;
-    if ((lane & (R == 4 ? 15 : (R == 2 ? 31 : 63))) == 0 && j < nb && n < N) {
-      if (ws == nullptr) y[n] = to_bf16(red[0]);
-      else ws[(size_t)slice * N + n] = red[0];
+    wave_reduce_rows<R>(acc);
+    if (lane == 63 && j < nb) {
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const int n = (wv + j * W) * R + rr;
+        if (n < N) {
+          if (ws == nullptr) y[n] = to_bf16(acc[rr]);
+          else ws[(size_t)slice * N + n] = acc[rr];
+        }
+      }
     }
   };
 
@@ -350,6 +316,227 @@ __global__ __launch_bounds__(256) void gemv_flat_kernel(const uint16_t* __restri
       }
     }
   }
+}
+
+// ---------------------------------------------------------------- MFMA layout
+// Same stream as the flat layout (every wave instruction one contiguous 1 KiB
+// run over a block of R rows), but the multiply-add runs on the matrix cores.
+// In instruction i lane L = m + 16 kb reads the 16 bytes of sub-chunk kb of
+// block-group 16 i + m (a block-group is one 128-k group of one row). For the
+// 4 dwords j of those bytes a 16x16x32 MFMA takes A[m][.] = the lane's 8
+// weights as bf16(128 + q) and B[.][n] = the matching 8 x values of lane
+// (n, kb), i.e. of group 16 i + n. D[m][n] then sums W of group m against x
+// of group n over the group's 128 k: the diagonal D[m][m] is group m's dot
+// product (the other entries are unused). The chain starts from -136 * sum(x)
+// of the group; lane (n + 16 q) holds D rows 4q..4q+3 of column n, so the
+// diagonal sits in the 16 lanes with n / 4 == q, register n % 4.
+// x of the slice is prepared once per workgroup in LDS: 16-byte pieces
+// (group g, sub-chunk kb, dword j) in the pair order of the dequant, slot
+// (4 kb + j) XOR-swizzled by (g & 15) so that the 16 lanes of a B read (16
+// consecutive groups, same slot) hit 16 different bank groups.
+template <int R, int I, int D, int WAVES, bool XLDS>
+__global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* __restrict__ x,
+                                                               const uint8_t* __restrict__ w,
+                                                               const uint16_t* __restrict__ s,
+                                                               uint16_t* __restrict__ y,
+                                                               float* __restrict__ ws,
+                                                               int N, int K, int gps) {
+  constexpr int NTHR = 64 * WAVES;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = (int)(blockIdx.x * WAVES + (tid >> 6));
+  const int W = (int)(gridDim.x * WAVES);
+  const int G = K / kGroup;
+  const int slice = blockIdx.y;
+  const int g0 = slice * gps;
+  const int g1 = min(G, g0 + gps);
+  const int Gs = g1 > g0 ? g1 - g0 : 0;        // groups per row in this slice
+  const int nblk = (N + R - 1) / R;
+  const int nb = wv < nblk ? (nblk - 1 - wv) / W + 1 : 0;
+
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint32_t)((uint64_t)N * (uint32_t)K / 2u));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, (uint32_t)N * (uint32_t)G * 2u);
+  const uint32_t rowb = (uint32_t)(K / 2);
+
+  __shared__ u32x4 xlds[kMaxChunks * 4];     // 64 groups x 16 pieces
+  __shared__ float clds[16 * I];              // -136 * group sum, per block-group (0 past the slice)
+
+  // ---- x pieces of the slice (issued first: L2 hits, needed before the weights)
+  constexpr int kPer = (kMaxChunks * 4 + NTHR - 1) / NTHR;
+  u32x4 xv[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int p = tid + NTHR * k;
+    // past the slice the offset is past the extent: the hardware returns 0
+    xv[k] = ld128(rx, p < Gs * 16 ? (uint32_t)(g0 * kGroup) * 2u + 16u * (uint32_t)p : 0xFFFFFFF0u);
+  }
+
+  // ---- static per-lane mapping (identical for every block)
+  const int m = lane & 15, kb = lane >> 4;
+  uint32_t woff[I], soff[I], xaddr[I];
+  float rmask[I][R];
+#pragma unroll
+  for (int i = 0; i < I; ++i) {
+    const int gi = 16 * i + m;                 // block-group of this lane's A row / B column
+    const bool ok = gi < R * Gs;
+    const int r = ok ? gi / Gs : 0;
+    const int gin = ok ? gi - r * Gs : 0;
+    // invalid lanes read past the extent (zeros); their products are masked by rmask
+    woff[i] = ok ? (uint32_t)r * rowb + (uint32_t)(g0 + gin) * 64u + (uint32_t)kb * 16u : 0xFFFFFFF0u;
+    soff[i] = ok ? ((uint32_t)r * (uint32_t)G + (uint32_t)(g0 + gin)) * 2u : 0xFFFFFFF0u;
+    // LDS byte address of piece (gin, kb, j = 0); piece j is at xaddr ^ (16 j)
+    xaddr[i] = (uint32_t)gin * 256u + 16u * ((uint32_t)(4 * kb) ^ (uint32_t)(gin & 15));
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) rmask[i][rr] = (ok && r == rr) ? 1.0f : 0.0f;
+  }
+  // one-hot of the diagonal register: lane (n + 16 q) holds D[4q + j][n]
+  float onehot[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) onehot[j] = (m == 4 * kb + j) ? 1.0f : 0.0f;
+
+  // ---- weight ring (loads are unconditional: rows past N and blocks past the
+  // wave's last one fall past the buffer extent and read 0)
+  u32x4 wbuf[D][I];
+  uint16_t sbuf[D][I];
+  auto issue = [&](u32x4 (&wb)[I], uint16_t (&sb)[I], int jb) {
+    const uint32_t b = (uint32_t)(wv + jb * W);
+    const uint32_t wbase = b * (uint32_t)R * rowb;
+    const uint32_t sbase = b * (uint32_t)R * (uint32_t)G * 2u;
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      wb[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i] == 0xFFFFFFF0u ? woff[i] : wbase + woff[i], 0, 2);
+      sb[i] = ld16(rs, soff[i] == 0xFFFFFFF0u ? soff[i] : sbase + soff[i]);
+    }
+  };
+#pragma unroll
+  for (int jb = 0; jb < D; ++jb) issue(wbuf[jb], sbuf[jb], jb);
+
+  // ---- prepare x in LDS: pair-interleave, swizzle, per-group -136 * sum
+  for (int e = tid; e < 16 * I; e += NTHR) clds[e] = 0.0f;
+  __syncthreads();
+  const uint32_t ones = vgpr_const(0x3F803F80u);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int p = tid + NTHR * k;               // piece p = 16 g + 4 kb + j
+    const u32x4 v = xv[k];                      // zeros past the slice
+    u32x4 o;
+    o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+    o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+    o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+    o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+    const int g = p >> 4, slot = (p & 15) ^ (g & 15);
+    if (p < kMaxChunks * 4) xlds[16 * g + slot] = o;
+    float sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(ones), 0.0f, false);
+    sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(ones), sx, false);
+    sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), as_bf16x2(ones), sx, false);
+    sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), as_bf16x2(ones), sx, false);
+    // 16 consecutive pieces form one group (p = tid + NTHR k, NTHR % 16 == 0):
+    // one DPP row of 16 lanes
+    sx = row16_sum(sx);
+    if (p < Gs * 16 && (p & 15) == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (r * Gs + g < 16 * I) clds[r * Gs + g] = -136.0f * sx;   // per block-group
+    }
+  }
+  __syncthreads();
+
+  const uint32_t magic = vgpr_const(kMagicPair);
+  const uint32_t mask = __builtin_amdgcn_readfirstlane(vgpr_const(kNibblePairMask));
+
+  auto consume = [&](const u32x4 (&wb)[I], const uint16_t (&sb)[I], int jb) {
+    float acc[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) acc[rr] = 0.0f;
+    // x stays in LDS: an opaque copy of the base keeps the compiler from
+    // hoisting these block-invariant reads into ~20 * I registers
+    uint32_t xbase = 0;
+    if (XLDS) asm volatile("v_mov_b32 %0, 0" : "=v"(xbase));
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      // C: -136 * sum(x) of block-groups 16 i + 4 q + (0..3) (rows of D in this lane)
+      f32x4 c = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(clds) + xbase +
+                                                4u * (uint32_t)(16 * i + 4 * kb));
+      const uint32_t wd[4] = {wb[i].x, wb[i].y, wb[i].z, wb[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w0 = wd[j], w1 = wd[j] >> 4, w2 = wd[j] >> 8, w3 = wd[j] >> 12;
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{(w0 & mask) | magic, (w1 & mask) | magic,
+                                                          (w2 & mask) | magic, (w3 & mask) | magic});
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(xlds) + xbase +
+                                                          (xaddr[i] ^ (16u * (uint32_t)j)));
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+      }
+      const float v = (c.x * onehot[0] + c.y * onehot[1]) + (c.z * onehot[2] + c.w * onehot[3]);
+      const float sv = bf16f(sb[i]) * v;
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) acc[rr] = fmaf(rmask[i][rr], sv, acc[rr]);
+    }
+    wave_reduce_rows<R>(acc);
+    if (lane == 63 && jb < nb) {
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const int n = (wv + jb * W) * R + rr;
+        if (n < N) {
+          if (ws == nullptr) y[n] = to_bf16(acc[rr]);
+          else ws[(size_t)slice * N + n] = acc[rr];
+        }
+      }
+    }
+  };
+
+  for (int j0 = 0; j0 < nb; j0 += D) {
+#pragma unroll
+    for (int jb = 0; jb < D; ++jb) {
+      if (j0 + jb < nb) {
+        consume(wbuf[jb], sbuf[jb], j0 + jb);
+        if (j0 + jb + D < nb) issue(wbuf[jb], sbuf[jb], j0 + jb + D);
+      }
+    }
+  }
+}
+
+// MFMA-layout geometry: a block of R rows holds 16 * I groups (R <= 4, I <= 8)
+static bool mfma_geometry(int gs, int* R, int* I) {
+  int g = 16, a = gs;
+  while (a % 2 == 0 && g > 1) { a /= 2; g /= 2; }   // g = 16 / gcd(gs, 16)
+  *R = g;
+  *I = g * gs / 16;
+  return gs > 0 && *R <= 4 && *I >= 1 && *I <= 8;
+}
+
+template <int R, int I>
+static hipError_t launch_mfma_ri(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
+                                 int N, int K, int gps, int sk, int depth, int waves, int bpw, bool xlds,
+                                 hipStream_t stream) {
+  const int nblk = (N + R - 1) / R;
+  const int nw = (nblk + bpw - 1) / bpw;
+#define W4A16_MF(DD, WV, XL)                                                                          \
+  if (depth == DD && waves == WV && xlds == XL) {                                                     \
+    dim3 grid((nw + WV - 1) / WV, sk);                                                                \
+    hipLaunchKernelGGL((gemv_mfma_kernel<R, I, DD, WV, XL>), grid, dim3(64 * WV), 0, stream, x, w, s, y, \
+                       ws, N, K, gps);                                                                \
+    return hipGetLastError();                                                                         \
+  }
+  W4A16_MF(1, 4, false) W4A16_MF(2, 4, false) W4A16_MF(1, 8, false) W4A16_MF(2, 8, false)
+  W4A16_MF(1, 4, true) W4A16_MF(2, 4, true) W4A16_MF(3, 4, true) W4A16_MF(1, 8, true) W4A16_MF(2, 8, true)
+  W4A16_MF(3, 8, true)
+#undef W4A16_MF
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_mfma(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
+                              int N, int K, int gps, int sk, int R, int I, int depth, int waves, int bpw,
+                              bool xlds, hipStream_t stream) {
+#define W4A16_RI(RR, II) \
+  if (R == RR && I == II)  \
+    return launch_mfma_ri<RR, II>(x, w, s, y, ws, N, K, gps, sk, depth, waves, bpw, xlds, stream);
+  W4A16_RI(1, 1) W4A16_RI(1, 2) W4A16_RI(1, 3) W4A16_RI(1, 4)
+  W4A16_RI(2, 1) W4A16_RI(2, 3) W4A16_RI(2, 5) W4A16_RI(2, 7)
+  W4A16_RI(4, 1) W4A16_RI(4, 3) W4A16_RI(4, 5) W4A16_RI(4, 7)
+#undef W4A16_RI
+  return hipErrorInvalidValue;
 }
 
 // flat-layout geometry for a slice of `cps` chunks per row; false if it does
@@ -427,6 +614,8 @@ static hipError_t launch_gemv_cpl(const uint16_t* x, const uint8_t* w, const uin
   return hipErrorInvalidValue;
 }
 
+constexpr int kHalfwaveFallback = 124;
+
 bool gemv_flat_fits(int gps) {
   int R, I;
   return flat_geometry(gps * 4, &R, &I);
@@ -435,17 +624,29 @@ bool gemv_flat_fits(int gps) {
 hipError_t launch_gemv_m1(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y,
                           float* ws, int N, int K, int gps, int sk, int variant,
                           hipStream_t stream) {
-  // variant: 1000 * layout (0 flat, 1 half-wave) + 100 * non-temporal
-  //          + 10 * prefetch depth + blocks (flat) / rows (half-wave) per wave
+  // variant: 1000 * layout (0 flat, 1 half-wave, 2 MFMA) + layout digits;
+  // flat and half-wave: 100 * non-temporal + 10 * prefetch depth + blocks
+  // (flat) / rows (half-wave) per wave
   const int layout = (variant / 1000) % 10;
   int R = 0, I = 0;
+  if (layout == 2 && mfma_geometry(gps, &R, &I)) {
+    // 2000 + 100 * (waves / 4 - 1 + 2 * x-in-LDS) + 10 * prefetch depth + row blocks per wave
+    const int h = (variant / 100) % 10;
+    const int waves = (h & 1) ? 8 : 4;
+    const bool xlds = (h & 2) != 0;
+    const int depth = (variant / 10) % 10 > 0 ? (variant / 10) % 10 : 2;
+    const int bpw = variant % 10 > 0 ? variant % 10 : 4;
+    return launch_mfma(x, w, s, y, ws, N, K, gps, sk, R, I, depth, waves, bpw, xlds, stream);
+  }
   if (layout == 0 && flat_geometry(gps * 4, &R, &I)) {
     const int nt = (variant / 100) % 10;
     const int depth = (variant / 10) % 10 > 0 ? (variant / 10) % 10 : 2;
     const int bpw = variant % 10 > 0 ? variant % 10 : 4;
     return launch_flat(x, w, s, y, ws, N, K, gps, sk, R, I, depth, nt, bpw, stream);
   }
-  const int v = variant % 1000;
+  // the half-wave kernel takes every slice of at most 64 groups; an MFMA
+  // variant whose slice length has no MFMA geometry runs its default
+  const int v = layout == 2 ? kHalfwaveFallback : variant % 1000;
   const int cpl = (gps * 4 + 31) / 32;   // chunks per lane in a slice
   switch (cpl) {
     case 1: return launch_gemv_cpl<1>(x, w, s, y, ws, N, K, gps, sk, v, stream);

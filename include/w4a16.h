@@ -180,14 +180,24 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  * Explicit kernel selection, for tests and benchmarks that must exercise a
  * particular kernel at a shape where the automatic choice would pick another.
  * The result of a forced path still satisfies the same contract.
- *   path   : 0 = automatic, 1 = M == 1 GEMV (weights streamed by half-waves,
- *            x in registers, at most 64 groups per split-K slice),
+ *   path   : 0 = automatic, 1 = M == 1 GEMV (at most 64 groups per split-K
+ *            slice),
  *            2 = M <= 16 MFMA 16x16x32 decode kernel, 3 = MFMA 32x32x16 tile
  *            kernel (LDS double-buffered; the only path of the grouped call)
- *   variant: -1 = default for the path; otherwise path 1: 100 * nt +
- *            10 * depth + rows, with nt 1 = non-temporal weight loads, depth
- *            1..4 = weight rows in flight per half-wave, rows 1..9 = target
- *            rows per half-wave (sets the grid size); path 2: 10 * waves_per_workgroup +
+ *   variant: -1 = default for the path; otherwise
+ *            path 1: 1000 * layout + layout digits.
+ *              layout 2 (default, MFMA diagonal contraction of 16 groups per
+ *              instruction): 2000 + 100 * h + 10 * depth + blocks, with
+ *              h = (waves_per_workgroup / 4 - 1) + 2 * x_staged_in_lds,
+ *              depth 1..3 = weight blocks in flight per wave (1..2 without
+ *              LDS staging), blocks 1..9 = row blocks per wave (sets the grid).
+ *              Slice lengths with no MFMA geometry run layout 1 variant 124.
+ *              layout 0 (1 KiB weight runs per wave) and layout 1 (one row
+ *              per half-wave, x in registers): 100 * nt + 10 * depth + rows,
+ *              nt 1 = non-temporal weight loads, depth 1..3 (layout 0) or
+ *              1..4 (layout 1) = loads in flight, rows 1..9 = rows or row
+ *              blocks per wave;
+ *            path 2: 10 * waves_per_workgroup +
  *            column_tiles_per_wave (41, 42, 44, 81, 82, 84); path 3: tile
  *            configuration index (0: 128x256, 1: 128x128).
  * An unavailable combination (e.g. path 1 with M != 1, path 2 with M > 16)

@@ -45,10 +45,12 @@ def test_pack_bit_exact(rows, K):
 # ------------------------------------------------------------------ decode GEMV (M = 1)
 
 GEMV_CASES = [
-    # N, K, split_k, variant (1000 * layout [0 flat, 1 half-wave] + 100 * non-temporal
-    #                         + 10 * prefetch depth + row blocks (rows) per wave)
-    (256, 512, 0, None),      # the tiny workload (flat, 4-row blocks)
-    (17408, 5120, 1, None),   # the decode workload (flat, 2-row blocks)
+    # N, K, split_k, variant (1000 * layout [0 flat, 1 half-wave, 2 MFMA] + layout digits;
+    #   flat / half-wave: 100 * non-temporal + 10 * prefetch depth + row blocks (rows) per wave)
+    # None = the default (MFMA 2213 where the slice length has an MFMA geometry,
+    # otherwise half-wave 124)
+    (256, 512, 0, None),      # the tiny workload (MFMA, 4-row blocks)
+    (17408, 5120, 1, None),   # the decode workload (MFMA, 2-row blocks)
     (1001, 5120, 1, 131),     # odd N: last 2-row block half outside
     (999, 8192, 1, 22),       # flat, 1-row blocks, 4 runs of 1 KiB
     (777, 4096, 1, 113),      # flat, 1-row blocks, 2 runs
@@ -68,6 +70,20 @@ GEMV_CASES = [
     (3, 5120, 1, None),       # fewer rows than one wave's blocks
     (40, 10240, 2, 24),       # flat with split-K: 40 groups per slice
     (41, 7680, 2, None),      # 30 groups per slice -> half-wave fallback
+    # MFMA layout: 2000 + 100 * (waves / 4 - 1 + 2 * x-in-LDS) + 10 * depth + row blocks per wave
+    (17408, 5120, 1, 2024),   # 2-row blocks, 5 runs
+    (17408, 5120, 1, 2314),   # x in LDS, 8 waves
+    (1001, 5120, 1, 2113),
+    (999, 8192, 1, 2022),     # 1-row blocks, 4 runs
+    (777, 4096, 1, 2331),     # 1-row blocks, 2 runs
+    (1003, 2560, 1, 2224),    # 4-row blocks, 5 runs
+    (1002, 1024, 1, 2112),    # 2-row blocks, 1 run
+    (256, 512, 1, 2221),      # 4-row blocks, 1 run (the tiny shape)
+    (40, 10240, 2, 2324),     # with split-K
+    (5, 5120, 1, 2011),       # fewer rows than one block per wave
+    (1000, 640, 1, 2213),     # 5 groups per slice: no MFMA geometry -> half-wave 124
+    (17408, 5120, 1, 122),    # flat layout at the decode shape
+    (17408, 5120, 1, 1124),   # half-wave layout at the decode shape
 ]
 
 
