@@ -30,10 +30,10 @@ int32_t pow2_at_least(int64_t v) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// GEMV default variant: layout 2 (MFMA diagonal contraction), 4-wave
-// workgroups with x staged in LDS, one weight block in flight per wave, three
-// row blocks per wave (encoding in the dispatcher of gemv.hip).
-constexpr int kGemvDefaultVariant = 2213;
+// GEMV default variant: layout 2 (MFMA diagonal contraction), one 8-wave
+// workgroup per compute unit, x held in registers, one weight block in
+// flight per wave (encoding in the dispatcher of gemv.hip).
+constexpr int kGemvDefaultVariant = 2110;
 // Skinny defaults: column tiles per wave and waves per workgroup.
 constexpr int kSkinnyNT = 4;
 constexpr int kSkinnyWaves = 4;

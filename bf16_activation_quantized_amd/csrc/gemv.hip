@@ -25,6 +25,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
+
 namespace w4a16 {
 
 template <int CPL, int D, int AUX>
@@ -344,15 +346,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
   constexpr int NTHR = 64 * WAVES;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = (int)(blockIdx.x * WAVES + (tid >> 6));
-  const int W = (int)(gridDim.x * WAVES);
+  const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave in the workgroup
   const int G = K / kGroup;
   const int slice = blockIdx.y;
   const int g0 = slice * gps;
   const int g1 = min(G, g0 + gps);
   const int Gs = g1 > g0 ? g1 - g0 : 0;        // groups per row in this slice
+  // the workgroup owns a contiguous, balanced range of row blocks; its waves
+  // take them in turn (block b_lo + wq + WAVES * j)
   const int nblk = (N + R - 1) / R;
-  const int nb = wv < nblk ? (nblk - 1 - wv) / W + 1 : 0;
+  const int b_lo = (int)(((int64_t)blockIdx.x * nblk) / gridDim.x);
+  const int b_hi = (int)(((int64_t)(blockIdx.x + 1) * nblk) / gridDim.x);
+  const int nb = wq < b_hi - b_lo ? (b_hi - b_lo - 1 - wq) / WAVES + 1 : 0;
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint32_t)((uint64_t)N * (uint32_t)K / 2u));
@@ -372,9 +377,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
     xv[k] = ld128(rx, p < Gs * 16 ? (uint32_t)(g0 * kGroup) * 2u + 16u * (uint32_t)p : 0xFFFFFFF0u);
   }
 
+  // every wave's x requests enter the compute unit's memory queue ahead of
+  // the first weight request of any wave of the workgroup
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
   // ---- static per-lane mapping (identical for every block)
   const int m = lane & 15, kb = lane >> 4;
-  uint32_t woff[I], soff[I], xaddr[I];
+  uint32_t woff[I], soff[I], xaddr[I], sshift[I];
   float rmask[I][R];
 #pragma unroll
   for (int i = 0; i < I; ++i) {
@@ -385,6 +396,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
     // invalid lanes read past the extent (zeros); their products are masked by rmask
     woff[i] = ok ? (uint32_t)r * rowb + (uint32_t)(g0 + gin) * 64u + (uint32_t)kb * 16u : 0xFFFFFFF0u;
     soff[i] = ok ? ((uint32_t)r * (uint32_t)G + (uint32_t)(g0 + gin)) * 2u : 0xFFFFFFF0u;
+    // scales are read as the aligned 32-bit word that holds them (16-bit
+    // loads get packed in pairs by the compiler, which ties the wait of one
+    // block to the next one's loads); in block 0 the lane's scale is the low
+    // half (shift 16 into the bf16 position) when its offset is 4-aligned
+    sshift[i] = (soff[i] & 2u) ? 0u : 16u;
     // LDS byte address of piece (gin, kb, j = 0); piece j is at xaddr ^ (16 j)
     xaddr[i] = (uint32_t)gin * 256u + 16u * ((uint32_t)(4 * kb) ^ (uint32_t)(gin & 15));
 #pragma unroll
@@ -395,19 +411,26 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
 #pragma unroll
   for (int j = 0; j < 4; ++j) onehot[j] = (m == 4 * kb + j) ? 1.0f : 0.0f;
 
-  // ---- weight ring (loads are unconditional: rows past N and blocks past the
-  // wave's last one fall past the buffer extent and read 0)
+  // ---- weight ring. Every slot is refilled after it is consumed, also past
+  // the wave's last block: such loads (and those of rows past N) use an
+  // offset past the buffer extent, which the hardware answers with zeros and
+  // no memory traffic, so the ring has the same wait counts on every trip.
   u32x4 wbuf[D][I];
-  uint16_t sbuf[D][I];
-  auto issue = [&](u32x4 (&wb)[I], uint16_t (&sb)[I], int jb) {
-    const uint32_t b = (uint32_t)(wv + jb * W);
-    const uint32_t wbase = b * (uint32_t)R * rowb;
-    const uint32_t sbase = b * (uint32_t)R * (uint32_t)G * 2u;
+  uint32_t sbuf[D][I];
+  auto issue = [&](u32x4 (&wb)[I], uint32_t (&sb)[I], int jb) {
+    // a dead block (or lane) has base (or offset) 0xFFFFFFF0; the saturating
+    // add keeps any sum with it at or above that, past every extent
+    const bool live = jb < nb;
+    const uint32_t b = (uint32_t)(b_lo + wq + jb * WAVES);
+    const uint32_t wbase = live ? b * (uint32_t)R * rowb : 0xFFFFFFF0u;
+    const uint32_t sbase = live ? b * (uint32_t)R * (uint32_t)G * 2u : 0xFFFFFFF0u;
 #pragma unroll
-    for (int i = 0; i < I; ++i) {
-      wb[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i] == 0xFFFFFFF0u ? woff[i] : wbase + woff[i], 0, 2);
-      sb[i] = ld16(rs, soff[i] == 0xFFFFFFF0u ? soff[i] : sbase + soff[i]);
-    }
+    for (int i = 0; i < I; ++i) sb[i] = ld32(rs, __builtin_elementwise_add_sat(sbase, soff[i]) & ~3u);
+#pragma unroll
+    for (int i = 0; i < I; ++i)
+      wb[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, __builtin_elementwise_add_sat(wbase, woff[i]), 0, 2);
+    // keep one block's loads together, in issue order
+    __builtin_amdgcn_sched_barrier(0);
   };
 #pragma unroll
   for (int jb = 0; jb < D; ++jb) issue(wbuf[jb], sbuf[jb], jb);
@@ -445,31 +468,78 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
   const uint32_t magic = vgpr_const(kMagicPair);
   const uint32_t mask = __builtin_amdgcn_readfirstlane(vgpr_const(kNibblePairMask));
 
-  auto consume = [&](const u32x4 (&wb)[I], const uint16_t (&sb)[I], int jb) {
+  // x in registers (XLDS false): every lane reads its B operands and initial
+  // C once from LDS; the empty asm makes them opaque, so the compiler keeps
+  // them live across blocks instead of re-reading LDS per block
+  constexpr int IR = XLDS ? 1 : I;
+  u32x4 xr[IR][4];
+  f32x4 cr[IR];
+  if constexpr (!XLDS) {
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      cr[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(clds) +
+                                              4u * (uint32_t)(16 * i + 4 * kb));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xr[i][j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(xlds) +
+                                                   (xaddr[i] ^ (16u * (uint32_t)j)));
+    }
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      asm volatile("" : "+v"(cr[i]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(xr[i][j]));
+    }
+  }
+
+  auto consume = [&](const u32x4 (&wb)[I], const uint32_t (&sb)[I], int jb) {
+    // block b's scale offsets are block 0's + b * R * G * 2: when R * G is odd
+    // and b is odd, every lane's scale sits in the other half of its word
+    const uint32_t flip = ((uint32_t)(b_lo + wq + jb * WAVES) & (uint32_t)(R * G) & 1u) << 4;
     float acc[R];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) acc[rr] = 0.0f;
-    // x stays in LDS: an opaque copy of the base keeps the compiler from
-    // hoisting these block-invariant reads into ~20 * I registers
+    // x in LDS: an opaque copy of the base keeps the compiler from hoisting
+    // these block-invariant reads into ~20 * I registers
     uint32_t xbase = 0;
     if (XLDS) asm volatile("v_mov_b32 %0, 0" : "=v"(xbase));
+    // B operands (x) and initial C (-136 * sum(x) of block-groups 16 i + 4 q
+    // + 0..3, the rows of D in this lane) of instruction group i; with x in
+    // LDS, group i + 1's reads are issued before group i's MFMAs
+    bf16x8 bq[2][4];
+    f32x4 cq[2];
+    auto lds_operands = [&](int i, bf16x8 (&bb)[4], f32x4& cc) {
+      if constexpr (XLDS) {
+        cc = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(clds) + xbase +
+                                             4u * (uint32_t)(16 * i + 4 * kb));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bb[j] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(xlds) + xbase +
+                                                   (xaddr[i] ^ (16u * (uint32_t)j)));
+      } else {
+        cc = cr[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bb[j] = __builtin_bit_cast(bf16x8, xr[i][j]);
+      }
+    };
+    lds_operands(0, bq[0], cq[0]);
 #pragma unroll
     for (int i = 0; i < I; ++i) {
-      // C: -136 * sum(x) of block-groups 16 i + 4 q + (0..3) (rows of D in this lane)
-      f32x4 c = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(clds) + xbase +
-                                                4u * (uint32_t)(16 * i + 4 * kb));
+      if (i + 1 < I) {
+        lds_operands(i + 1, bq[(i + 1) & 1], cq[(i + 1) & 1]);
+        if (XLDS) __builtin_amdgcn_sched_barrier(0);
+      }
+      f32x4 c = cq[i & 1];
       const uint32_t wd[4] = {wb[i].x, wb[i].y, wb[i].z, wb[i].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t w0 = wd[j], w1 = wd[j] >> 4, w2 = wd[j] >> 8, w3 = wd[j] >> 12;
         const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{(w0 & mask) | magic, (w1 & mask) | magic,
                                                           (w2 & mask) | magic, (w3 & mask) | magic});
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(xlds) + xbase +
-                                                          (xaddr[i] ^ (16u * (uint32_t)j)));
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[i & 1][j], c, 0, 0, 0);
       }
       const float v = (c.x * onehot[0] + c.y * onehot[1]) + (c.z * onehot[2] + c.w * onehot[3]);
-      const float sv = bf16f(sb[i]) * v;
+      const float sv = __uint_as_float((sb[i] << (sshift[i] ^ flip)) & 0xFFFF0000u) * v;
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) acc[rr] = fmaf(rmask[i][rr], sv, acc[rr]);
     }
@@ -477,7 +547,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
     if (lane == 63 && jb < nb) {
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
-        const int n = (wv + jb * W) * R + rr;
+        const int n = (b_lo + wq + jb * WAVES) * R + rr;
         if (n < N) {
           if (ws == nullptr) y[n] = to_bf16(acc[rr]);
           else ws[(size_t)slice * N + n] = acc[rr];
@@ -489,10 +559,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
   for (int j0 = 0; j0 < nb; j0 += D) {
 #pragma unroll
     for (int jb = 0; jb < D; ++jb) {
-      if (j0 + jb < nb) {
-        consume(wbuf[jb], sbuf[jb], j0 + jb);
-        if (j0 + jb + D < nb) issue(wbuf[jb], sbuf[jb], j0 + jb + D);
-      }
+      if (j0 + jb < nb) consume(wbuf[jb], sbuf[jb], j0 + jb);
+      issue(wbuf[jb], sbuf[jb], j0 + jb + D);
     }
   }
 }
@@ -506,22 +574,50 @@ static bool mfma_geometry(int gs, int* R, int* I) {
   return gs > 0 && *R <= 4 && *I >= 1 && *I <= 8;
 }
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+// Instances that fit the register budget of their occupancy without spills
+// (a 12-wave workgroup leaves 170 VGPRs per wave, a 16-wave one 128).
+template <int R, int I, int D, int WV, bool XL>
+constexpr bool mfma_fits() {
+  if (WV == 16) return XL && D == 1 && R * I <= 10;
+  if (WV == 12) return XL ? !(D == 2 && I == 7) : (D == 1 && I <= 3);
+  if (WV == 8) return XL || !(D == 2 && I == 7);
+  return true;
+}
+
 template <int R, int I>
 static hipError_t launch_mfma_ri(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                                  int N, int K, int gps, int sk, int depth, int waves, int bpw, bool xlds,
                                  hipStream_t stream) {
   const int nblk = (N + R - 1) / R;
-  const int nw = (nblk + bpw - 1) / bpw;
+  // bpw 0: one workgroup per compute unit; otherwise bpw row blocks per wave
+  const int per_wg = waves * (bpw > 0 ? bpw : 1);
+  int gx = (nblk + per_wg - 1) / per_wg;
+  if (bpw == 0) gx = std::min(cu_count(), (nblk + waves - 1) / waves);
+  if (gx < 1) gx = 1;
 #define W4A16_MF(DD, WV, XL)                                                                          \
-  if (depth == DD && waves == WV && xlds == XL) {                                                     \
-    dim3 grid((nw + WV - 1) / WV, sk);                                                                \
-    hipLaunchKernelGGL((gemv_mfma_kernel<R, I, DD, WV, XL>), grid, dim3(64 * WV), 0, stream, x, w, s, y, \
-                       ws, N, K, gps);                                                                \
-    return hipGetLastError();                                                                         \
+  if constexpr (mfma_fits<R, I, DD, WV, XL>()) {                                                           \
+    if (depth == DD && waves == WV && xlds == XL) {                                                   \
+      hipLaunchKernelGGL((gemv_mfma_kernel<R, I, DD, WV, XL>), dim3(gx, sk), dim3(64 * WV), 0, stream, x, w, \
+                         s, y, ws, N, K, gps);                                                        \
+      return hipGetLastError();                                                                       \
+    }                                                                                                 \
   }
-  W4A16_MF(1, 4, false) W4A16_MF(2, 4, false) W4A16_MF(1, 8, false) W4A16_MF(2, 8, false)
+  W4A16_MF(1, 4, false) W4A16_MF(2, 4, false) W4A16_MF(1, 8, false) W4A16_MF(2, 8, false) W4A16_MF(1, 12, false)
   W4A16_MF(1, 4, true) W4A16_MF(2, 4, true) W4A16_MF(3, 4, true) W4A16_MF(1, 8, true) W4A16_MF(2, 8, true)
-  W4A16_MF(3, 8, true)
+  W4A16_MF(1, 12, true) W4A16_MF(2, 12, true) W4A16_MF(1, 16, true)
 #undef W4A16_MF
   return hipErrorInvalidValue;
 }
@@ -630,12 +726,13 @@ hipError_t launch_gemv_m1(const uint16_t* x, const uint8_t* w, const uint16_t* s
   const int layout = (variant / 1000) % 10;
   int R = 0, I = 0;
   if (layout == 2 && mfma_geometry(gps, &R, &I)) {
-    // 2000 + 100 * (waves / 4 - 1 + 2 * x-in-LDS) + 10 * prefetch depth + row blocks per wave
+    // 2000 + 100 * (4 * x-in-LDS + waves / 4 - 1) + 10 * prefetch depth
+    //      + row blocks per wave (0: one workgroup per compute unit)
     const int h = (variant / 100) % 10;
-    const int waves = (h & 1) ? 8 : 4;
-    const bool xlds = (h & 2) != 0;
-    const int depth = (variant / 10) % 10 > 0 ? (variant / 10) % 10 : 2;
-    const int bpw = variant % 10 > 0 ? variant % 10 : 4;
+    const int waves = 4 * ((h & 3) + 1);
+    const bool xlds = (h & 4) != 0;
+    const int depth = (variant / 10) % 10 > 0 ? (variant / 10) % 10 : 1;
+    const int bpw = variant % 10;
     return launch_mfma(x, w, s, y, ws, N, K, gps, sk, R, I, depth, waves, bpw, xlds, stream);
   }
   if (layout == 0 && flat_geometry(gps * 4, &R, &I)) {

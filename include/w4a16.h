@@ -188,9 +188,12 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  *            path 1: 1000 * layout + layout digits.
  *              layout 2 (default, MFMA diagonal contraction of 16 groups per
  *              instruction): 2000 + 100 * h + 10 * depth + blocks, with
- *              h = (waves_per_workgroup / 4 - 1) + 2 * x_staged_in_lds,
- *              depth 1..3 = weight blocks in flight per wave (1..2 without
- *              LDS staging), blocks 1..9 = row blocks per wave (sets the grid).
+ *              h = 4 * x_staged_in_lds + (waves_per_workgroup / 4 - 1)
+ *              (waves 4, 8, 12, 16; x held in registers otherwise),
+ *              depth 1..3 = weight blocks in flight per wave, blocks 1..9 =
+ *              row blocks per wave (sets the grid), 0 = one workgroup per
+ *              compute unit. Combinations that would not fit the register
+ *              budget of their occupancy are not built (W4A16_ERR_LAUNCH).
  *              Slice lengths with no MFMA geometry run layout 1 variant 124.
  *              layout 0 (1 KiB weight runs per wave) and layout 1 (one row
  *              per half-wave, x in registers): 100 * nt + 10 * depth + rows,

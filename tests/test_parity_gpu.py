@@ -47,7 +47,7 @@ def test_pack_bit_exact(rows, K):
 GEMV_CASES = [
     # N, K, split_k, variant (1000 * layout [0 flat, 1 half-wave, 2 MFMA] + layout digits;
     #   flat / half-wave: 100 * non-temporal + 10 * prefetch depth + row blocks (rows) per wave)
-    # None = the default (MFMA 2213 where the slice length has an MFMA geometry,
+    # None = the default (MFMA 2110 where the slice length has an MFMA geometry,
     # otherwise half-wave 124)
     (256, 512, 0, None),      # the tiny workload (MFMA, 4-row blocks)
     (17408, 5120, 1, None),   # the decode workload (MFMA, 2-row blocks)
@@ -70,17 +70,31 @@ GEMV_CASES = [
     (3, 5120, 1, None),       # fewer rows than one wave's blocks
     (40, 10240, 2, 24),       # flat with split-K: 40 groups per slice
     (41, 7680, 2, None),      # 30 groups per slice -> half-wave fallback
-    # MFMA layout: 2000 + 100 * (waves / 4 - 1 + 2 * x-in-LDS) + 10 * depth + row blocks per wave
-    (17408, 5120, 1, 2024),   # 2-row blocks, 5 runs
-    (17408, 5120, 1, 2314),   # x in LDS, 8 waves
-    (1001, 5120, 1, 2113),
-    (999, 8192, 1, 2022),     # 1-row blocks, 4 runs
-    (777, 4096, 1, 2331),     # 1-row blocks, 2 runs
-    (1003, 2560, 1, 2224),    # 4-row blocks, 5 runs
-    (1002, 1024, 1, 2112),    # 2-row blocks, 1 run
-    (256, 512, 1, 2221),      # 4-row blocks, 1 run (the tiny shape)
-    (40, 10240, 2, 2324),     # with split-K
+    # MFMA layout: 2000 + 100 * (4 * x-in-LDS + waves / 4 - 1) + 10 * depth
+    #              + row blocks per wave (0: one workgroup per compute unit)
+    (17408, 5120, 1, 2024),   # 2-row blocks, 5 instructions, x in registers
+    (17408, 5120, 1, 2514),   # x in LDS, 8 waves
+    (17408, 5120, 1, 2610),   # x in LDS, 12 waves, one workgroup per CU
+    (17408, 5120, 1, 2620),
+    (17408, 5120, 1, 2710),   # 16 waves
+    (17408, 5120, 1, 2110),   # 8 waves, x in registers, one workgroup per CU
+    (17408, 5120, 1, 2120),
+    (1001, 5120, 1, 2115),
+    (1003, 2560, 1, 2110),    # 4-row blocks, 5 instructions
+    (1002, 1024, 1, 2210),    # 12 waves, x in registers (2-row blocks, 1 instruction)
+    (1001, 5120, 1, 2413),
+    (999, 8192, 1, 2022),     # 1-row blocks, 4 instructions
+    (777, 4096, 1, 2431),     # 1-row blocks, 2 instructions, depth 3
+    (1003, 2560, 1, 2424),    # 4-row blocks, 5 instructions
+    (1002, 1024, 1, 2012),    # 2-row blocks, 1 instruction
+    (1002, 1024, 1, 2610),
+    (256, 512, 1, 2421),      # 4-row blocks, 1 instruction (the tiny shape)
+    (256, 512, 1, 2610),      # fewer blocks than one workgroup per CU can take
+    (40, 10240, 2, 2524),     # with split-K
+    (40, 10240, 2, 2610),
     (5, 5120, 1, 2011),       # fewer rows than one block per wave
+    (5, 5120, 1, 2710),
+    (33, 8192, 4, 2620),      # split-K, 16 groups per slice, 1-row blocks
     (1000, 640, 1, 2213),     # 5 groups per slice: no MFMA geometry -> half-wave 124
     (17408, 5120, 1, 122),    # flat layout at the decode shape
     (17408, 5120, 1, 1124),   # half-wave layout at the decode shape
