@@ -20,10 +20,12 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
 
-SOURCES = ["api.cpp", "pack_reduce.hip", "gemv.hip", "skinny.hip", "tile.hip"]
-# the decode kernels keep their small MFMA accumulators in VGPRs (the default
-# heuristic moved them through AGPRs with extra copies)
-EXTRA_FLAGS = {"gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCES = ["api.cpp", "pack_reduce.hip", "gemv.hip", "skinny.hip", "tile.hip", "prefill.hip"]
+# MFMA accumulators that the VALU reads (diagonal extraction, per-group
+# rescale) stay in VGPRs (the default heuristic moved them through AGPRs with
+# extra copies)
+EXTRA_FLAGS = {"gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 

@@ -85,9 +85,11 @@ struct Plan {
   int64_t ld;        // row stride of the row sums
 };
 
+// Tile configuration 2 (LDS-DMA staging, 8 waves of 128 x 32, tile.hip).
 int default_tile_cfg(int64_t M, int64_t N) {
   (void)M;
-  return N >= 4096 ? 0 : 1;
+  (void)N;
+  return 2;
 }
 
 w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg, Plan* p) {

@@ -25,6 +25,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
 }
 
+// Scales read as the aligned 32-bit word that holds them: the buffer starts
+// at the (16-byte aligned) tensor base and its extent is rounded up to a
+// multiple of 4. The at most 2 bytes past the tensor lie in the same aligned
+// word as its last scale, hence in a mapped page; without the rounding, an
+// odd element count would make the word of the last scale partly out of range
+// and the hardware would return 0 for all of it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_scale_rsrc(const uint16_t* s, uint32_t count) {
+  return make_rsrc(s, (count * 2u + 3u) & ~3u);
+}
+
 __device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }

@@ -361,7 +361,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint32_t)((uint64_t)N * (uint32_t)K / 2u));
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, (uint32_t)N * (uint32_t)G * 2u);
+  const __amdgpu_buffer_rsrc_t rs = make_scale_rsrc(s, (uint32_t)N * (uint32_t)G);
   const uint32_t rowb = (uint32_t)(K / 2);
 
   __shared__ u32x4 xlds[kMaxChunks * 4];     // 64 groups x 16 pieces

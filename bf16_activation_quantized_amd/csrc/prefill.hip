@@ -1,0 +1,332 @@
+// Prefill / grouped W4A16 GEMM for gfx950 with LDS-DMA staging and in-register
+// dequantisation.
+//
+// Numerics are those of the tile kernel: the weight operand is bf16(128 + q),
+// exact, from the magic-constant OR ("[ROCm][Kernel] W4A16 skinny GEMM:
+// hand-asm kernel for gfx1151", section 1); each 128-group's MFMA chain of a
+// 16x16 output tile starts from -136 * sum_{k in g} x[m, k] (row sums from the
+// pre-pass), so after the group's 4 MFMA steps it holds sum_k x * (q - 8) in
+// fp32, which is scaled by the column's bf16 scale and added to the fp32
+// accumulator. No weight is ever rounded.
+//
+// Structure (one 256-thread workgroup per 128 x 256 output tile, 4 waves of
+// 128 x 64; one workgroup per compute unit):
+//  * one K-stage = one 128-group: X [128 rows, 128 k] bf16 (32 KiB), the
+//    packed weights [256 rows, 64 B] (16 KiB, still 4-bit) and the 128 row
+//    sums; NSTAGE stages in LDS, filled by buffer loads that write LDS
+//    directly (no registers, no VALU), issued NSTAGE - 1 groups ahead;
+//  * each wave reads its 64 columns of packed weights once per group and
+//    dequantises them in registers (64 VGPRs of bf16 B operands), then sweeps
+//    the 8 row tiles of 16: 4 MFMA 16x16x32 steps per (row tile, column tile),
+//    4 chains interleaved, one rescale FMA per output element per group;
+//  * within a group the MFMA k order is permuted: lane (r, kb) of step st
+//    holds k = 32 kb + 8 st + 0..7 for both operands, so one lane's four steps
+//    of packed weights are one 16-byte LDS read;
+//  * LDS rows are XOR-swizzled in 16-byte chunks (X by row & 7, weights by
+//    (row >> 1) & 3): the DMA lanes fetch the chunk that belongs at their LDS
+//    slot, and the MFMA operand reads are bank-conflict free;
+//  * one barrier per group, after an explicit wait for the next group's DMA.
+// The M tail and N tail read zeros through the exact buffer extents; stores
+// past the last row are dropped and columns >= N are skipped.
+#include "common.hpp"
+#include "launch.hpp"
+#include "tilemap.hpp"
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int kPM = 128;                    // rows per tile
+constexpr int kPN = 256;                    // columns per tile (4 waves x 64)
+constexpr int kXStage = kPM * 256;          // X: 128 rows x 128 k x 2 B
+constexpr int kWStage = kPN * 64;           // packed W: 256 rows x 128 k / 2
+constexpr int kRStage = kPM * 4;            // -136 * row sums: 128 fp32
+constexpr int kStage = kXStage + kWStage + kRStage;
+
+struct PrefillArgs {
+  const uint16_t* x;       // [M_total, K]
+  const uint8_t* w;        // [G, N, K/2]
+  const uint16_t* s;       // [G, N, K/128]
+  const float* sxn;        // [K/128, ld]
+  uint16_t* y;             // [M_total, N]
+  float* ws;               // [SK, M_total, N] fp32 split-K partials, or nullptr
+  const int32_t* m_sizes;  // [G] on device, or nullptr
+  int M_total, N, K, G, ld;
+  int gps;                 // 128-groups per split-K slice
+  int mtiles, ntiles;
+};
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at their maxima), followed
+// by a workgroup barrier. The "memory" clobber keeps LDS reads on their side.
+template <int VM>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, soff, 0, 0);
+}
+
+}  // namespace
+
+template <int NSTAGE, int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs args) {
+  static_assert(NSTAGE == 2 || NSTAGE == 3, "stages");
+  static_assert(NW == 4 || NW == 8, "waves");
+  constexpr int TN = kPN / NW;          // columns per wave
+  constexpr int SN = TN / 16;           // 16-column MFMA tiles per wave
+  constexpr int QX = 32 / NW;           // X DMA instructions per wave and group
+  constexpr int QW = 16 / NW;           // W DMA instructions per wave and group
+  constexpr int RL = 32 / NW;           // row-sum DMA lanes per wave (16 B = 4 rows each)
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Gk = args.K / kGroup;
+
+  int mt, nt;
+  tile_coords(blockIdx.x, gridDim.x, args.mtiles, args.ntiles, &mt, &nt);
+  const TileRows tr = tile_rows(mt, kPM, args.M_total, args.m_sizes, args.G);
+  if (tr.rows <= 0) return;
+  const int row0 = tr.row0, rows = tr.rows;
+  const int n0 = nt * kPN;
+  const int ncols = min(kPN, args.N - n0);
+
+  const uint32_t K2 = (uint32_t)args.K / 2u;
+  const uint32_t KB = (uint32_t)args.K * 2u;   // bytes per X row
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x + (size_t)row0 * args.K, (uint32_t)rows * KB);
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(args.w + ((size_t)tr.wg * args.N + n0) * K2, (uint32_t)ncols * K2);
+  // scales: the whole tensor (word-aligned reads, see make_scale_rsrc); columns
+  // past N read other scales or zeros and are never stored
+  const __amdgpu_buffer_rsrc_t rs =
+      make_scale_rsrc(args.s, (uint32_t)((size_t)(args.m_sizes != nullptr ? args.G : 1) * args.N * Gk));
+  const __amdgpu_buffer_rsrc_t rsx =
+      make_rsrc(args.sxn + row0, (uint32_t)(((size_t)Gk * args.ld - row0) * 4u));
+  const int slice = blockIdx.y;
+  const int gb = slice * args.gps;
+  const int ge = min(Gk, gb + args.gps);
+  const int ng = ge > gb ? ge - gb : 0;
+
+  // ---- DMA lane offsets (constant over groups)
+  // X instruction i of wave wv fills LDS block q = QX wv + i, i.e. tile rows
+  // 4 q + (lane >> 4), slot lane & 15; the chunk stored in slot p of row r is
+  // p ^ (r & 7), and r & 7 = (4 i + (lane >> 4)) & 7 only depends on i's parity.
+  const int xr = lane >> 4, xp = lane & 15;
+  uint32_t xvo[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int r = 4 * QX * wv + 4 * e + xr;
+    xvo[e] = (uint32_t)r * KB + 16u * (uint32_t)(xp ^ (r & 7));
+  }
+  // W instruction i fills block q = QW wv + i: tile rows 16 q + (lane >> 2),
+  // slot lane & 3; the chunk stored in slot p of row r is p ^ ((r >> 1) & 3).
+  const int wr = lane >> 2, wp = lane & 3;
+  const uint32_t wvo = (uint32_t)(16 * QW * wv + wr) * K2 + 16u * (uint32_t)(wp ^ ((wr >> 1) & 3));
+  // row sums: lanes 0..RL-1 of each wave fetch 4 rows each
+  const uint32_t rvo = (uint32_t)(4 * RL * wv + 4 * lane) * 4u;
+
+  // Row offsets always go into the vector offset, which the hardware range
+  // checks against the buffer extent (rows past the tile read zeros); the
+  // scalar offset only carries the group's k offset, which stays inside a row.
+  auto issue = [&](int g, int stage) {
+    uint8_t* base = lds + stage * kStage;
+#pragma unroll
+    for (int i = 0; i < QX; ++i)
+      dma16(rx, base + 1024 * (QX * wv + i), xvo[i & 1] + (uint32_t)(i >> 1) * 8u * KB, (uint32_t)g * 256u);
+#pragma unroll
+    for (int i = 0; i < QW; ++i)
+      dma16(rw, base + kXStage + 1024 * (QW * wv + i), wvo + (uint32_t)i * 16u * K2, (uint32_t)g * 64u);
+    if (lane < RL)
+      dma16(rsx, base + kXStage + kWStage + 16 * RL * wv, rvo + (uint32_t)g * (uint32_t)args.ld * 4u, 0u);
+  };
+
+  // ---- scales: the aligned word holding s[n][g] for this lane's SN columns
+  const int m16 = lane & 15, kb = lane >> 4;
+  uint32_t soff[SN];
+#pragma unroll
+  for (int ns = 0; ns < SN; ++ns)
+    soff[ns] = (uint32_t)((size_t)tr.wg * args.N + n0 + TN * wv + 16 * ns + m16) * (uint32_t)Gk * 2u;
+  auto load_scales = [&](uint32_t (&sw)[SN], int g) {
+#pragma unroll
+    for (int ns = 0; ns < SN; ++ns) sw[ns] = ld32(rs, (soff[ns] + 2u * (uint32_t)g) & ~3u);
+  };
+  auto scale_of = [&](uint32_t word, int ns, int g) {
+    const uint32_t o = soff[ns] + 2u * (uint32_t)g;
+    return __uint_as_float((o & 2u) ? (word & 0xFFFF0000u) : (word << 16));
+  };
+
+  // ---- LDS operand offsets within a stage
+  // A (X): row 16 ms + m16, logical chunk 4 kb + st, slot chunk ^ (row & 7)
+  uint32_t aoff[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+    aoff[st] = (uint32_t)m16 * 256u + 16u * (uint32_t)((4 * kb + st) ^ (m16 & 7));
+  // B (packed W): row TN wv + 16 ns + m16, logical chunk kb
+  const uint32_t boff = kXStage + (uint32_t)(TN * wv + m16) * 64u + 16u * (uint32_t)(kb ^ ((m16 >> 1) & 3));
+  // C init: -136 * row sums of rows 16 ms + 4 kb + 0..3
+  const uint32_t roff = kXStage + kWStage + 16u * (uint32_t)kb;
+
+  const uint32_t magic = vgpr_const(kMagicPair);
+  const uint32_t mask = __builtin_amdgcn_readfirstlane(vgpr_const(kNibblePairMask));
+
+  f32x4 acc[8][SN];
+#pragma unroll
+  for (int ms = 0; ms < 8; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < SN; ++ns) acc[ms][ns] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  uint32_t sc_cur[SN], sc_nxt[SN];
+
+  auto compute = [&](int stage, int g) {
+    const uint8_t* sb = lds + stage * kStage;
+    // row tile ms's operands: initial C and the 4 steps' A fragments
+    f32x4 cq[2];
+    bf16x8 aq[2][4];
+    auto read_rows = [&](int ms, f32x4& c0, bf16x8 (&a)[4]) {
+      c0 = *reinterpret_cast<const f32x4*>(sb + roff + 64u * (uint32_t)ms);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        a[st] = *reinterpret_cast<const bf16x8*>(sb + aoff[st] + 4096u * (uint32_t)ms);
+    };
+    read_rows(0, cq[0], aq[0]);
+    // dequantise this wave's TN columns x 128 k: bd[ns][st] = 8 bf16 (128 + q)
+    bf16x8 bd[SN][4];
+#pragma unroll
+    for (int ns = 0; ns < SN; ++ns) {
+      const u32x4 pk = *reinterpret_cast<const u32x4*>(sb + boff + 1024u * (uint32_t)ns);
+      const uint32_t wd[4] = {pk.x, pk.y, pk.z, pk.w};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const uint32_t w0 = wd[st], w4 = w0 >> 4;
+        u32x4 o;
+        o.x = and_or_sv(__builtin_amdgcn_perm(w4, w0, 0x0C040C00u), mask, magic);
+        o.y = and_or_sv(__builtin_amdgcn_perm(w4, w0, 0x0C050C01u), mask, magic);
+        o.z = and_or_sv(__builtin_amdgcn_perm(w4, w0, 0x0C060C02u), mask, magic);
+        o.w = and_or_sv(__builtin_amdgcn_perm(w4, w0, 0x0C070C03u), mask, magic);
+        bd[ns][st] = __builtin_bit_cast(bf16x8, o);
+      }
+    }
+    float scv[SN];
+#pragma unroll
+    for (int ns = 0; ns < SN; ++ns) scv[ns] = scale_of(sc_cur[ns], ns, g);
+#pragma unroll
+    for (int ms = 0; ms < 8; ++ms) {
+      // the next row tile's LDS reads go out before this tile's MFMAs
+      if (ms + 1 < 8) read_rows(ms + 1, cq[(ms + 1) & 1], aq[(ms + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x4 c0 = cq[ms & 1];
+      f32x4 t[SN];
+#pragma unroll
+      for (int ns = 0; ns < SN; ++ns) t[ns] = c0;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int ns = 0; ns < SN; ++ns)
+          t[ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[ms & 1][st], bd[ns][st], t[ns], 0, 0, 0);
+#pragma unroll
+      for (int ns = 0; ns < SN; ++ns) {
+        acc[ms][ns].x = fmaf(scv[ns], t[ns].x, acc[ms][ns].x);
+        acc[ms][ns].y = fmaf(scv[ns], t[ns].y, acc[ms][ns].y);
+        acc[ms][ns].z = fmaf(scv[ns], t[ns].z, acc[ms][ns].z);
+        acc[ms][ns].w = fmaf(scv[ns], t[ns].w, acc[ms][ns].w);
+      }
+    }
+  };
+
+  // ---- pipeline. Issue order: DMA(0), [DMA(1)], S(0), then per group j:
+  // DMA(j + NSTAGE - 1), S(j + 1). Before the barrier that ends group j the
+  // DMA of group j + 1 must be complete; the ops issued after it are then
+  // S(j), DMA(j + NSTAGE - 1) (if NSTAGE == 3) and S(j + 1).
+  constexpr int kDmaOps = QX + QW + 1;   // DMA instructions per wave and group
+  if (ng > 0) {
+    issue(gb, 0);
+    if (NSTAGE == 3 && ng > 1) issue(gb + 1, 1);
+    load_scales(sc_cur, gb);
+    if (NSTAGE == 3 && ng > 1) wait_vm_barrier<kDmaOps + SN>();
+    else wait_vm_barrier<0>();
+  }
+  for (int j = 0; j < ng; ++j) {
+    const int g = gb + j;
+    const bool ahead = j + NSTAGE - 1 < ng;
+    if (ahead) issue(g + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
+    if (j + 1 < ng) load_scales(sc_nxt, g + 1);
+    compute(j % NSTAGE, g);
+    if (j + 1 < ng) {
+      if (NSTAGE == 3 && ahead) wait_vm_barrier<SN + kDmaOps + SN>();
+      else wait_vm_barrier<0>();
+#pragma unroll
+      for (int ns = 0; ns < SN; ++ns) sc_cur[ns] = sc_nxt[ns];
+    }
+  }
+
+  // ---- epilogue: lane holds rows 16 ms + 4 kb + i of column TN wv + 16 ns + m16
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(args.y + (size_t)row0 * args.N, (uint32_t)rows * (uint32_t)args.N * 2u);
+  const __amdgpu_buffer_rsrc_t rws =
+      make_rsrc(args.ws + ((size_t)slice * args.M_total + row0) * args.N, (uint32_t)rows * (uint32_t)args.N * 4u);
+  if (args.ws == nullptr) {
+#pragma unroll
+    for (int ns = 0; ns < SN; ++ns) {
+      const int ncol = TN * wv + 16 * ns + m16;
+      if (ncol < ncols) {
+#pragma unroll
+        for (int ms = 0; ms < 8; ++ms)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t e = (uint32_t)(16 * ms + 4 * kb + i) * (uint32_t)args.N + (uint32_t)(n0 + ncol);
+            st16(to_bf16(acc[ms][ns][i]), ry, e * 2u);
+          }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ns = 0; ns < SN; ++ns) {
+      const int ncol = TN * wv + 16 * ns + m16;
+      if (ncol < ncols) {
+#pragma unroll
+        for (int ms = 0; ms < 8; ++ms)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t e = (uint32_t)(16 * ms + 4 * kb + i) * (uint32_t)args.N + (uint32_t)(n0 + ncol);
+            st32(__float_as_uint(acc[ms][ns][i]), rws, e * 4u);
+          }
+      }
+    }
+  }
+}
+
+template <int NSTAGE, int NW>
+static hipError_t launch_prefill_t(const PrefillArgs& a, int sk, hipStream_t stream) {
+  const int lds_bytes = NSTAGE * kStage;
+  static bool attr_set = false;   // per instantiation; the attribute is per function
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NSTAGE, NW>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const long long blocks = (long long)a.mtiles * a.ntiles;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_kernel<NSTAGE, NW>), dim3((unsigned)blocks, sk), dim3(64 * NW), lds_bytes, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
+                          float* ws, const int32_t* m_sizes, int M_total, int N, int K, int G, int ld, int gps,
+                          int sk, int nstage, int waves, hipStream_t stream) {
+  PrefillArgs a;
+  a.x = x; a.w = w; a.s = s; a.sxn = sxn; a.y = y; a.ws = ws; a.m_sizes = m_sizes;
+  a.M_total = M_total; a.N = N; a.K = K; a.G = G; a.ld = ld; a.gps = gps;
+  a.mtiles = (M_total + kPM - 1) / kPM + (m_sizes != nullptr ? G : 0);
+  a.ntiles = (N + kPN - 1) / kPN;
+  if (waves == 8 && nstage == 3) return launch_prefill_t<3, 8>(a, sk, stream);
+  if (waves == 8 && nstage == 2) return launch_prefill_t<2, 8>(a, sk, stream);
+  if (waves == 4 && nstage == 3) return launch_prefill_t<3, 4>(a, sk, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace w4a16

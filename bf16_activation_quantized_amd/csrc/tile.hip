@@ -27,6 +27,7 @@
 // [0, M_total)) to find its group, and surplus workgroups exit at once.
 #include "common.hpp"
 #include "launch.hpp"
+#include "tilemap.hpp"
 
 namespace w4a16 {
 
@@ -97,39 +98,11 @@ __global__ __launch_bounds__(64 * WM * WN) void tile_kernel(const TileArgs args)
   const int wm = wave / WN, wn = wave % WN;
   const int Gk = args.K / kGroup;
 
-  // ---- tile id: XCD-contiguous, then GROUP_M grouping over (mt, nt)
-  const int nblocks = gridDim.x;
-  const int lid = xcd_remap(blockIdx.x, nblocks);
-  constexpr int GM = 8;
-  const int MT = args.mtiles, NTn = args.ntiles;
-  const int per_group = GM * NTn;
-  const int grp = lid / per_group;
-  const int first_m = grp * GM;
-  const int gsz = min(MT - first_m, GM);
-  const int mt_lin = first_m + (lid % per_group) % gsz;
-  const int nt = (lid % per_group) / gsz;
-
-  // ---- resolve (weight group, rows)
-  int wg = 0, row0 = mt_lin * BM, rows = min(BM, args.M_total - row0);
-  if (args.m_sizes != nullptr) {
-    int cnt = 0, start = 0;
-    bool found = false;
-    for (int gg = 0; gg < args.G; ++gg) {
-      int ms = args.m_sizes[gg];
-      ms = ms < 0 ? 0 : ms;
-      ms = start >= args.M_total ? 0 : min(ms, args.M_total - start);
-      const int t = (ms + BM - 1) / BM;
-      if (!found && mt_lin < cnt + t) {
-        wg = gg;
-        row0 = start + (mt_lin - cnt) * BM;
-        rows = min(BM, start + ms - row0);
-        found = true;
-      }
-      cnt += t;
-      start += ms;
-    }
-    if (!found) return;
-  }
+  // ---- tile id and rows
+  int mt_lin, nt;
+  tile_coords(blockIdx.x, gridDim.x, args.mtiles, args.ntiles, &mt_lin, &nt);
+  const TileRows tr = tile_rows(mt_lin, BM, args.M_total, args.m_sizes, args.G);
+  const int wg = tr.wg, row0 = tr.row0, rows = tr.rows;
   if (rows <= 0) return;
   const int n0 = nt * BN;
   const int ncols = min(BN, args.N - n0);
@@ -223,7 +196,9 @@ __global__ __launch_bounds__(64 * WM * WN) void tile_kernel(const TileArgs args)
     for (int ms = 0; ms < SM; ++ms) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x4 v = ld128(rsx, sx_off[ms][j], gb);
+        // the group offset is a row offset of the row-sum matrix: it goes into
+        // the range-checked vector offset, never the scalar one
+        const u32x4 v = ld128(rsx, sx_off[ms][j] + gb);
         ini[ms][4 * j + 0] = __uint_as_float(v.x);
         ini[ms][4 * j + 1] = __uint_as_float(v.y);
         ini[ms][4 * j + 2] = __uint_as_float(v.z);
@@ -334,11 +309,14 @@ static hipError_t launch_tile_t(const TileArgs& a0, int mtiles_bound, int sk, hi
   return hipGetLastError();
 }
 
-// Tile configurations (BM x BN, waves WM x WN):
-//   0: 128 x 256, 2 x 4 waves (wave tile 64 x 64)
-//   1: 128 x 128, 2 x 2 waves (wave tile 64 x 64)
+// Tile configurations (BM x BN):
+//   0: 128 x 256, 2 x 4 waves of 64 x 64, weights dequantised into LDS
+//   1: 128 x 128, 2 x 2 waves of 64 x 64, weights dequantised into LDS
+//   2: 128 x 256, 8 waves of 128 x 32, LDS-DMA staging, 3 stages (prefill.hip)
+//   3: as 2 with 2 stages
+//   4: as 2 with 4 waves of 128 x 64
 struct TileCfg { int bm, bn; };
-static const TileCfg kTileCfgs[] = {{128, 256}, {128, 128}};
+static const TileCfg kTileCfgs[] = {{128, 256}, {128, 128}, {128, 256}, {128, 256}, {128, 256}};
 int tile_num_cfgs() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0])); }
 int tile_bm(int cfg) { return kTileCfgs[cfg].bm; }
 int tile_bn(int cfg) { return kTileCfgs[cfg].bn; }
@@ -347,6 +325,9 @@ hipError_t launch_tile(const uint16_t* x, const uint8_t* w, const uint16_t* s, c
                        float* ws, const int32_t* m_sizes, int M_total, int N, int K, int G, int ld, int gps,
                        int sk, int cfg, hipStream_t stream) {
   if (cfg < 0 || cfg >= tile_num_cfgs()) return hipErrorInvalidValue;
+  if (cfg >= 2)
+    return launch_prefill(x, w, s, sxn, y, ws, m_sizes, M_total, N, K, G, ld, gps, sk, cfg == 3 ? 2 : 3,
+                          cfg == 4 ? 4 : 8, stream);
   TileArgs a;
   a.x = x; a.w = w; a.s = s; a.sxn = sxn; a.y = y; a.ws = ws; a.m_sizes = m_sizes;
   a.M_total = M_total; a.N = N; a.K = K; a.G = G; a.ld = ld; a.gps = gps;

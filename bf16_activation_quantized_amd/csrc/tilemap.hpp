@@ -1,0 +1,55 @@
+// Tile scheduling shared by the tile GEMM kernels (plain and grouped).
+#pragma once
+
+#include "common.hpp"
+
+namespace w4a16 {
+
+// Linear workgroup id -> (m-tile, n-tile). Workgroup ids are first remapped
+// so that each XCD owns a contiguous run of tiles, then tiles are ordered in
+// bands of GROUP_M = 8 m-tiles, column by column ("Add Triton BF16xINT4
+// rowwise GEMM for ROCm gfx942/gfx950", Implementation: XCD remapping and
+// GROUP_SIZE_M grouping): neighbouring workgroups share weight columns and
+// activation rows in one L2.
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int MT, int NT, int* mt, int* nt) {
+  constexpr int GM = 8;
+  const int lid = xcd_remap(bid, nblocks);
+  const int per_group = GM * NT;
+  const int grp = lid / per_group;
+  const int first_m = grp * GM;
+  const int gsz = min(MT - first_m, GM);
+  *mt = first_m + (lid % per_group) % gsz;
+  *nt = (lid % per_group) / gsz;
+}
+
+// Rows of linear m-tile `mt` (BM rows each). Plain: one weight group of
+// M_total rows. Grouped ("Native fused grouped kernel" on the MI350X Triton
+// page): the m-tiles of group g follow those of groups < g; each group's
+// size is clamped to [0, M_total - start). rows <= 0 means no work.
+struct TileRows {
+  int wg, row0, rows;
+};
+__device__ __forceinline__ TileRows tile_rows(int mt, int BM, int M_total, const int32_t* m_sizes, int G) {
+  TileRows t{0, mt * BM, min(BM, M_total - mt * BM)};
+  if (m_sizes == nullptr) return t;
+  int cnt = 0, start = 0;
+  bool found = false;
+  for (int gg = 0; gg < G; ++gg) {
+    int ms = m_sizes[gg];
+    ms = ms < 0 ? 0 : ms;
+    ms = start >= M_total ? 0 : min(ms, M_total - start);
+    const int tiles = (ms + BM - 1) / BM;
+    if (!found && mt < cnt + tiles) {
+      t.wg = gg;
+      t.row0 = start + (mt - cnt) * BM;
+      t.rows = min(BM, start + ms - t.row0);
+      found = true;
+    }
+    cnt += tiles;
+    start += ms;
+  }
+  if (!found) t.rows = 0;
+  return t;
+}
+
+}  // namespace w4a16

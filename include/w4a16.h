@@ -182,8 +182,8 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  * The result of a forced path still satisfies the same contract.
  *   path   : 0 = automatic, 1 = M == 1 GEMV (at most 64 groups per split-K
  *            slice),
- *            2 = M <= 16 MFMA 16x16x32 decode kernel, 3 = MFMA 32x32x16 tile
- *            kernel (LDS double-buffered; the only path of the grouped call)
+ *            2 = M <= 16 MFMA 16x16x32 decode kernel, 3 = MFMA tile kernel
+ *            (LDS-staged; the only path of the grouped call)
  *   variant: -1 = default for the path; otherwise
  *            path 1: 1000 * layout + layout digits.
  *              layout 2 (default, MFMA diagonal contraction of 16 groups per
@@ -202,7 +202,10 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  *              blocks per wave;
  *            path 2: 10 * waves_per_workgroup +
  *            column_tiles_per_wave (41, 42, 44, 81, 82, 84); path 3: tile
- *            configuration index (0: 128x256, 1: 128x128).
+ *            configuration index (0: 128x256 and 1: 128x128 with weights
+ *            dequantised into LDS; 2 (default): 128x256 with LDS-DMA staging,
+ *            8 waves, 3 LDS stages; 3: as 2 with 2 stages; 4: as 2 with 4
+ *            waves).
  * An unavailable combination (e.g. path 1 with M != 1, path 2 with M > 16)
  * returns W4A16_ERR_SHAPE.
  */

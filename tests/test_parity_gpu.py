@@ -95,6 +95,8 @@ GEMV_CASES = [
     (5, 5120, 1, 2011),       # fewer rows than one block per wave
     (5, 5120, 1, 2710),
     (33, 8192, 4, 2620),      # split-K, 16 groups per slice, 1-row blocks
+    (1001, 896, 2, 2410),     # N * G odd: the last scale is the low half of a word
+    (1001, 896, 2, 2110),     #   that ends past the tensor (4 + 3 groups per slice)
     (1000, 640, 1, 2213),     # 5 groups per slice: no MFMA geometry -> half-wave 124
     (17408, 5120, 1, 122),    # flat layout at the decode shape
     (17408, 5120, 1, 1124),   # half-wave layout at the decode shape
@@ -148,6 +150,23 @@ TILE_CASES = [
     (1, 256, 256, 1, 0),      # one row through the tile kernel (M tail)
     (255, 129, 512, 0, 0),
     (600, 700, 1280, 0, 1),
+    # LDS-DMA kernel: 2 = 8 waves, 3 stages; 3 = 8 waves, 2 stages; 4 = 4 waves, 3 stages
+    (17, 100, 128, 1, 2),     # one group: no second stage in flight; M and N tails
+    (130, 256, 256, 1, 2),    # two groups
+    (300, 1000, 640, 1, 2),   # steady state, N tail of 232 columns
+    (129, 513, 384, 2, 2),    # split-K slices of 2 and 1 groups
+    (64, 64, 1024, 4, 3),
+    (257, 300, 256, 8, 2),    # more slices than groups: empty slices write zeros
+    (1, 256, 256, 1, 2),
+    (255, 129, 512, 0, 2),
+    (600, 700, 1280, 0, 3),
+    (1322, 512, 2560, 1, 2),  # the prefill row count and depth
+    (1322, 512, 2560, 1, 3),
+    (129, 511, 384, 1, 2),    # N * G odd, no split
+    (77, 257, 640, 1, 3),
+    (300, 1000, 640, 1, 4),
+    (129, 513, 384, 2, 4),
+    (1322, 512, 2560, 1, 4),
 ]
 
 
@@ -169,6 +188,12 @@ GROUPED_CASES = [
     ([0, 0, 0, 50], 128, 128, None),
     ([128, 128, 128], 256, 512, 1),
     ([1, 1, 1, 1, 1], 64, 128, 0),
+    ([37], 256, 384, 2),
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 2),
+    ([128, 128, 128], 256, 512, 3),
+    ([1, 1, 1, 1, 1], 64, 128, 2),
+    ([0, 0, 0, 50], 128, 128, 3),
+    ([5, 70, 33], 257, 384, 2),   # N * G odd per weight group: unaligned group bases
 ]
 
 
