@@ -9,22 +9,25 @@
 // fp32, which is scaled by the column's bf16 scale and added to the fp32
 // accumulator. No weight is ever rounded.
 //
-// Structure (one 256-thread workgroup per 128 x 256 output tile, 4 waves of
-// 128 x 64; one workgroup per compute unit):
-//  * one K-stage = one 128-group: X [128 rows, 128 k] bf16 (32 KiB), the
-//    packed weights [256 rows, 64 B] (16 KiB, still 4-bit) and the 128 row
-//    sums; NSTAGE stages in LDS, filled by buffer loads that write LDS
-//    directly (no registers, no VALU), issued NSTAGE - 1 groups ahead;
-//  * each wave reads its 64 columns of packed weights once per group and
-//    dequantises them in registers (64 VGPRs of bf16 B operands), then sweeps
-//    the 8 row tiles of 16: 4 MFMA 16x16x32 steps per (row tile, column tile),
-//    4 chains interleaved, one rescale FMA per output element per group;
+// Structure (one 512-thread workgroup per (16 MS) x 256 output tile, 8 waves
+// of (16 MS) x 32, MS = 8; one workgroup per compute unit):
+//  * one K-stage = one 128-group: X [16 MS rows, 128 k] bf16, the packed
+//    weights [256 rows, 64 B] (16 KiB, still 4-bit) and the 16 MS row sums;
+//    NSTAGE stages in LDS, filled by buffer loads that write LDS directly (no
+//    registers, no VALU), issued NSTAGE - 1 groups ahead;
+//  * each wave reads its 32 columns of packed weights once per group and
+//    dequantises them in registers (32 VGPRs of bf16 B operands), then sweeps
+//    the MS row tiles of 16: 4 MFMA 16x16x32 steps per (row tile, column
+//    tile), one rescale FMA per output element per group. A dequantised
+//    fragment serves MS row tiles: with VALU ops issuing only about every 8
+//    cycles while the matrix core is busy, dequant + rescale must stay near 2
+//    VALU ops per 16-cycle MFMA, which the taller tile (MS = 14) meets;
 //  * within a group the MFMA k order is permuted: lane (r, kb) of step st
 //    holds k = 32 kb + 8 st + 0..7 for both operands, so one lane's four steps
 //    of packed weights are one 16-byte LDS read;
 //  * LDS rows are XOR-swizzled in 16-byte chunks (X by row & 7, weights by
 //    (row >> 1) & 3): the DMA lanes fetch the chunk that belongs at their LDS
-//    slot, and the MFMA operand reads are bank-conflict free;
+//    slot, and the MFMA operand reads avoid bank conflicts;
 //  * one barrier per group, after an explicit wait for the next group's DMA.
 // The M tail and N tail read zeros through the exact buffer extents; stores
 // past the last row are dropped and columns >= N are skipped.
@@ -36,12 +39,19 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int kPM = 128;                    // rows per tile
-constexpr int kPN = 256;                    // columns per tile (4 waves x 64)
-constexpr int kXStage = kPM * 256;          // X: 128 rows x 128 k x 2 B
+constexpr int kPN = 256;                    // columns per tile (8 waves x 32)
+constexpr int kNW = 8;                      // waves per workgroup
 constexpr int kWStage = kPN * 64;           // packed W: 256 rows x 128 k / 2
-constexpr int kRStage = kPM * 4;            // -136 * row sums: 128 fp32
-constexpr int kStage = kXStage + kWStage + kRStage;
+
+// LDS stage of a tile with MS row tiles of 16: X, packed W, row sums
+template <int MS>
+struct Stage {
+  static constexpr int kRows = 16 * MS;
+  static constexpr int kX = kRows * 256;     // X: rows x 128 k x 2 B
+  static constexpr int kW = kWStage;
+  static constexpr int kR = kRows * 4;       // -136 * row sums, fp32
+  static constexpr int kBytes = kX + kW + kR;
+};
 
 struct PrefillArgs {
   const uint16_t* x;       // [M_total, K]
@@ -71,15 +81,17 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst
 
 }  // namespace
 
-template <int NSTAGE, int NW>
-__global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs args) {
+template <int NSTAGE, int MS>
+__global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs args) {
   static_assert(NSTAGE == 2 || NSTAGE == 3, "stages");
-  static_assert(NW == 4 || NW == 8, "waves");
-  constexpr int TN = kPN / NW;          // columns per wave
-  constexpr int SN = TN / 16;           // 16-column MFMA tiles per wave
-  constexpr int QX = 32 / NW;           // X DMA instructions per wave and group
-  constexpr int QW = 16 / NW;           // W DMA instructions per wave and group
-  constexpr int RL = 32 / NW;           // row-sum DMA lanes per wave (16 B = 4 rows each)
+  static_assert(MS % 2 == 0 && MS <= 16, "row tiles");
+  using ST = Stage<MS>;
+  constexpr int BM = ST::kRows;
+  constexpr int TN = kPN / kNW;         // columns per wave (32)
+  constexpr int SN = TN / 16;           // 16-column MFMA tiles per wave (2)
+  constexpr int QX = MS / 2;            // X DMA instructions per wave and group (4 rows of 256 B each)
+  constexpr int QW = 16 / kNW;          // W DMA instructions per wave and group
+  constexpr int RL = MS / 2;            // row-sum DMA lanes per wave (16 B = 4 rows each)
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -89,7 +101,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs args
 
   int mt, nt;
   tile_coords(blockIdx.x, gridDim.x, args.mtiles, args.ntiles, &mt, &nt);
-  const TileRows tr = tile_rows(mt, kPM, args.M_total, args.m_sizes, args.G);
+  const TileRows tr = tile_rows(mt, BM, args.M_total, args.m_sizes, args.G);
   if (tr.rows <= 0) return;
   const int row0 = tr.row0, rows = tr.rows;
   const int n0 = nt * kPN;
@@ -114,34 +126,43 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs args
   // ---- DMA lane offsets (constant over groups)
   // X instruction i of wave wv fills LDS block q = QX wv + i, i.e. tile rows
   // 4 q + (lane >> 4), slot lane & 15; the chunk stored in slot p of row r is
-  // p ^ (r & 7), and r & 7 = (4 i + (lane >> 4)) & 7 only depends on i's parity.
-  const int xr = lane >> 4, xp = lane & 15;
-  uint32_t xvo[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int r = 4 * QX * wv + 4 * e + xr;
-    xvo[e] = (uint32_t)r * KB + 16u * (uint32_t)(xp ^ (r & 7));
-  }
+  // p ^ (r & 7), and r & 7 = 4 (q & 1) + (lane >> 4): row offset
+  // 4 (q & ~1) KB plus xvo[q & 1].
+  // (recomputed from the lane id at each issue: a few VALU ops per group
+  // instead of registers held across the main loop)
+  auto xvo = [&](int e) {
+    const int xr = lane >> 4, xp = lane & 15;
+    return (uint32_t)(4 * e + xr) * KB + 16u * (uint32_t)(xp ^ (4 * e + xr));
+  };
   // W instruction i fills block q = QW wv + i: tile rows 16 q + (lane >> 2),
   // slot lane & 3; the chunk stored in slot p of row r is p ^ ((r >> 1) & 3).
-  const int wr = lane >> 2, wp = lane & 3;
-  const uint32_t wvo = (uint32_t)(16 * QW * wv + wr) * K2 + 16u * (uint32_t)(wp ^ ((wr >> 1) & 3));
+  auto wvo = [&]() {
+    const int wr = lane >> 2, wp = lane & 3;
+    return (uint32_t)(16 * QW * wv + wr) * K2 + 16u * (uint32_t)(wp ^ ((wr >> 1) & 3));
+  };
   // row sums: lanes 0..RL-1 of each wave fetch 4 rows each
-  const uint32_t rvo = (uint32_t)(4 * RL * wv + 4 * lane) * 4u;
+  auto rvo = [&]() { return (uint32_t)(4 * RL * wv + 4 * lane) * 4u; };
 
   // Row offsets always go into the vector offset, which the hardware range
   // checks against the buffer extent (rows past the tile read zeros); the
   // scalar offset only carries the group's k offset, which stays inside a row.
   auto issue = [&](int g, int stage) {
-    uint8_t* base = lds + stage * kStage;
+    uint8_t* base = lds + stage * ST::kBytes;
+    // the group is the same in every lane; keeping its offsets scalar avoids
+    // a waterfall loop around each load
+    const uint32_t gx = __builtin_amdgcn_readfirstlane((uint32_t)g * 256u);
+    const uint32_t gw = __builtin_amdgcn_readfirstlane((uint32_t)g * 64u);
+    const uint32_t xo0 = xvo(0), xo1 = xvo(1);
 #pragma unroll
-    for (int i = 0; i < QX; ++i)
-      dma16(rx, base + 1024 * (QX * wv + i), xvo[i & 1] + (uint32_t)(i >> 1) * 8u * KB, (uint32_t)g * 256u);
+    for (int i = 0; i < QX; ++i) {
+      const int q = QX * wv + i;
+      dma16(rx, base + 1024 * q, ((q & 1) ? xo1 : xo0) + (uint32_t)(4 * (q & ~1)) * KB, gx);
+    }
+    const uint32_t wo = wvo();
 #pragma unroll
-    for (int i = 0; i < QW; ++i)
-      dma16(rw, base + kXStage + 1024 * (QW * wv + i), wvo + (uint32_t)i * 16u * K2, (uint32_t)g * 64u);
+    for (int i = 0; i < QW; ++i) dma16(rw, base + ST::kX + 1024 * (QW * wv + i), wo + (uint32_t)i * 16u * K2, gw);
     if (lane < RL)
-      dma16(rsx, base + kXStage + kWStage + 16 * RL * wv, rvo + (uint32_t)g * (uint32_t)args.ld * 4u, 0u);
+      dma16(rsx, base + ST::kX + ST::kW + 16 * RL * wv, rvo() + (uint32_t)g * (uint32_t)args.ld * 4u, 0u);
   };
 
   // ---- scales: the aligned word holding s[n][g] for this lane's SN columns
@@ -161,36 +182,35 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs args
 
   // ---- LDS operand offsets within a stage
   // A (X): row 16 ms + m16, logical chunk 4 kb + st, slot chunk ^ (row & 7)
-  uint32_t aoff[4];
-#pragma unroll
-  for (int st = 0; st < 4; ++st)
-    aoff[st] = (uint32_t)m16 * 256u + 16u * (uint32_t)((4 * kb + st) ^ (m16 & 7));
+  // (4 kb + st) ^ (m16 & 7) = ((4 kb) ^ (m16 & 7)) ^ st: one base register
+  const uint32_t aoff0 = (uint32_t)m16 * 256u + 16u * (uint32_t)((4 * kb) ^ (m16 & 7));
   // B (packed W): row TN wv + 16 ns + m16, logical chunk kb
-  const uint32_t boff = kXStage + (uint32_t)(TN * wv + m16) * 64u + 16u * (uint32_t)(kb ^ ((m16 >> 1) & 3));
+  const uint32_t boff = ST::kX + (uint32_t)(TN * wv + m16) * 64u + 16u * (uint32_t)(kb ^ ((m16 >> 1) & 3));
   // C init: -136 * row sums of rows 16 ms + 4 kb + 0..3
-  const uint32_t roff = kXStage + kWStage + 16u * (uint32_t)kb;
+  const uint32_t roff = ST::kX + ST::kW + 16u * (uint32_t)kb;
 
   const uint32_t magic = vgpr_const(kMagicPair);
   const uint32_t mask = __builtin_amdgcn_readfirstlane(vgpr_const(kNibblePairMask));
 
-  f32x4 acc[8][SN];
+  f32x4 acc[MS][SN];
 #pragma unroll
-  for (int ms = 0; ms < 8; ++ms)
+  for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
     for (int ns = 0; ns < SN; ++ns) acc[ms][ns] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   uint32_t sc_cur[SN], sc_nxt[SN];
 
   auto compute = [&](int stage, int g) {
-    const uint8_t* sb = lds + stage * kStage;
-    // row tile ms's operands: initial C and the 4 steps' A fragments
+    const uint8_t* sb = lds + stage * ST::kBytes;
+    // row tile ms's operands: initial C and the 4 steps' A fragments; the next
+    // row tile's reads go out before this tile's MFMAs (two register sets)
     f32x4 cq[2];
     bf16x8 aq[2][4];
     auto read_rows = [&](int ms, f32x4& c0, bf16x8 (&a)[4]) {
       c0 = *reinterpret_cast<const f32x4*>(sb + roff + 64u * (uint32_t)ms);
 #pragma unroll
       for (int st = 0; st < 4; ++st)
-        a[st] = *reinterpret_cast<const bf16x8*>(sb + aoff[st] + 4096u * (uint32_t)ms);
+        a[st] = *reinterpret_cast<const bf16x8*>(sb + (aoff0 ^ (16u * (uint32_t)st)) + 4096u * (uint32_t)ms);
     };
     read_rows(0, cq[0], aq[0]);
     // dequantise this wave's TN columns x 128 k: bd[ns][st] = 8 bf16 (128 + q)
@@ -214,11 +234,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs args
 #pragma unroll
     for (int ns = 0; ns < SN; ++ns) scv[ns] = scale_of(sc_cur[ns], ns, g);
 #pragma unroll
-    for (int ms = 0; ms < 8; ++ms) {
-      // the next row tile's LDS reads go out before this tile's MFMAs
-      if (ms + 1 < 8) read_rows(ms + 1, cq[(ms + 1) & 1], aq[(ms + 1) & 1]);
+    for (int ms = 0; ms < MS; ++ms) {
+      const int cur = ms & 1;
+      if (ms + 1 < MS) read_rows(ms + 1, cq[(ms + 1) & 1], aq[(ms + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      const f32x4 c0 = cq[ms & 1];
+      const f32x4 c0 = cq[cur];
       f32x4 t[SN];
 #pragma unroll
       for (int ns = 0; ns < SN; ++ns) t[ns] = c0;
@@ -226,7 +246,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs args
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int ns = 0; ns < SN; ++ns)
-          t[ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[ms & 1][st], bd[ns][st], t[ns], 0, 0, 0);
+          t[ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[cur][st], bd[ns][st], t[ns], 0, 0, 0);
 #pragma unroll
       for (int ns = 0; ns < SN; ++ns) {
         acc[ms][ns].x = fmaf(scv[ns], t[ns].x, acc[ms][ns].x);
@@ -237,17 +257,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs args
     }
   };
 
-  // ---- pipeline. Issue order: DMA(0), [DMA(1)], S(0), then per group j:
-  // DMA(j + NSTAGE - 1), S(j + 1). Before the barrier that ends group j the
-  // DMA of group j + 1 must be complete; the ops issued after it are then
-  // S(j), DMA(j + NSTAGE - 1) (if NSTAGE == 3) and S(j + 1).
-  constexpr int kDmaOps = QX + QW + 1;   // DMA instructions per wave and group
+  // ---- pipeline: group j + NSTAGE - 1 is loaded while group j is computed.
+  // The barrier that ends group j waits for all of this wave's vector-memory
+  // operations (vmcnt(0)): that includes the DMA of group j + 1, and also the
+  // DMA of group j + 2 issued at the start of group j, which has had a whole
+  // group of compute to land. A precise count would let group j + 2 stay in
+  // flight, but it is only correct while the compiler emits no other vector
+  // memory operations (spills count too), so the simple wait is used.
   if (ng > 0) {
     issue(gb, 0);
     if (NSTAGE == 3 && ng > 1) issue(gb + 1, 1);
     load_scales(sc_cur, gb);
-    if (NSTAGE == 3 && ng > 1) wait_vm_barrier<kDmaOps + SN>();
-    else wait_vm_barrier<0>();
+    wait_vm_barrier<0>();
   }
   for (int j = 0; j < ng; ++j) {
     const int g = gb + j;
@@ -256,8 +277,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs args
     if (j + 1 < ng) load_scales(sc_nxt, g + 1);
     compute(j % NSTAGE, g);
     if (j + 1 < ng) {
-      if (NSTAGE == 3 && ahead) wait_vm_barrier<SN + kDmaOps + SN>();
-      else wait_vm_barrier<0>();
+      wait_vm_barrier<0>();
 #pragma unroll
       for (int ns = 0; ns < SN; ++ns) sc_cur[ns] = sc_nxt[ns];
     }
@@ -273,7 +293,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs args
       const int ncol = TN * wv + 16 * ns + m16;
       if (ncol < ncols) {
 #pragma unroll
-        for (int ms = 0; ms < 8; ++ms)
+        for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t e = (uint32_t)(16 * ms + 4 * kb + i) * (uint32_t)args.N + (uint32_t)(n0 + ncol);
@@ -287,7 +307,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs args
       const int ncol = TN * wv + 16 * ns + m16;
       if (ncol < ncols) {
 #pragma unroll
-        for (int ms = 0; ms < 8; ++ms)
+        for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t e = (uint32_t)(16 * ms + 4 * kb + i) * (uint32_t)args.N + (uint32_t)(n0 + ncol);
@@ -298,35 +318,37 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const PrefillArgs args
   }
 }
 
-template <int NSTAGE, int NW>
-static hipError_t launch_prefill_t(const PrefillArgs& a, int sk, hipStream_t stream) {
-  const int lds_bytes = NSTAGE * kStage;
+template <int NSTAGE, int MS>
+static hipError_t launch_prefill_t(PrefillArgs a, int sk, hipStream_t stream) {
+  constexpr int BM = Stage<MS>::kRows;
+  const int lds_bytes = NSTAGE * Stage<MS>::kBytes;
   static bool attr_set = false;   // per instantiation; the attribute is per function
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NSTAGE, NW>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NSTAGE, MS>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  a.mtiles = (a.M_total + BM - 1) / BM + (a.m_sizes != nullptr ? a.G : 0);
+  a.ntiles = (a.N + kPN - 1) / kPN;
   const long long blocks = (long long)a.mtiles * a.ntiles;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<NSTAGE, NW>), dim3((unsigned)blocks, sk), dim3(64 * NW), lds_bytes, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<NSTAGE, MS>), dim3((unsigned)blocks, sk), dim3(64 * kNW), lds_bytes, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
                           float* ws, const int32_t* m_sizes, int M_total, int N, int K, int G, int ld, int gps,
-                          int sk, int nstage, int waves, hipStream_t stream) {
+                          int sk, int row_tiles, hipStream_t stream) {
   PrefillArgs a;
   a.x = x; a.w = w; a.s = s; a.sxn = sxn; a.y = y; a.ws = ws; a.m_sizes = m_sizes;
   a.M_total = M_total; a.N = N; a.K = K; a.G = G; a.ld = ld; a.gps = gps;
-  a.mtiles = (M_total + kPM - 1) / kPM + (m_sizes != nullptr ? G : 0);
-  a.ntiles = (N + kPN - 1) / kPN;
-  if (waves == 8 && nstage == 3) return launch_prefill_t<3, 8>(a, sk, stream);
-  if (waves == 8 && nstage == 2) return launch_prefill_t<2, 8>(a, sk, stream);
-  if (waves == 4 && nstage == 3) return launch_prefill_t<3, 4>(a, sk, stream);
-  return hipErrorInvalidValue;
+  a.mtiles = 0; a.ntiles = 0;
+  switch (row_tiles) {
+    case 8: return launch_prefill_t<3, 8>(a, sk, stream);     // 128 x 256 tiles, 3 x 48.5 KiB stages
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace w4a16

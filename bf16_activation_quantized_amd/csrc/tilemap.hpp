@@ -49,6 +49,12 @@ __device__ __forceinline__ TileRows tile_rows(int mt, int BM, int M_total, const
     start += ms;
   }
   if (!found) t.rows = 0;
+  // the walk reads m_sizes with vector loads; the results are the same in
+  // every lane, and saying so keeps the buffer descriptors built from them in
+  // scalar registers (otherwise every buffer access becomes a waterfall loop)
+  t.wg = __builtin_amdgcn_readfirstlane(t.wg);
+  t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+  t.rows = __builtin_amdgcn_readfirstlane(t.rows);
   return t;
 }
 

@@ -204,8 +204,7 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  *            column_tiles_per_wave (41, 42, 44, 81, 82, 84); path 3: tile
  *            configuration index (0: 128x256 and 1: 128x128 with weights
  *            dequantised into LDS; 2 (default): 128x256 with LDS-DMA staging,
- *            8 waves, 3 LDS stages; 3: as 2 with 2 stages; 4: as 2 with 4
- *            waves).
+ *            8 waves, 3 LDS stages).
  * An unavailable combination (e.g. path 1 with M != 1, path 2 with M > 16)
  * returns W4A16_ERR_SHAPE.
  */

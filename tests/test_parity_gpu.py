@@ -155,18 +155,14 @@ TILE_CASES = [
     (130, 256, 256, 1, 2),    # two groups
     (300, 1000, 640, 1, 2),   # steady state, N tail of 232 columns
     (129, 513, 384, 2, 2),    # split-K slices of 2 and 1 groups
-    (64, 64, 1024, 4, 3),
     (257, 300, 256, 8, 2),    # more slices than groups: empty slices write zeros
     (1, 256, 256, 1, 2),
     (255, 129, 512, 0, 2),
-    (600, 700, 1280, 0, 3),
     (1322, 512, 2560, 1, 2),  # the prefill row count and depth
-    (1322, 512, 2560, 1, 3),
+    (64, 64, 1024, 4, 2),
+    (600, 700, 1280, 0, 2),
+    (77, 257, 640, 1, 2),
     (129, 511, 384, 1, 2),    # N * G odd, no split
-    (77, 257, 640, 1, 3),
-    (300, 1000, 640, 1, 4),
-    (129, 513, 384, 2, 4),
-    (1322, 512, 2560, 1, 4),
 ]
 
 
@@ -190,9 +186,9 @@ GROUPED_CASES = [
     ([1, 1, 1, 1, 1], 64, 128, 0),
     ([37], 256, 384, 2),
     ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 2),
-    ([128, 128, 128], 256, 512, 3),
     ([1, 1, 1, 1, 1], 64, 128, 2),
-    ([0, 0, 0, 50], 128, 128, 3),
+    ([128, 128, 128], 256, 512, 2),
+    ([0, 0, 0, 50], 128, 128, 2),
     ([5, 70, 33], 257, 384, 2),   # N * G odd per weight group: unaligned group bases
 ]
 
