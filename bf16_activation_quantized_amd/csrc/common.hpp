@@ -107,6 +107,20 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
   return r;
 }
 
+// Two dwords shifted right by `sh` with one v_lshrrev_b64 (issued at the rate
+// of a 32-bit shift on gfx950): bits of `hi` that move into `lo` land in
+// positions that the nibble mask clears, so lo >> sh and hi >> sh are both
+// usable for the magic-constant unpack. Inline asm keeps the compiler from
+// splitting it into two 32-bit shifts.
+template <int SH>
+__device__ __forceinline__ void shr64_pair(uint32_t lo, uint32_t hi, uint32_t& olo, uint32_t& ohi) {
+  const uint64_t v = ((uint64_t)hi << 32) | lo;
+  uint64_t r;
+  asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "n"(SH), "v"(v));
+  olo = (uint32_t)r;
+  ohi = (uint32_t)(r >> 32);
+}
+
 // Natural k order: pair j (0..3) = (bf16(128+q[2j]), bf16(128+q[2j+1])).
 // v_perm puts byte j of w into byte 0 and byte j of (w >> 4) into byte 2.
 __device__ __forceinline__ uint32_t magic_pair_natural(uint32_t w, uint32_t w4, int j) {

@@ -354,9 +354,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
   const int Gs = g1 > g0 ? g1 - g0 : 0;        // groups per row in this slice
   // the workgroup owns a contiguous, balanced range of row blocks; its waves
   // take them in turn (block b_lo + wq + WAVES * j)
+  // (the first nblk % grid workgroups take one block more)
   const int nblk = (N + R - 1) / R;
-  const int b_lo = (int)(((int64_t)blockIdx.x * nblk) / gridDim.x);
-  const int b_hi = (int)(((int64_t)(blockIdx.x + 1) * nblk) / gridDim.x);
+  const int bper = nblk / (int)gridDim.x, brem = nblk - bper * (int)gridDim.x;
+  const int b_lo = (int)blockIdx.x * bper + min((int)blockIdx.x, brem);
+  const int b_hi = b_lo + bper + ((int)blockIdx.x < brem ? 1 : 0);
   const int nb = wq < b_hi - b_lo ? (b_hi - b_lo - 1 - wq) / WAVES + 1 : 0;
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)K * 2u);
@@ -391,8 +393,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
   for (int i = 0; i < I; ++i) {
     const int gi = 16 * i + m;                 // block-group of this lane's A row / B column
     const bool ok = gi < R * Gs;
-    const int r = ok ? gi / Gs : 0;
-    const int gin = ok ? gi - r * Gs : 0;
+    // row r and slice group gin of the block-group (by compares: R <= 4)
+    int r = 0, gin = gi;
+#pragma unroll
+    for (int rr = 1; rr < R; ++rr)
+      if (gin >= Gs) { gin -= Gs; ++r; }
+    if (!ok) r = gin = 0;
     // invalid lanes read past the extent (zeros); their products are masked by rmask
     woff[i] = ok ? (uint32_t)r * rowb + (uint32_t)(g0 + gin) * 64u + (uint32_t)kb * 16u : 0xFFFFFFF0u;
     soff[i] = ok ? ((uint32_t)r * (uint32_t)G + (uint32_t)(g0 + gin)) * 2u : 0xFFFFFFF0u;
@@ -531,12 +537,30 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
       }
       f32x4 c = cq[i & 1];
       const uint32_t wd[4] = {wb[i].x, wb[i].y, wb[i].z, wb[i].w};
+      if constexpr (WAVES <= 8) {
+        // two dwords per 64-bit shift where the register budget has room for
+        // the aligned pairs (up to 8 waves)
+        uint32_t w4[4], w8[4], w12[4];
+        shr64_pair<4>(wd[0], wd[1], w4[0], w4[1]);
+        shr64_pair<4>(wd[2], wd[3], w4[2], w4[3]);
+        shr64_pair<8>(wd[0], wd[1], w8[0], w8[1]);
+        shr64_pair<8>(wd[2], wd[3], w8[2], w8[3]);
+        shr64_pair<12>(wd[0], wd[1], w12[0], w12[1]);
+        shr64_pair<12>(wd[2], wd[3], w12[2], w12[3]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w0 = wd[j], w1 = wd[j] >> 4, w2 = wd[j] >> 8, w3 = wd[j] >> 12;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{(w0 & mask) | magic, (w1 & mask) | magic,
-                                                          (w2 & mask) | magic, (w3 & mask) | magic});
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[i & 1][j], c, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{(wd[j] & mask) | magic, (w4[j] & mask) | magic,
+                                                            (w8[j] & mask) | magic, (w12[j] & mask) | magic});
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[i & 1][j], c, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w0 = wd[j], w1 = wd[j] >> 4, w2 = wd[j] >> 8, w3 = wd[j] >> 12;
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{(w0 & mask) | magic, (w1 & mask) | magic,
+                                                            (w2 & mask) | magic, (w3 & mask) | magic});
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[i & 1][j], c, 0, 0, 0);
+        }
       }
       const float v = (c.x * onehot[0] + c.y * onehot[1]) + (c.z * onehot[2] + c.w * onehot[3]);
       const float sv = __uint_as_float((sb[i] << (sshift[i] ^ flip)) & 0xFFFF0000u) * v;
