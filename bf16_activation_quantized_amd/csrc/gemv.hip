@@ -379,10 +379,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
     xv[k] = ld128(rx, p < Gs * 16 ? (uint32_t)(g0 * kGroup) * 2u + 16u * (uint32_t)p : 0xFFFFFFF0u);
   }
 
-  // every wave's x requests enter the compute unit's memory queue ahead of
-  // the first weight request of any wave of the workgroup
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
+  // the wave's x requests go out ahead of its first weight request
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- static per-lane mapping (identical for every block)
