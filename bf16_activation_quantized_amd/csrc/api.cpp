@@ -34,9 +34,17 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // workgroup per compute unit, x held in registers, one weight block in
 // flight per wave (encoding in the dispatcher of gemv.hip).
 constexpr int kGemvDefaultVariant = 2110;
-// Skinny defaults: column tiles per wave and waves per workgroup.
+// Skinny (M <= 16): variants below 1000 are the group-striped layout
+// (10 * waves + column tiles per wave); 1000 * u + 100 * row tiles + 10 *
+// units in flight + waves / 4 is the streaming layout with units of 4 << (u - 1)
+// groups (one workgroup per compute unit, X of the slice in LDS, at most
+// kSkinnyStreamMaxGroups groups per slice). The default is the group-striped
+// layout: at the small-batch decode workload both run at the same rate.
 constexpr int kSkinnyNT = 4;
 constexpr int kSkinnyWaves = 4;
+constexpr int kSkinnyDefaultVariant = 44;
+
+bool skinny_streaming(int variant) { return (variant > 0 ? variant : kSkinnyDefaultVariant) >= 1000; }
 
 Path auto_path(int64_t M, int64_t K, int32_t sk) {
   const int64_t Gk = K / kGroup;
@@ -49,7 +57,7 @@ Path auto_path(int64_t M, int64_t K, int32_t sk) {
   return kPathTile;
 }
 
-int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg) {
+int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg, int variant) {
   const int64_t Gk = K / kGroup;
   int32_t sk = 1;
   if (M >= 512) return 1;   // split-K only for small M ("Split-K without atomics")
@@ -60,6 +68,13 @@ int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg) {
       break;
     }
     case kPathSkinny: {
+      if (skinny_streaming(variant)) {
+        // a slice's X must fit LDS; then enough row blocks x slices for the GPU
+        sk = pow2_at_least(ceil_div(Gk, w4a16::kSkinnyStreamMaxGroups));
+        const int64_t blocks = ceil_div(N, 16);
+        while (sk < 16 && blocks * sk < 1024 && sk * 2 <= Gk) sk <<= 1;
+        break;
+      }
       const int64_t wgs = ceil_div(N, 16 * kSkinnyNT);
       while (sk < 16 && wgs * sk < 512 && ceil_div(Gk, (int64_t)sk * 2) >= kSkinnyWaves) sk <<= 1;
       break;
@@ -108,7 +123,7 @@ w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w
     tile_cfg = variant >= 0 ? variant : default_tile_cfg(M, N);
     if (tile_cfg >= w4a16::tile_num_cfgs()) return W4A16_ERR_SHAPE;
   }
-  int32_t sk = split_k > 0 ? split_k : auto_split(path, M, N, K, tile_cfg);
+  int32_t sk = split_k > 0 ? split_k : auto_split(path, M, N, K, tile_cfg, variant);
   if (sk > Gk && split_k == 0) sk = 1;
   if (path == kPathGemv && ceil_div(Gk, sk) > 64) {
     if (split_k != 0) return W4A16_ERR_SPLIT_K;   // explicit split too small for the GEMV path
@@ -170,8 +185,15 @@ w4a16_status run_gemm(const uint16_t* x, const uint8_t* w, const uint16_t* s, ui
       break;
     }
     case kPathSkinny: {
+      const int v = p.variant > 0 ? p.variant : kSkinnyDefaultVariant;
+      if (v >= 1000 && p.gps <= w4a16::kSkinnyStreamMaxGroups) {
+        e = w4a16::launch_skinny_stream(x, w, s, y, ws_split, iM, iN, iK, p.gps, p.sk, (v / 100) % 10,
+                                        (v / 10) % 10, 4 * (v % 10), 4 << ((v / 1000) - 1), strm);
+        break;
+      }
+      // group-striped layout (also for slices too long for the streaming one)
       int nt = kSkinnyNT, waves = kSkinnyWaves;
-      if (p.variant > 0) { nt = p.variant % 10; waves = p.variant / 10; }
+      if (v < 1000) { nt = v % 10; waves = v / 10; }
       e = w4a16::launch_skinny(x, w, s, y, ws_split, iM, iN, iK, p.gps, p.sk, nt, waves, strm);
       break;
     }

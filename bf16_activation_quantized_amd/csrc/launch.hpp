@@ -18,6 +18,14 @@ hipError_t launch_gemv_m1(const uint16_t* x, const uint8_t* w, const uint16_t* s
 hipError_t launch_skinny(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                          int M, int N, int K, int gps, int sk, int nt, int waves, hipStream_t stream);
 
+// 1 <= M <= 16 decode, streaming layout: one workgroup per compute unit, X of
+// the slice staged in LDS (gps <= kSkinnyStreamMaxGroups), nt row tiles of 16
+// per unit of gb groups, depth units in flight per wave, `waves` per workgroup.
+constexpr int kSkinnyStreamMaxGroups = 32;
+hipError_t launch_skinny_stream(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
+                                int M, int N, int K, int gps, int sk, int nt, int depth, int waves, int gb,
+                                hipStream_t stream);
+
 // out[g * ld + m] = -136 * sum_{k in group g} x[m, k]
 hipError_t launch_rowsum_neg136(const uint16_t* x, float* out, int M, int K, int ld, hipStream_t stream);
 

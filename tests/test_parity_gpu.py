@@ -115,7 +115,7 @@ def test_gemv_parity(N, K, sk, variant):
 # ------------------------------------------------------------------ skinny MFMA (M <= 16)
 
 SKINNY_CASES = [
-    # M, N, K, split_k, variant (10 * waves + column tiles per wave)
+    # M, N, K, split_k, variant (10 * waves + column tiles per wave; or streaming)
     (1, 256, 512, 1, 44),
     (2, 1000, 1024, 1, 44),
     (3, 17, 384, 1, 41),
@@ -126,6 +126,18 @@ SKINNY_CASES = [
     (16, 100, 384, 16, 44),   # more slices than groups
     (7, 300, 640, 1, 82),
     (16, 8192, 1024, 0, None),
+    # streaming layout: 1000 + 100 * row tiles + 10 * units in flight + waves / 4
+    (1, 256, 512, 1, 1131),
+    (3, 17, 384, 1, 1121),        # fewer rows than one 16-row block
+    (5, 100, 640, 1, 3131),       # ragged unit (5 groups in a 16-group unit)
+    (15, 1000, 1024, 2, 2121),
+    (16, 513, 2048, 4, 2122),
+    (16, 1000, 4096, 1, 3112),    # 32 groups in one slice (the LDS maximum)
+    (16, 777, 1280, 4, 1222),     # uneven slices (3, 3, 3, 1 groups)
+    (16, 100, 384, 16, 1131),     # more slices than groups (empty slices write zeros)
+    (16, 512, 8192, 1, 1131),     # slice too long for LDS: group-striped fallback
+    (16, 8192, 8192, 0, None),    # small-batch decode workload, default split
+    (9, 2048, 8192, 2, 1122),
 ]
 
 
