@@ -12,7 +12,7 @@ import torch
 
 import bf16_activation_quantized_amd as w4
 import oracle
-from synth import make_inputs, make_workspace
+from synth import make_config, make_inputs, make_workspace
 from gpu_util import DevCase, bf16_dev, bits_host, check_gate, u8_dev
 
 pytestmark = pytest.mark.gpu
@@ -213,6 +213,64 @@ def test_grouped_parity(ms, N, K, cfg):
     y = w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, variant=cfg)
     torch.cuda.synchronize()
     check_gate(bits_host(y), oracle.gemm_grouped(c.x, d.p_host, c.s, c.m_sizes), f"grouped {ms} N={N} K={K}")
+
+
+# ------------------------------------------------------------------ full sizes, sampled outputs
+
+def _sample_entries(rng, M, N, n_random, row_edges=(), col_edges=()):
+    """Random (row, col) pairs plus the corners of the given row and column
+    boundaries (tile edges, last row and column)."""
+    rows = list(rng.integers(0, M, n_random))
+    cols = list(rng.integers(0, N, n_random))
+    for r in list(row_edges) + [0, M - 1]:
+        for c in list(col_edges) + [0, N - 1]:
+            if 0 <= r < M and 0 <= c < N:
+                rows.append(r)
+                cols.append(c)
+    return np.asarray(rows, dtype=np.int64), np.asarray(cols, dtype=np.int64)
+
+
+def _gate_sampled(y_bits, rows, cols, ref, what):
+    got = y_bits[rows, cols]
+    assert np.all(np.isfinite(oracle.bf16_to_f64(y_bits))), f"{what}: non-finite output"
+    check_gate(got, ref, what)
+
+
+def test_prefill_full_size_sampled():
+    # the deep-prefill workload in the launch configuration bench.py times
+    # (default path and tile configuration), checked on sampled entries
+    c = make_config("prefill")
+    d = DevCase(c)
+    y = bits_host(w4.w4a16_gemm(d.x, d.w, d.s))
+    torch.cuda.synchronize()
+    M, N = c.M, c.N
+    rng = np.random.default_rng(11)
+    rows, cols = _sample_entries(rng, M, N, 3000, row_edges=(127, 128, 1279, 1280, 1321),
+                                 col_edges=(255, 256, 19199, 19200, 19455))
+    ref = oracle.gemm_entries(c.x, d.p_host, c.s, rows, cols)
+    _gate_sampled(y, rows, cols, ref, "prefill 1322x19456x2560 sampled")
+
+
+def test_grouped_full_size_sampled():
+    c = make_config("grouped")
+    d = DevCase(c)
+    y = bits_host(w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes))
+    torch.cuda.synchronize()
+    ms = c.m_sizes.astype(np.int64)
+    starts = oracle.group_starts(ms)
+    rng = np.random.default_rng(12)
+    all_rows, all_cols, all_ref = [], [], []
+    for g in range(ms.shape[0]):
+        if ms[g] == 0:
+            continue
+        r0 = int(starts[g])
+        rows, cols = _sample_entries(rng, int(ms[g]), c.N, 300, row_edges=(127, 128), col_edges=(255, 256))
+        ref = oracle.gemm_entries(c.x[r0:r0 + int(ms[g])], d.p_host[g], c.s[g], rows, cols)
+        all_rows.append(rows + r0)
+        all_cols.append(cols)
+        all_ref.append(ref)
+    _gate_sampled(y, np.concatenate(all_rows), np.concatenate(all_cols), np.concatenate(all_ref),
+                  f"grouped G=8 {list(ms)} sampled")
 
 
 def test_grouped_empty_total_is_noop():
