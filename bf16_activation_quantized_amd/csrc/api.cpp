@@ -107,6 +107,29 @@ int default_tile_cfg(int64_t M, int64_t N) {
   return 2;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+// Grouped launches: the grid holds ceil(M_total / BM) + G row tiles per column
+// tile (group boundaries split tiles). Shorter tiles (96 rows, configuration
+// 3) when that whole grid still fits one wave of workgroups over the compute
+// units: each tile then finishes sooner and no tile waits for a second round.
+int default_grouped_tile_cfg(int64_t G, int64_t M_total, int64_t N) {
+  const int64_t nt = ceil_div(N, 256);
+  if ((ceil_div(M_total, 96) + G) * nt <= device_cus()) return 3;
+  return default_tile_cfg(M_total, N);
+}
+
 w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg, Plan* p) {
   const int64_t Gk = K / kGroup;
   Path path = auto_path(M, K, split_k);
@@ -294,7 +317,7 @@ w4a16_status w4a16_gemm_grouped_ex(const uint16_t* x, const uint8_t* w_packed, c
     return W4A16_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_packed) || !aligned16(scales) || !aligned16(y)) return W4A16_ERR_ALIGN;
   if (((uintptr_t)m_sizes & 3u) != 0) return W4A16_ERR_ALIGN;
-  int tile_cfg = default_tile_cfg(M_total, N);
+  int tile_cfg = default_grouped_tile_cfg(G, M_total, N);
   if (cfg != nullptr) {
     if (cfg->path != 0 && cfg->path != kPathTile) return W4A16_ERR_SHAPE;
     if (cfg->variant >= 0) tile_cfg = cfg->variant;

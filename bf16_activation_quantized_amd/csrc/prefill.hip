@@ -347,6 +347,7 @@ hipError_t launch_prefill(const uint16_t* x, const uint8_t* w, const uint16_t* s
   a.mtiles = 0; a.ntiles = 0;
   switch (row_tiles) {
     case 8: return launch_prefill_t<3, 8>(a, sk, stream);     // 128 x 256 tiles, 3 x 48.5 KiB stages
+    case 6: return launch_prefill_t<3, 6>(a, sk, stream);     // 96 x 256 tiles, 3 x 40.4 KiB stages
     default: return hipErrorInvalidValue;
   }
 }

@@ -211,7 +211,10 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  *            runs variant 44; path 3: tile
  *            configuration index (0: 128x256 and 1: 128x128 with weights
  *            dequantised into LDS; 2 (default): 128x256 with LDS-DMA staging,
- *            8 waves, 3 LDS stages).
+ *            8 waves, 3 LDS stages; 3: the same with 96x256 tiles, the
+ *            default of the grouped call when its whole grid of
+ *            (ceil(M_total/96) + G) x ceil(N/256) tiles fits one workgroup
+ *            per compute unit).
  * An unavailable combination (e.g. path 1 with M != 1, path 2 with M > 16)
  * returns W4A16_ERR_SHAPE.
  */

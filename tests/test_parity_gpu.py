@@ -162,7 +162,7 @@ TILE_CASES = [
     (1, 256, 256, 1, 0),      # one row through the tile kernel (M tail)
     (255, 129, 512, 0, 0),
     (600, 700, 1280, 0, 1),
-    # LDS-DMA kernel: 2 = 8 waves, 3 stages; 3 = 8 waves, 2 stages; 4 = 4 waves, 3 stages
+    # LDS-DMA kernel, 8 waves, 3 stages: 2 = 128 x 256 tiles, 3 = 96 x 256 tiles
     (17, 100, 128, 1, 2),     # one group: no second stage in flight; M and N tails
     (130, 256, 256, 1, 2),    # two groups
     (300, 1000, 640, 1, 2),   # steady state, N tail of 232 columns
@@ -175,6 +175,13 @@ TILE_CASES = [
     (600, 700, 1280, 0, 2),
     (77, 257, 640, 1, 2),
     (129, 511, 384, 1, 2),    # N * G odd, no split
+    (17, 100, 128, 1, 3),
+    (97, 256, 256, 1, 3),     # one row past a 96-row tile
+    (300, 1000, 640, 1, 3),
+    (129, 513, 384, 2, 3),
+    (257, 300, 256, 8, 3),
+    (1322, 512, 2560, 1, 3),
+    (95, 129, 512, 0, 3),
 ]
 
 
@@ -202,6 +209,10 @@ GROUPED_CASES = [
     ([128, 128, 128], 256, 512, 2),
     ([0, 0, 0, 50], 128, 128, 2),
     ([5, 70, 33], 257, 384, 2),   # N * G odd per weight group: unaligned group bases
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 3),   # 96-row tiles
+    ([96, 97, 95, 0, 1], 256, 640, 3),
+    ([37], 256, 384, 3),
+    ([0, 0, 0, 50], 128, 128, 3),
 ]
 
 
