@@ -2,6 +2,8 @@
 // enqueued), path and split-K selection, workspace layout and launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include <stddef.h>
 #include <stdint.h>
 
@@ -40,9 +42,9 @@ constexpr int kGemvDefaultVariant = 2110;
 // groups (one workgroup per compute unit, X of the slice in LDS, at most
 // kSkinnyStreamMaxGroups groups per slice). The default is the group-striped
 // layout: at the small-batch decode workload both run at the same rate.
-constexpr int kSkinnyNT = 4;
-constexpr int kSkinnyWaves = 4;
-constexpr int kSkinnyDefaultVariant = 44;
+constexpr int kSkinnyNT = 2;
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyDefaultVariant = 10 * kSkinnyWaves + kSkinnyNT;
 
 bool skinny_streaming(int variant) { return (variant > 0 ? variant : kSkinnyDefaultVariant) >= 1000; }
 
@@ -75,8 +77,11 @@ int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg, int
         while (sk < 16 && blocks * sk < 1024 && sk * 2 <= Gk) sk <<= 1;
         break;
       }
-      const int64_t wgs = ceil_div(N, 16 * kSkinnyNT);
-      while (sk < 16 && wgs * sk < 512 && ceil_div(Gk, (int64_t)sk * 2) >= kSkinnyWaves) sk <<= 1;
+      // one workgroup per compute unit or more; every wave keeps at least one group
+      const int v = variant > 0 ? variant : kSkinnyDefaultVariant;
+      const int nt = v % 10, waves = v / 10;
+      const int64_t wgs = ceil_div(N, 16 * (int64_t)std::max(nt, 1));
+      while (sk < 16 && wgs * sk < 256 && ceil_div(Gk, (int64_t)sk * 2) >= waves) sk <<= 1;
       break;
     }
     case kPathTile: {

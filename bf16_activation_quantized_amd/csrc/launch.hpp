@@ -22,6 +22,9 @@ hipError_t launch_skinny(const uint16_t* x, const uint8_t* w, const uint16_t* s,
 // the slice staged in LDS (gps <= kSkinnyStreamMaxGroups), nt row tiles of 16
 // per unit of gb groups, depth units in flight per wave, `waves` per workgroup.
 constexpr int kSkinnyStreamMaxGroups = 32;
+// slices of at most this many groups stage their scales in LDS (16 NT x gps x 2
+// bytes, at most 32 KiB)
+constexpr int kSkinnyMaxScaleGroups = 256;
 hipError_t launch_skinny_stream(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                                 int M, int N, int K, int gps, int sk, int nt, int depth, int waves, int gb,
                                 hipStream_t stream);

@@ -20,7 +20,12 @@
 //
 // Work split: a workgroup of WAVES waves owns a column block; its waves take
 // the 128-groups of the K-slice round robin and are reduced through LDS at
-// the end. gridDim.y = SK slices ("Add Triton BF16xINT4 rowwise GEMM for
+// the end. A group's X is fetched in whole cache lines (4 rows x 256 bytes
+// per instruction) and transposed into the MFMA layout through a per-wave
+// LDS tile; the slice's scales of the block's columns are staged in LDS once.
+// Fetched in the MFMA layout instead, X (16 rows x 4 pieces spread over 256
+// bytes per instruction) and the scales (one line per column) cost more
+// address-unit time than the weight stream itself. gridDim.y = SK slices ("Add Triton BF16xINT4 rowwise GEMM for
 // ROCm gfx942/gfx950", Implementation "Split-K without atomics": fp32
 // partials to ws[s, :, :] with plain stores).
 #include <algorithm>
@@ -34,7 +39,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
   return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
 }
 
-template <int NT, int WAVES>
+template <int NT, int WAVES, bool SLDS>
 __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __restrict__ x,
                                                             const uint8_t* __restrict__ w,
                                                             const uint16_t* __restrict__ s,
@@ -42,6 +47,13 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
                                                             float* __restrict__ ws,
                                                             int M, int N, int K, int gps) {
   __shared__ f32x4 red[WAVES > 1 ? (WAVES - 1) : 1][NT][64];
+  // per-wave staging of one group of X: [16 rows][16 slots of 16 bytes], the
+  // piece p of row r in slot p ^ r (conflict-free for both access patterns)
+  __shared__ u32x4 xst[WAVES][16 * 16];
+  // SLDS: the slice's scales of the workgroup's 16 NT columns, [column][group]
+  // (dynamic size 16 NT x gps x 2 bytes), fetched once in whole lines; per
+  // group the lanes then read LDS instead of one line per column
+  extern __shared__ uint16_t scl[];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -52,13 +64,18 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
   const int g0 = slice * gps;
   const int g1 = min(G, g0 + gps);
   const int nb = blockIdx.x * 16 * NT;
+  const int gs = g1 > g0 ? g1 - g0 : 0;
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint32_t)((uint64_t)N * (uint32_t)K / 2u));
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, (uint32_t)N * (uint32_t)G * 2u);
 
-  // per-lane row bases
-  const uint32_t xrow = (uint32_t)col * (uint32_t)K * 2u + (uint32_t)kb * 64u;   // row m = col
+  // per-lane row bases. X is fetched in whole cache lines: load j of a group
+  // covers rows 4 j .. 4 j + 3, lane l reading 16-byte piece l % 16 of row
+  // 4 j + l / 16 (a fetch in the MFMA layout would touch 32 partly used lines
+  // per instruction); the wave then transposes the group through LDS.
+  const uint32_t xrow = (uint32_t)(lane >> 4) * (uint32_t)K * 2u + 16u * (uint32_t)(lane & 15);
+  const uint32_t xrow4 = 4u * (uint32_t)K * 2u;
   uint32_t wrow[NT], srow[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -82,18 +99,26 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
   auto issue = [&](u32x4 (&xb)[4], u32x4 (&wb)[NT], uint16_t (&sb)[NT], int g) {
     const uint32_t xo = xrow + (uint32_t)g * 256u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xb[j] = ld128(rx, xo + 16u * j);
+    for (int j = 0; j < 4; ++j) xb[j] = ld128(rx, xo + xrow4 * (uint32_t)j);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       wb[t] = ld128(rw, wrow[t] + (uint32_t)g * 64u);
-      sb[t] = ld16(rs, srow[t] + (uint32_t)g * 2u);
+      if constexpr (!SLDS) sb[t] = ld16(rs, srow[t] + (uint32_t)g * 2u);
+      else sb[t] = (uint16_t)(16 * t + col) * (uint16_t)gs + (uint16_t)(g - g0);   // LDS index
     }
   };
   auto compute = [&](const u32x4 (&xb)[4], const u32x4 (&wb)[NT], const uint16_t (&sb)[NT]) {
+    u32x4* xw = xst[wave];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * j + (lane >> 4), pc = lane & 15;
+      xw[16 * r + (pc ^ r)] = xb[j];
+    }
     bf16x8 a[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x4 v = xb[j];
+      // row m = col, piece 4 kb + j: k = 128 g + 32 kb + 8 j + 0..7
+      const u32x4 v = xw[16 * col + ((4 * kb + j) ^ col)];
       a[j] = as_bf16x8(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
                        __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
     }
@@ -112,7 +137,7 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
                                    magic_pair_interleaved(wd[j], 2), magic_pair_interleaved(wd[j], 3));
         tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b, tmp, 0, 0, 0);
       }
-      const float sc = bf16f(sb[t]);
+      const float sc = bf16f(SLDS ? scl[sb[t]] : sb[t]);
       acc[t].x = fmaf(sc, tmp.x, acc[t].x);
       acc[t].y = fmaf(sc, tmp.y, acc[t].y);
       acc[t].z = fmaf(sc, tmp.z, acc[t].z);
@@ -121,15 +146,61 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
   };
 
   int g = g0 + wave;
-  if (g < g1) issue(xb0, wb0, sb0, g);
-  while (g < g1) {
+  if constexpr (SLDS) {
+    // scales first (the wait for them then covers nothing else), then the
+    // wave's first two groups, then the scales go to LDS
+    constexpr int kB = 16;               // loads per batch
+    const int per_col = (gs + 63) / 64;  // 64-scale chunks per column
+    const int items = (16 * NT / WAVES) * per_col;
+    uint16_t sv[kB];
+    auto sc_item = [&](int it, int& c, int& gi) {
+      c = wave + WAVES * (it / per_col);
+      gi = 64 * (it % per_col) + lane;
+    };
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      int c, gi;
+      sc_item(b, c, gi);
+      sv[b] = b < items && gi < gs ? ld16(rs, ((uint32_t)(nb + c) * (uint32_t)G + (uint32_t)(g0 + gi)) * 2u) : 0;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (g < g1) issue(xb0, wb0, sb0, g);
     if (g + WAVES < g1) issue(xb1, wb1, sb1, g + WAVES);
-    compute(xb0, wb0, sb0);
-    g += WAVES;
-    if (g >= g1) break;
-    if (g + WAVES < g1) issue(xb0, wb0, sb0, g + WAVES);
-    compute(xb1, wb1, sb1);
-    g += WAVES;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      int c, gi;
+      sc_item(b, c, gi);
+      if (b < items && gi < gs) scl[c * gs + gi] = sv[b];
+    }
+    for (int it0 = kB; it0 < items; it0 += kB) {
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        int c, gi;
+        sc_item(it0 + b, c, gi);
+        if (it0 + b < items && gi < gs) scl[c * gs + gi] = ld16(rs, ((uint32_t)(nb + c) * (uint32_t)G + (uint32_t)(g0 + gi)) * 2u);
+      }
+    }
+    __syncthreads();
+    while (g < g1) {
+      compute(xb0, wb0, sb0);
+      if (g + 2 * WAVES < g1) issue(xb0, wb0, sb0, g + 2 * WAVES);
+      g += WAVES;
+      if (g >= g1) break;
+      compute(xb1, wb1, sb1);
+      if (g + 2 * WAVES < g1) issue(xb1, wb1, sb1, g + 2 * WAVES);
+      g += WAVES;
+    }
+  } else {
+    if (g < g1) issue(xb0, wb0, sb0, g);
+    while (g < g1) {
+      if (g + WAVES < g1) issue(xb1, wb1, sb1, g + WAVES);
+      compute(xb0, wb0, sb0);
+      g += WAVES;
+      if (g >= g1) break;
+      if (g + WAVES < g1) issue(xb0, wb0, sb0, g + WAVES);
+      compute(xb1, wb1, sb1);
+      g += WAVES;
+    }
   }
 
   // cross-wave reduction: waves 1.. park their tiles in LDS, wave 0 sums
@@ -436,12 +507,28 @@ hipError_t launch_skinny_stream(const uint16_t* x, const uint8_t* w, const uint1
 
 hipError_t launch_skinny(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                          int M, int N, int K, int gps, int sk, int nt, int waves, hipStream_t stream) {
-#define W4A16_SKINNY(NTT, WV)                                                                      \
-  if (nt == NTT && waves == WV) {                                                                  \
-    dim3 grid((N + 16 * NTT - 1) / (16 * NTT), sk);                                                \
-    hipLaunchKernelGGL((skinny_kernel<NTT, WV>), grid, dim3(64 * WV), 0, stream, x, w, s, y, ws, M, \
-                       N, K, gps);                                                                 \
-    return hipGetLastError();                                                                      \
+  // scales staged in LDS while the slice's scale block stays small
+  const bool slds = gps <= kSkinnyMaxScaleGroups;
+#define W4A16_SKINNY(NTT, WV)                                                                          \
+  if (nt == NTT && waves == WV) {                                                                      \
+    dim3 grid((N + 16 * NTT - 1) / (16 * NTT), sk);                                                    \
+    if (slds) {                                                                                        \
+      const size_t dyn = ((size_t)16 * NTT * gps * 2 + 15) & ~(size_t)15;                              \
+      static bool attr = false; /* per instantiation: the attribute is per function */                \
+      if (!attr) {                                                                                     \
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<NTT, WV, true>), \
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,                \
+                                           16 * NTT * kSkinnyMaxScaleGroups * 2);                      \
+        if (e != hipSuccess) return e;                                                                 \
+        attr = true;                                                                                   \
+      }                                                                                                \
+      hipLaunchKernelGGL((skinny_kernel<NTT, WV, true>), grid, dim3(64 * WV), dyn, stream, x, w, s, y, \
+                         ws, M, N, K, gps);                                                            \
+    } else {                                                                                           \
+      hipLaunchKernelGGL((skinny_kernel<NTT, WV, false>), grid, dim3(64 * WV), 0, stream, x, w, s, y,  \
+                         ws, M, N, K, gps);                                                            \
+    }                                                                                                  \
+    return hipGetLastError();                                                                          \
   }
   W4A16_SKINNY(1, 4)
   W4A16_SKINNY(2, 4)
