@@ -106,12 +106,6 @@ struct Plan {
 };
 
 // Tile configuration 2 (LDS-DMA staging, 8 waves of 128 x 32, tile.hip).
-int default_tile_cfg(int64_t M, int64_t N) {
-  (void)M;
-  (void)N;
-  return 2;
-}
-
 // Compute units of the current device (cached per device).
 int device_cus() {
   static int cache[64] = {0};
@@ -129,10 +123,38 @@ int device_cus() {
 // tile (group boundaries split tiles). Shorter tiles (96 rows, configuration
 // 3) when that whole grid still fits one wave of workgroups over the compute
 // units: each tile then finishes sooner and no tile waits for a second round.
+// Tile height of the LDS-DMA kernel for `tiles(bm)` output tiles on the
+// device's compute units (one workgroup per unit): the fewest rounds x rows
+// per tile, each height weighted by its measured per-row rate relative to
+// the 128-row tile (shorter tiles amortise the per-group dequantisation and
+// barrier over fewer rows; at 1322 x 19456: 4 rounds of 128 rows 170 us, 4
+// of 112 rows 162 us, 5 of 96 rows 176 us).
+template <class F>
+int pick_tile_cfg(F tiles) {
+  struct Cand { int cfg, bm; double rate; };
+  static const Cand cands[] = {{2, 128, 1.0}, {4, 112, 0.917}, {3, 96, 0.907}};
+  const int64_t cus = device_cus();
+  int best = 2;
+  double best_cost = 0.0;
+  for (const Cand& c : cands) {
+    const double cost = (double)ceil_div(tiles(c.bm), cus) * c.bm / c.rate;
+    if (best_cost == 0.0 || cost < best_cost * (1.0 - 1e-9)) {
+      best = c.cfg;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+int default_tile_cfg(int64_t M, int64_t N) {
+  const int64_t nt = ceil_div(N, 256);
+  return pick_tile_cfg([&](int bm) { return ceil_div(std::max<int64_t>(M, 1), bm) * nt; });
+}
+
+// grouped: the host bound on the tile count, ceil(M_total / bm) + G per column
 int default_grouped_tile_cfg(int64_t G, int64_t M_total, int64_t N) {
   const int64_t nt = ceil_div(N, 256);
-  if ((ceil_div(M_total, 96) + G) * nt <= device_cus()) return 3;
-  return default_tile_cfg(M_total, N);
+  return pick_tile_cfg([&](int bm) { return (ceil_div(std::max<int64_t>(M_total, 1), bm) + G) * nt; });
 }
 
 w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg, Plan* p) {

@@ -10,7 +10,7 @@
 // accumulator. No weight is ever rounded.
 //
 // Structure (one 512-thread workgroup per (16 MS) x 256 output tile, 8 waves
-// of (16 MS) x 32, MS = 8; one workgroup per compute unit):
+// of (16 MS) x 32, MS = 6, 7 or 8; one workgroup per compute unit):
 //  * one K-stage = one 128-group: X [16 MS rows, 128 k] bf16, the packed
 //    weights [256 rows, 64 B] (16 KiB, still 4-bit) and the 16 MS row sums;
 //    NSTAGE stages in LDS, filled by buffer loads that write LDS directly (no
@@ -84,14 +84,15 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst
 template <int NSTAGE, int MS>
 __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs args) {
   static_assert(NSTAGE == 2 || NSTAGE == 3, "stages");
-  static_assert(MS % 2 == 0 && MS <= 16, "row tiles");
+  static_assert(MS >= 2 && MS <= 16, "row tiles");
   using ST = Stage<MS>;
   constexpr int BM = ST::kRows;
   constexpr int TN = kPN / kNW;         // columns per wave (32)
   constexpr int SN = TN / 16;           // 16-column MFMA tiles per wave (2)
-  constexpr int QX = MS / 2;            // X DMA instructions per wave and group (4 rows of 256 B each)
+  constexpr int NQX = 4 * MS;           // X DMA instructions per group (4 rows of 256 B each)
+  constexpr int QX = (NQX + kNW - 1) / kNW;   // per wave (block q = wave + 8 i)
   constexpr int QW = 16 / kNW;          // W DMA instructions per wave and group
-  constexpr int RL = MS / 2;            // row-sum DMA lanes per wave (16 B = 4 rows each)
+  constexpr int RL = 4 * MS;            // row-sum DMA lanes of wave 0 (16 B = 4 rows each)
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -124,10 +125,10 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   const int ng = ge > gb ? ge - gb : 0;
 
   // ---- DMA lane offsets (constant over groups)
-  // X instruction i of wave wv fills LDS block q = QX wv + i, i.e. tile rows
-  // 4 q + (lane >> 4), slot lane & 15; the chunk stored in slot p of row r is
-  // p ^ (r & 7), and r & 7 = 4 (q & 1) + (lane >> 4): row offset
-  // 4 (q & ~1) KB plus xvo[q & 1].
+  // X instruction i of wave wv fills LDS block q = wv + 8 i (if q < 4 MS),
+  // i.e. tile rows 4 q + (lane >> 4), slot lane & 15; the chunk stored in
+  // slot p of row r is p ^ (r & 7), and r & 7 = 4 (q & 1) + (lane >> 4): row
+  // offset 4 (q & ~1) KB plus xvo[q & 1].
   // (recomputed from the lane id at each issue: a few VALU ops per group
   // instead of registers held across the main loop)
   auto xvo = [&](int e) {
@@ -140,8 +141,8 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     const int wr = lane >> 2, wp = lane & 3;
     return (uint32_t)(16 * QW * wv + wr) * K2 + 16u * (uint32_t)(wp ^ ((wr >> 1) & 3));
   };
-  // row sums: lanes 0..RL-1 of each wave fetch 4 rows each
-  auto rvo = [&]() { return (uint32_t)(4 * RL * wv + 4 * lane) * 4u; };
+  // row sums: lanes 0..RL-1 of wave 0 fetch 4 rows each
+  auto rvo = [&]() { return (uint32_t)(4 * lane) * 4u; };
 
   // Row offsets always go into the vector offset, which the hardware range
   // checks against the buffer extent (rows past the tile read zeros); the
@@ -155,14 +156,15 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     const uint32_t xo0 = xvo(0), xo1 = xvo(1);
 #pragma unroll
     for (int i = 0; i < QX; ++i) {
-      const int q = QX * wv + i;
-      dma16(rx, base + 1024 * q, ((q & 1) ? xo1 : xo0) + (uint32_t)(4 * (q & ~1)) * KB, gx);
+      const int q = wv + kNW * i;   // wave-uniform
+      if (NQX % kNW == 0 || q < NQX)
+        dma16(rx, base + 1024 * q, ((q & 1) ? xo1 : xo0) + (uint32_t)(4 * (q & ~1)) * KB, gx);
     }
     const uint32_t wo = wvo();
 #pragma unroll
     for (int i = 0; i < QW; ++i) dma16(rw, base + ST::kX + 1024 * (QW * wv + i), wo + (uint32_t)i * 16u * K2, gw);
-    if (lane < RL)
-      dma16(rsx, base + ST::kX + ST::kW + 16 * RL * wv, rvo() + (uint32_t)g * (uint32_t)args.ld * 4u, 0u);
+    if (wv == 0 && lane < RL)
+      dma16(rsx, base + ST::kX + ST::kW, rvo() + (uint32_t)g * (uint32_t)args.ld * 4u, 0u);
   };
 
   // ---- scales: the aligned word holding s[n][g] for this lane's SN columns
@@ -347,6 +349,7 @@ hipError_t launch_prefill(const uint16_t* x, const uint8_t* w, const uint16_t* s
   a.mtiles = 0; a.ntiles = 0;
   switch (row_tiles) {
     case 8: return launch_prefill_t<3, 8>(a, sk, stream);     // 128 x 256 tiles, 3 x 48.5 KiB stages
+    case 7: return launch_prefill_t<3, 7>(a, sk, stream);     // 112 x 256 tiles, 3 x 44.4 KiB stages
     case 6: return launch_prefill_t<3, 6>(a, sk, stream);     // 96 x 256 tiles, 3 x 40.4 KiB stages
     default: return hipErrorInvalidValue;
   }

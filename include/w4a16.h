@@ -210,11 +210,13 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  *            2122, 3121, 3112, 3131; with more than 32 groups per slice it
  *            runs variant 82; path 3: tile
  *            configuration index (0: 128x256 and 1: 128x128 with weights
- *            dequantised into LDS; 2 (default): 128x256 with LDS-DMA staging,
- *            8 waves, 3 LDS stages; 3: the same with 96x256 tiles, the
- *            default of the grouped call when its whole grid of
- *            (ceil(M_total/96) + G) x ceil(N/256) tiles fits one workgroup
- *            per compute unit).
+ *            dequantised into LDS; 2: 128x256 with LDS-DMA staging, 8
+ *            waves, 3 LDS stages; 3: the same with 96x256 tiles; 4: the
+ *            same with 112x256 tiles). By default the call picks among 2, 3
+ *            and 4 the tile height with the fewest rounds of one workgroup
+ *            per compute unit times rows per tile, weighted by each
+ *            height's measured per-row rate (the grouped call counts
+ *            ceil(M_total/h) + G row tiles per column).
  * An unavailable combination (e.g. path 1 with M != 1, path 2 with M > 16)
  * returns W4A16_ERR_SHAPE.
  */

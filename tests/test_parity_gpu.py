@@ -182,6 +182,15 @@ TILE_CASES = [
     (257, 300, 256, 8, 3),
     (1322, 512, 2560, 1, 3),
     (95, 129, 512, 0, 3),
+    # 4 = 112 x 256 tiles (7 row tiles: the X stage is 28 DMA blocks over 8 waves)
+    (17, 100, 128, 1, 4),
+    (113, 256, 256, 1, 4),    # one row past a 112-row tile
+    (300, 1000, 640, 1, 4),
+    (129, 513, 384, 2, 4),
+    (257, 300, 256, 8, 4),
+    (1322, 512, 2560, 1, 4),
+    (111, 129, 512, 0, 4),
+    (224, 257, 384, 1, 4),    # exactly two tiles; N * G odd
 ]
 
 
@@ -213,6 +222,9 @@ GROUPED_CASES = [
     ([96, 97, 95, 0, 1], 256, 640, 3),
     ([37], 256, 384, 3),
     ([0, 0, 0, 50], 128, 128, 3),
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 4),   # 112-row tiles
+    ([112, 113, 111, 0, 1], 256, 640, 4),
+    ([37], 256, 384, 4),
 ]
 
 
@@ -256,7 +268,7 @@ def test_prefill_full_size_sampled():
     torch.cuda.synchronize()
     M, N = c.M, c.N
     rng = np.random.default_rng(11)
-    rows, cols = _sample_entries(rng, M, N, 3000, row_edges=(127, 128, 1279, 1280, 1321),
+    rows, cols = _sample_entries(rng, M, N, 3000, row_edges=(111, 112, 127, 128, 1231, 1232, 1279, 1280, 1321),
                                  col_edges=(255, 256, 19199, 19200, 19455))
     ref = oracle.gemm_entries(c.x, d.p_host, c.s, rows, cols)
     _gate_sampled(y, rows, cols, ref, "prefill 1322x19456x2560 sampled")
