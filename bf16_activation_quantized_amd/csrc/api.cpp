@@ -132,7 +132,7 @@ int device_cus() {
 template <class F>
 int pick_tile_cfg(F tiles) {
   struct Cand { int cfg, bm; double rate; };
-  static const Cand cands[] = {{2, 128, 1.0}, {4, 112, 0.917}, {3, 96, 0.907}};
+  static const Cand cands[] = {{2, 128, 1.0}, {4, 112, 0.917}, {3, 96, 0.907}, {5, 80, 0.85}};
   const int64_t cus = device_cus();
   int best = 2;
   double best_cost = 0.0;
@@ -151,10 +151,12 @@ int default_tile_cfg(int64_t M, int64_t N) {
   return pick_tile_cfg([&](int bm) { return ceil_div(std::max<int64_t>(M, 1), bm) * nt; });
 }
 
-// grouped: the host bound on the tile count, ceil(M_total / bm) + G per column
+// grouped: M_sizes stays on the device, so the tile count is estimated as
+// ceil(M_total / bm) + G / 2 per column (each group's partial last tile
+// adds half a tile on average; the kernel maps only the real tiles)
 int default_grouped_tile_cfg(int64_t G, int64_t M_total, int64_t N) {
   const int64_t nt = ceil_div(N, 256);
-  return pick_tile_cfg([&](int bm) { return (ceil_div(std::max<int64_t>(M_total, 1), bm) + G) * nt; });
+  return pick_tile_cfg([&](int bm) { return (ceil_div(std::max<int64_t>(M_total, 1), bm) + G / 2) * nt; });
 }
 
 w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg, Plan* p) {

@@ -10,7 +10,7 @@
 // accumulator. No weight is ever rounded.
 //
 // Structure (one 512-thread workgroup per (16 MS) x 256 output tile, 8 waves
-// of (16 MS) x 32, MS = 6, 7 or 8; one workgroup per compute unit):
+// of (16 MS) x 32, MS = 5 .. 8; one workgroup per compute unit):
 //  * one K-stage = one 128-group: X [16 MS rows, 128 k] bf16, the packed
 //    weights [256 rows, 64 B] (16 KiB, still 4-bit) and the 16 MS row sums;
 //    NSTAGE stages in LDS, filled by buffer loads that write LDS directly (no
@@ -101,7 +101,13 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   const int Gk = args.K / kGroup;
 
   int mt, nt;
-  tile_coords(blockIdx.x, gridDim.x, args.mtiles, args.ntiles, &mt, &nt);
+  int MT = args.mtiles, nblocks = (int)gridDim.x;
+  if (args.m_sizes != nullptr) {
+    MT = real_mtiles(BM, args.M_total, args.m_sizes, args.G);
+    nblocks = MT * args.ntiles;
+    if ((int)blockIdx.x >= nblocks) return;
+  }
+  tile_coords(blockIdx.x, nblocks, MT, args.ntiles, &mt, &nt);
   const TileRows tr = tile_rows(mt, BM, args.M_total, args.m_sizes, args.G);
   if (tr.rows <= 0) return;
   const int row0 = tr.row0, rows = tr.rows;
@@ -351,6 +357,7 @@ hipError_t launch_prefill(const uint16_t* x, const uint8_t* w, const uint16_t* s
     case 8: return launch_prefill_t<3, 8>(a, sk, stream);     // 128 x 256 tiles, 3 x 48.5 KiB stages
     case 7: return launch_prefill_t<3, 7>(a, sk, stream);     // 112 x 256 tiles, 3 x 44.4 KiB stages
     case 6: return launch_prefill_t<3, 6>(a, sk, stream);     // 96 x 256 tiles, 3 x 40.4 KiB stages
+    case 5: return launch_prefill_t<3, 5>(a, sk, stream);     // 80 x 256 tiles, 3 x 36.3 KiB stages
     default: return hipErrorInvalidValue;
   }
 }

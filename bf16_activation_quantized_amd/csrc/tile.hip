@@ -100,7 +100,13 @@ __global__ __launch_bounds__(64 * WM * WN) void tile_kernel(const TileArgs args)
 
   // ---- tile id and rows
   int mt_lin, nt;
-  tile_coords(blockIdx.x, gridDim.x, args.mtiles, args.ntiles, &mt_lin, &nt);
+  int MT = args.mtiles, nblocks = (int)gridDim.x;
+  if (args.m_sizes != nullptr) {
+    MT = real_mtiles(BM, args.M_total, args.m_sizes, args.G);
+    nblocks = MT * args.ntiles;
+    if ((int)blockIdx.x >= nblocks) return;
+  }
+  tile_coords(blockIdx.x, nblocks, MT, args.ntiles, &mt_lin, &nt);
   const TileRows tr = tile_rows(mt_lin, BM, args.M_total, args.m_sizes, args.G);
   const int wg = tr.wg, row0 = tr.row0, rows = tr.rows;
   if (rows <= 0) return;
@@ -314,7 +320,7 @@ static hipError_t launch_tile_t(const TileArgs& a0, int mtiles_bound, int sk, hi
 //   1: 128 x 128, 2 x 2 waves of 64 x 64, weights dequantised into LDS
 //   2: 128 x 256, 8 waves of 128 x 32, LDS-DMA staging, 3 stages (prefill.hip)
 struct TileCfg { int bm, bn; };
-static const TileCfg kTileCfgs[] = {{128, 256}, {128, 128}, {128, 256}, {96, 256}, {112, 256}};
+static const TileCfg kTileCfgs[] = {{128, 256}, {128, 128}, {128, 256}, {96, 256}, {112, 256}, {80, 256}};
 int tile_num_cfgs() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0])); }
 int tile_bm(int cfg) { return kTileCfgs[cfg].bm; }
 int tile_bn(int cfg) { return kTileCfgs[cfg].bn; }
@@ -323,7 +329,7 @@ hipError_t launch_tile(const uint16_t* x, const uint8_t* w, const uint16_t* s, c
                        float* ws, const int32_t* m_sizes, int M_total, int N, int K, int G, int ld, int gps,
                        int sk, int cfg, hipStream_t stream) {
   if (cfg < 0 || cfg >= tile_num_cfgs()) return hipErrorInvalidValue;
-  if (cfg >= 2)   // LDS-DMA kernel: 8 (cfg 2), 6 (cfg 3) or 7 (cfg 4) row tiles of 16
+  if (cfg >= 2)   // LDS-DMA kernel: 8 (cfg 2), 6 (cfg 3), 7 (cfg 4) or 5 (cfg 5) row tiles of 16
     return launch_prefill(x, w, s, sxn, y, ws, m_sizes, M_total, N, K, G, ld, gps, sk, kTileCfgs[cfg].bm / 16, stream);
   TileArgs a;
   a.x = x; a.w = w; a.s = s; a.sxn = sxn; a.y = y; a.ws = ws; a.m_sizes = m_sizes;

@@ -58,4 +58,21 @@ __device__ __forceinline__ TileRows tile_rows(int mt, int BM, int M_total, const
   return t;
 }
 
+// Grouped: the m-tiles that hold rows, sum over groups of ceil(m_g / BM)
+// (same clamping as tile_rows). The grid is sized on the host from the bound
+// ceil(M_total / BM) + G per column; mapping only the real tiles, spread
+// evenly over the XCDs, keeps the empty ones from taking a share of one XCD
+// that its 32 compute units then lack for real tiles.
+__device__ __forceinline__ int real_mtiles(int BM, int M_total, const int32_t* m_sizes, int G) {
+  int cnt = 0, start = 0;
+  for (int gg = 0; gg < G; ++gg) {
+    int ms = m_sizes[gg];
+    ms = ms < 0 ? 0 : ms;
+    ms = start >= M_total ? 0 : min(ms, M_total - start);
+    cnt += (ms + BM - 1) / BM;
+    start += ms;
+  }
+  return __builtin_amdgcn_readfirstlane(cnt);
+}
+
 }  // namespace w4a16

@@ -211,12 +211,12 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  *            runs variant 82; path 3: tile
  *            configuration index (0: 128x256 and 1: 128x128 with weights
  *            dequantised into LDS; 2: 128x256 with LDS-DMA staging, 8
- *            waves, 3 LDS stages; 3: the same with 96x256 tiles; 4: the
- *            same with 112x256 tiles). By default the call picks among 2, 3
- *            and 4 the tile height with the fewest rounds of one workgroup
- *            per compute unit times rows per tile, weighted by each
- *            height's measured per-row rate (the grouped call counts
- *            ceil(M_total/h) + G row tiles per column).
+ *            waves, 3 LDS stages; 3, 4, 5: the same with 96x256, 112x256
+ *            and 80x256 tiles). By default the call picks among 2 to 5 the
+ *            tile height with the fewest rounds of one workgroup per compute
+ *            unit times rows per tile, weighted by each height's measured
+ *            per-row rate (the grouped call estimates ceil(M_total/h) + G/2
+ *            row tiles per column).
  * An unavailable combination (e.g. path 1 with M != 1, path 2 with M > 16)
  * returns W4A16_ERR_SHAPE.
  */

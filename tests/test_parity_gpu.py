@@ -191,6 +191,12 @@ TILE_CASES = [
     (1322, 512, 2560, 1, 4),
     (111, 129, 512, 0, 4),
     (224, 257, 384, 1, 4),    # exactly two tiles; N * G odd
+    # 5 = 80 x 256 tiles (20 X DMA blocks over 8 waves)
+    (17, 100, 128, 1, 5),
+    (81, 256, 256, 1, 5),
+    (300, 1000, 640, 1, 5),
+    (257, 300, 256, 8, 5),
+    (1322, 512, 2560, 1, 5),
 ]
 
 
@@ -225,6 +231,9 @@ GROUPED_CASES = [
     ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 4),   # 112-row tiles
     ([112, 113, 111, 0, 1], 256, 640, 4),
     ([37], 256, 384, 4),
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 5),   # 80-row tiles
+    ([80, 81, 79, 0, 1], 256, 640, 5),
+    ([0, 0, 0, 0, 0, 0, 0, 700], 512, 256, 5),      # all rows in the last group
 ]
 
 
