@@ -127,12 +127,12 @@ int device_cus() {
 // device's compute units (one workgroup per unit): the fewest rounds x rows
 // per tile, each height weighted by its measured per-row rate relative to
 // the 128-row tile (shorter tiles amortise the per-group dequantisation and
-// barrier over fewer rows; at 1322 x 19456: 4 rounds of 128 rows 170 us, 4
-// of 112 rows 162 us, 5 of 96 rows 176 us).
+// barrier over fewer rows; at 1322 x 19456 on one box: 4 rounds of 128 rows
+// 166 us, 4 of 112 rows 161 us, 3 of 144 rows 146 us, 5 of 96 rows 176 us).
 template <class F>
 int pick_tile_cfg(F tiles) {
   struct Cand { int cfg, bm; double rate; };
-  static const Cand cands[] = {{2, 128, 1.0}, {4, 112, 0.917}, {3, 96, 0.907}, {5, 80, 0.85}};
+  static const Cand cands[] = {{2, 128, 1.0}, {6, 144, 0.96}, {4, 112, 0.91}, {3, 96, 0.907}, {5, 80, 0.85}};
   const int64_t cus = device_cus();
   int best = 2;
   double best_cost = 0.0;

@@ -33,28 +33,29 @@ namespace w4a16 {
 
 // ---------------------------------------------------------------- row sums
 // out[g * ld + m] = -136 * sum_{k in group g} x[m, k], fp32. One wave per
-// row; a wave instruction covers 512 consecutive k (4 groups), a group's 16
-// lanes are summed with a 16-lane reduction.
+// row; a wave instruction covers 512 consecutive k (4 groups) and up to 8 of
+// them are in flight before any is reduced; a group's 16 lanes are summed
+// with DPP row sums. Loads past the row read zeros (exact buffer extent).
 __global__ __launch_bounds__(256) void rowsum_neg136_kernel(const uint16_t* __restrict__ x,
                                                            float* __restrict__ out, int M, int K,
                                                            int ld) {
+  constexpr int U = 8;
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
-  const uint16_t* xr = x + (size_t)m * K;
-  for (int base = 0; base < K; base += 512) {
-    const int k = base + 8 * lane;
-    float p = 0.0f;
-    if (k < K) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(xr + k);
-      p = (bf16lo(v.x) + bf16hi(v.x)) + (bf16lo(v.y) + bf16hi(v.y)) +
-          (bf16lo(v.z) + bf16hi(v.z)) + (bf16lo(v.w) + bf16hi(v.w));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)m * K, (uint32_t)K * 2u);
+  for (int base = 0; base < K; base += 512 * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld128(rx, (uint32_t)(base + 512 * u + 8 * lane) * 2u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = base + 512 * u + 8 * lane;
+      float p = (bf16lo(v[u].x) + bf16hi(v[u].x)) + (bf16lo(v[u].y) + bf16hi(v[u].y)) +
+                (bf16lo(v[u].z) + bf16hi(v[u].z)) + (bf16lo(v[u].w) + bf16hi(v[u].w));
+      p = row16_sum(p);
+      if ((lane & 15) == 0 && k < K) out[(size_t)(k / kGroup) * ld + m] = -136.0f * p;
     }
-    p += __shfl_xor(p, 8, 16);
-    p += __shfl_xor(p, 4, 16);
-    p += __shfl_xor(p, 2, 16);
-    p += __shfl_xor(p, 1, 16);
-    if ((lane & 15) == 0 && k < K) out[(size_t)(k / kGroup) * ld + m] = -136.0f * p;
   }
 }
 
@@ -320,7 +321,7 @@ static hipError_t launch_tile_t(const TileArgs& a0, int mtiles_bound, int sk, hi
 //   1: 128 x 128, 2 x 2 waves of 64 x 64, weights dequantised into LDS
 //   2: 128 x 256, 8 waves of 128 x 32, LDS-DMA staging, 3 stages (prefill.hip)
 struct TileCfg { int bm, bn; };
-static const TileCfg kTileCfgs[] = {{128, 256}, {128, 128}, {128, 256}, {96, 256}, {112, 256}, {80, 256}};
+static const TileCfg kTileCfgs[] = {{128, 256}, {128, 128}, {128, 256}, {96, 256}, {112, 256}, {80, 256}, {144, 256}};
 int tile_num_cfgs() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0])); }
 int tile_bm(int cfg) { return kTileCfgs[cfg].bm; }
 int tile_bn(int cfg) { return kTileCfgs[cfg].bn; }
@@ -329,7 +330,7 @@ hipError_t launch_tile(const uint16_t* x, const uint8_t* w, const uint16_t* s, c
                        float* ws, const int32_t* m_sizes, int M_total, int N, int K, int G, int ld, int gps,
                        int sk, int cfg, hipStream_t stream) {
   if (cfg < 0 || cfg >= tile_num_cfgs()) return hipErrorInvalidValue;
-  if (cfg >= 2)   // LDS-DMA kernel: 8 (cfg 2), 6 (cfg 3), 7 (cfg 4) or 5 (cfg 5) row tiles of 16
+  if (cfg >= 2)   // LDS-DMA kernel: 8 (cfg 2), 6 (cfg 3), 7 (cfg 4), 5 (cfg 5) or 9 (cfg 6) row tiles of 16
     return launch_prefill(x, w, s, sxn, y, ws, m_sizes, M_total, N, K, G, ld, gps, sk, kTileCfgs[cfg].bm / 16, stream);
   TileArgs a;
   a.x = x; a.w = w; a.s = s; a.sxn = sxn; a.y = y; a.ws = ws; a.m_sizes = m_sizes;

@@ -191,6 +191,14 @@ TILE_CASES = [
     (1322, 512, 2560, 1, 4),
     (111, 129, 512, 0, 4),
     (224, 257, 384, 1, 4),    # exactly two tiles; N * G odd
+    # 6 = 144 x 256 tiles (36 X DMA blocks over 8 waves, 3 x 52.6 KiB stages)
+    (17, 100, 128, 1, 6),
+    (145, 256, 256, 1, 6),    # one row past a 144-row tile
+    (300, 1000, 640, 1, 6),
+    (129, 513, 384, 2, 6),
+    (257, 300, 256, 8, 6),
+    (1322, 512, 2560, 1, 6),
+    (143, 129, 512, 0, 6),
     # 5 = 80 x 256 tiles (20 X DMA blocks over 8 waves)
     (17, 100, 128, 1, 5),
     (81, 256, 256, 1, 5),
@@ -234,6 +242,7 @@ GROUPED_CASES = [
     ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 5),   # 80-row tiles
     ([80, 81, 79, 0, 1], 256, 640, 5),
     ([0, 0, 0, 0, 0, 0, 0, 700], 512, 256, 5),      # all rows in the last group
+    ([144, 145, 143, 0, 1], 256, 640, 6),           # 144-row tiles
 ]
 
 
@@ -277,7 +286,7 @@ def test_prefill_full_size_sampled():
     torch.cuda.synchronize()
     M, N = c.M, c.N
     rng = np.random.default_rng(11)
-    rows, cols = _sample_entries(rng, M, N, 3000, row_edges=(111, 112, 127, 128, 1231, 1232, 1279, 1280, 1321),
+    rows, cols = _sample_entries(rng, M, N, 3000, row_edges=(111, 112, 127, 128, 143, 144, 1231, 1232, 1279, 1280, 1295, 1296, 1321),
                                  col_edges=(255, 256, 19199, 19200, 19455))
     ref = oracle.gemm_entries(c.x, d.p_host, c.s, rows, cols)
     _gate_sampled(y, rows, cols, ref, "prefill 1322x19456x2560 sampled")
