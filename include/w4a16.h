@@ -213,11 +213,10 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  *            dequantised into LDS; 2: 128x256 with LDS-DMA staging, 8
  *            waves, 3 LDS stages; 3, 4, 5, 6: the same with 96x256,
  *            112x256, 80x256 and 144x256 tiles). By default the call picks
- *            among 2 to 6 the
- *            tile height with the fewest rounds of one workgroup per compute
- *            unit times rows per tile, weighted by each height's measured
- *            per-row rate (the grouped call estimates ceil(M_total/h) + G/2
- *            row tiles per column).
+ *            among 2 to 6 the tile height with the fewest rounds of one
+ *            workgroup per compute unit times rows per tile, weighted by
+ *            each height's measured per-row rate (the grouped call
+ *            estimates ceil(M_total/h) + G/2 row tiles per column).
  * An unavailable combination (e.g. path 1 with M != 1, path 2 with M > 16)
  * returns W4A16_ERR_SHAPE.
  */
