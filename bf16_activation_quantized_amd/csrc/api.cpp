@@ -59,14 +59,45 @@ Path auto_path(int64_t M, int64_t K, int32_t sk) {
   return kPathTile;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+// Split-K of the tile path for `tiles` output tiles: the largest power of two
+// (at most 16 and at most the group count) that keeps tiles x SK within one
+// workgroup per compute unit, so the slices run in one round; 1 from M = 1024
+// on (the pages prune split-K at M >= 512; here the one-round rule already
+// stops it wherever the tiles fill the GPU, and at 512 x 8192 x 8192 a split
+// of 2 over 128 tiles is 13 % faster). (Doubling until tiles x SK reaches the
+// compute-unit count overshoots into a second, mostly idle round: at M =
+// 96..384, N x K = 17408 x 5120 that cost 24-52 %.)
+int32_t tile_split(int64_t M, int64_t tiles, int64_t Gk) {
+  int32_t sk = 1;
+  if (M >= 1024) return 1;   // split-K only for small M ("Split-K without atomics")
+  const int64_t cus = device_cus();
+  while (sk < 16 && tiles * sk * 2 <= cus && sk * 2 <= Gk) sk <<= 1;
+  return sk;
+}
+
 int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg, int variant) {
   const int64_t Gk = K / kGroup;
   int32_t sk = 1;
-  if (M >= 512) return 1;   // split-K only for small M ("Split-K without atomics")
+  if (M >= 1024) return 1;   // split-K only for small M ("Split-K without atomics")
   switch (path) {
     case kPathGemv: {
-      sk = pow2_at_least(ceil_div(Gk, 64));           // register budget for x
-      while (sk < 16 && N * sk < 16384 && ceil_div(Gk, sk * 2) >= 1 && sk * 2 <= Gk) sk <<= 1;
+      // only what the register budget for x needs (at most 64 groups per
+      // slice): a split adds the reduce kernel, and over N x K from 1024 x
+      // 8192 to 28672 x 8192 one slice was fastest wherever it fits
+      sk = pow2_at_least(ceil_div(Gk, 64));
       break;
     }
     case kPathSkinny: {
@@ -86,7 +117,7 @@ int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg, int
     }
     case kPathTile: {
       const int64_t tiles = ceil_div(M, w4a16::tile_bm(tile_cfg)) * ceil_div(N, w4a16::tile_bn(tile_cfg));
-      while (sk < 16 && tiles * sk < 256 && sk * 2 <= Gk) sk <<= 1;
+      sk = tile_split(M, tiles, Gk);
       break;
     }
     default:
@@ -106,38 +137,30 @@ struct Plan {
 };
 
 // Tile configuration 2 (LDS-DMA staging, 8 waves of 128 x 32, tile.hip).
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cache[dev] = v;
-  }
-  return cache[dev];
-}
 
 // Grouped launches: the grid holds ceil(M_total / BM) + G row tiles per column
 // tile (group boundaries split tiles). Shorter tiles (96 rows, configuration
 // 3) when that whole grid still fits one wave of workgroups over the compute
 // units: each tile then finishes sooner and no tile waits for a second round.
-// Tile height of the LDS-DMA kernel for `tiles(bm)` output tiles on the
-// device's compute units (one workgroup per unit): the fewest rounds x rows
-// per tile, each height weighted by its measured per-row rate relative to
-// the 128-row tile (shorter tiles amortise the per-group dequantisation and
-// barrier over fewer rows; at 1322 x 19456 on one box: 4 rounds of 128 rows
-// 166 us, 4 of 112 rows 161 us, 3 of 144 rows 146 us, 5 of 96 rows 176 us).
-template <class F>
-int pick_tile_cfg(F tiles) {
+// Tile height of the LDS-DMA kernel (and, with automatic split-K, the split):
+// one workgroup per compute unit, so the time is the rounds of tiles x slices
+// times one unit's time, taken proportional to its rows x groups and divided
+// by each height's measured per-row rate relative to the 128-row tile
+// (shorter tiles amortise the per-group dequantisation and barrier over fewer
+// rows; at 1322 x 19456 x 2560 on one box: 4 rounds of 128 rows 166 us, 4 of
+// 112 rows 161 us, 3 of 144 rows 146 us, 5 of 96 rows 176 us). `tiles(bm)`
+// counts the output tiles, `split(tiles)` gives the split for a tile count.
+template <class T, class S>
+int pick_tile_cfg(int64_t Gk, T tiles, S split) {
   struct Cand { int cfg, bm; double rate; };
   static const Cand cands[] = {{2, 128, 1.0}, {6, 144, 0.96}, {4, 112, 0.91}, {3, 96, 0.907}, {5, 80, 0.85}};
   const int64_t cus = device_cus();
   int best = 2;
   double best_cost = 0.0;
   for (const Cand& c : cands) {
-    const double cost = (double)ceil_div(tiles(c.bm), cus) * c.bm / c.rate;
+    const int64_t t = tiles(c.bm);
+    const int64_t sk = std::max<int64_t>(1, split(t));
+    const double cost = (double)ceil_div(t * sk, cus) * c.bm / c.rate * (double)ceil_div(Gk, sk);
     if (best_cost == 0.0 || cost < best_cost * (1.0 - 1e-9)) {
       best = c.cfg;
       best_cost = cost;
@@ -146,17 +169,22 @@ int pick_tile_cfg(F tiles) {
   return best;
 }
 
-int default_tile_cfg(int64_t M, int64_t N) {
-  const int64_t nt = ceil_div(N, 256);
-  return pick_tile_cfg([&](int bm) { return ceil_div(std::max<int64_t>(M, 1), bm) * nt; });
+// split_k = 0: automatic, chosen with the height (tile_split); otherwise fixed
+int default_tile_cfg(int64_t M, int64_t N, int64_t K, int32_t split_k) {
+  const int64_t nt = ceil_div(N, 256), Gk = K / kGroup;
+  return pick_tile_cfg(
+      Gk, [&](int bm) { return ceil_div(std::max<int64_t>(M, 1), bm) * nt; },
+      [&](int64_t t) { return split_k > 0 ? (int64_t)split_k : (int64_t)tile_split(M, t, Gk); });
 }
 
-// grouped: M_sizes stays on the device, so the tile count is estimated as
-// ceil(M_total / bm) + G / 2 per column (each group's partial last tile
-// adds half a tile on average; the kernel maps only the real tiles)
-int default_grouped_tile_cfg(int64_t G, int64_t M_total, int64_t N) {
+// grouped (no split-K): M_sizes stays on the device, so the tile count is
+// estimated as ceil(M_total / bm) + G / 2 per column (each group's partial
+// last tile adds half a tile on average; the kernel maps only the real tiles)
+int default_grouped_tile_cfg(int64_t G, int64_t M_total, int64_t N, int64_t K) {
   const int64_t nt = ceil_div(N, 256);
-  return pick_tile_cfg([&](int bm) { return (ceil_div(std::max<int64_t>(M_total, 1), bm) + G / 2) * nt; });
+  return pick_tile_cfg(
+      K / kGroup, [&](int bm) { return (ceil_div(std::max<int64_t>(M_total, 1), bm) + G / 2) * nt; },
+      [](int64_t) { return (int64_t)1; });
 }
 
 w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg, Plan* p) {
@@ -172,7 +200,7 @@ w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w
   if (path == kPathSkinny && M > 16) return W4A16_ERR_SHAPE;
   int tile_cfg = 0;
   if (path == kPathTile) {
-    tile_cfg = variant >= 0 ? variant : default_tile_cfg(M, N);
+    tile_cfg = variant >= 0 ? variant : default_tile_cfg(M, N, K, split_k);
     if (tile_cfg >= w4a16::tile_num_cfgs()) return W4A16_ERR_SHAPE;
   }
   int32_t sk = split_k > 0 ? split_k : auto_split(path, M, N, K, tile_cfg, variant);
@@ -346,7 +374,7 @@ w4a16_status w4a16_gemm_grouped_ex(const uint16_t* x, const uint8_t* w_packed, c
     return W4A16_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_packed) || !aligned16(scales) || !aligned16(y)) return W4A16_ERR_ALIGN;
   if (((uintptr_t)m_sizes & 3u) != 0) return W4A16_ERR_ALIGN;
-  int tile_cfg = default_grouped_tile_cfg(G, M_total, N);
+  int tile_cfg = default_grouped_tile_cfg(G, M_total, N, K);
   if (cfg != nullptr) {
     if (cfg->path != 0 && cfg->path != kPathTile) return W4A16_ERR_SHAPE;
     if (cfg->variant >= 0) tile_cfg = cfg->variant;

@@ -78,10 +78,13 @@ w4a16_status w4a16_pack_int4(const uint8_t* q, uint8_t* w_packed,
 
 /*
  * The split-K factor the library uses for w4a16_gemm when split_k == 0
- * (auto) at this shape: 1 for M >= 512 (split-K is restricted to small M,
- * "Split-K without atomics", on the MI350X Triton page), otherwise a factor
- * chosen from the shape so that the decode kernels fill the GPU. Returns 0 on
- * invalid dimensions.
+ * (auto) at this shape: 1 for M >= 1024 (split-K is restricted to small M,
+ * "Split-K without atomics", on the MI350X Triton page); below that, for the
+ * M = 1 GEMV only what its register budget for x needs (at most 64 groups per
+ * slice), for the M <= 16 kernel enough slices for one workgroup per compute
+ * unit, and for the tile kernel the largest power of two (at most 16) that
+ * keeps tiles x SK within one workgroup per compute unit, chosen together
+ * with the tile height. Returns 0 on invalid dimensions.
  */
 int32_t w4a16_gemm_auto_split_k(int64_t M, int64_t N, int64_t K);
 

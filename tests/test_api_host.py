@@ -124,9 +124,18 @@ def test_explicit_path_errors():
 
 
 def test_auto_split_rule():
-    # split-K is used only below M = 512 ("Split-K without atomics")
-    for M in (512, 1322, 4096):
+    # split-K is used only below M = 1024 ("Split-K without atomics" prunes
+    # at 512; the tile kernel's one-round rule stops it earlier on wide N)
+    for M in (1024, 1322, 4096):
         assert w4.w4a16_gemm_auto_split_k(M, 64, 8192) == 1
+    # the tile kernel: tiles x SK stay within one workgroup per compute unit
+    # (256 on the host without a device): 1322 x 19456 has 760+ tiles
+    assert w4.w4a16_gemm_auto_split_k(1322, 19456, 2560) == 1
+    assert w4.w4a16_gemm_auto_split_k(128, 17408, 5120) == 2     # 68 tiles of 128 x 256
+    # the decode GEMV splits only for its register budget (<= 64 groups per slice)
+    assert w4.w4a16_gemm_auto_split_k(1, 17408, 5120) == 1
+    assert w4.w4a16_gemm_auto_split_k(1, 256, 512) == 1
+    assert w4.w4a16_gemm_auto_split_k(1, 8192, 16384) == 2
     for M in (1, 2, 16, 100):
         sk = w4.w4a16_gemm_auto_split_k(M, 256, 8192)
         assert sk in (1, 2, 4, 8, 16)
