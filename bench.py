@@ -187,6 +187,61 @@ def bench_pack(steps, warmup):
     return dict(rows=N, K=K, us_per_step=t * 1e6, gbs=(N * K * 1.5) / t / 1e9)
 
 
+def bench_dispatch(N, K, Ms, steps=20):
+    """Path / tile height / split-K selection over M at one N x K: the
+    automatic choice (split_k=0, no path) against every explicit one, each
+    graph-timed over `steps` calls with rotated weight copies. One JSON line
+    per M: auto time, the best explicit (name, SK, time) and their ratio."""
+    import torch
+    import bf16_activation_quantized_amd as w4
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    q = torch.randint(0, 16, (N, K), dtype=torch.uint8, device="cuda", generator=g)
+    w = w4.w4a16_pack_int4(q)
+    del q
+    s = (torch.rand(N, K // 128, device="cuda", generator=g) * 0.015 + 0.005).to(torch.bfloat16)
+    wb = eff_weight_bytes(N, K)
+    copies = max(1, math.ceil(ROTATE_BYTES / wb))
+    ws_ = [w] + [w.clone() for _ in range(copies - 1)]
+    ss_ = [s] + [s.clone() for _ in range(copies - 1)]
+    out = []
+    for M in Ms:
+        x = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        cands = [("auto", None, None, 0)]
+        if M == 1:
+            cands += [("gemv", w4.PATH_GEMV, None, sk) for sk in (1, 2, 4)]
+        if M <= 16:
+            cands += [("small-batch", w4.PATH_SKINNY, None, sk) for sk in (1, 2, 4, 8)]
+        if M > 1:
+            for cfg in (2, 3, 4, 5, 6):
+                for sk in ((1, 2, 4, 8) if M < 1024 else (1, 2)):
+                    cands.append((f"tile{cfg}", w4.PATH_TILE, cfg, sk))
+        res = []
+        for name, path, var, sk in cands:
+            need = w4.w4a16_gemm_workspace_bytes(M, N, K, sk, path=path, variant=var)
+            wsp = torch.empty(max(need // 4, 1) + 4, dtype=torch.float32, device="cuda")
+
+            def step(i, path=path, var=var, sk=sk, wsp=wsp):
+                w4.w4a16_gemm(x, ws_[i % copies], ss_[i % copies], y=y, split_k=sk, workspace=wsp,
+                              path=path, variant=var)
+            try:
+                _, t = time_steps(step, steps, 3)
+                res.append((t * 1e6, name, sk))
+            except RuntimeError as e:   # a combination the library refuses
+                log(f"dispatch M={M} {name} sk={sk}: {e}")
+            del wsp
+        auto = res[0]
+        best = min(res[1:] or res)
+        r = dict(N=N, K=K, M=M, auto_us=round(auto[0], 2), best=[best[1], best[2], round(best[0], 2)],
+                 auto_vs_best=round(auto[0] / best[0], 3), auto_sk=w4.w4a16_gemm_auto_split_k(M, N, K),
+                 auto_tflops=round(2.0 * M * N * K / auto[0] / 1e6, 1), auto_gbs=round(wb / auto[0] / 1e3, 1))
+        print(json.dumps(r), flush=True)
+        out.append(r)
+        del x, y
+    return out
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle (unpack + dequant + fp64 GEMV) on the decode workload, timed
     on the host cores."""
@@ -235,13 +290,16 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default=None,
-                    choices=["decode_gemv", "decode_splitk", "prefill", "grouped", "pack", "tiny"],
+                    choices=["decode_gemv", "decode_splitk", "prefill", "grouped", "pack", "tiny", "dispatch"],
                     help="measure one workload only and print its record (for profiling)")
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--variant", type=int, default=None)
     ap.add_argument("--path", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
+    ap.add_argument("--shape", default="17408,5120", help="N,K of --only dispatch")
+    ap.add_argument("--ms", default="1,2,16,32,64,96,128,192,256,384,512,1024,2048",
+                    help="M values of --only dispatch")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -257,6 +315,10 @@ def main():
         sys.exit(1)
     w4._lib()   # fails loudly if the HIP library is not built
 
+    if args.only == "dispatch":
+        N, K = (int(v) for v in args.shape.split(","))
+        bench_dispatch(N, K, [int(v) for v in args.ms.split(",")])
+        return
     if args.only:
         if args.only in ("decode_gemv", "decode_splitk", "tiny"):
             r, _, _ = bench_decode(args.only, args.steps, args.warmup, args.split_k, args.path, args.variant)
