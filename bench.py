@@ -172,6 +172,28 @@ def bench_grouped(name, steps, warmup, variant=None):
                 tflops=flops / t / 1e12, frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS), d, y
 
 
+def bench_batched(name, steps, warmup, variant=None, split_k=0):
+    import torch
+    import bf16_activation_quantized_amd as w4
+    from synth import make_config, CONFIGS
+    cfg = CONFIGS[name]
+    B, M, N, K = cfg["B"], cfg["M"], cfg["N"], cfg["K"]
+    c = make_config(name)
+    d = Dev(c, 1)
+    x = d.x.view(B, M, K)
+    y = torch.empty((B, M, N), dtype=torch.bfloat16, device="cuda")
+    need = w4.w4a16_gemm_batched_workspace_bytes(B, M, N, K, split_k, variant)
+    ws = torch.empty(max(need // 4, 1) + 4, dtype=torch.float32, device="cuda")
+
+    def step(i):
+        w4.w4a16_gemm_batched(x, d.w[0], d.s[0], y=y, split_k=split_k, workspace=ws, variant=variant)
+
+    total, t = time_steps(step, steps, warmup)
+    flops = 2.0 * B * M * N * K
+    return dict(B=B, M=M, N=N, K=K, us_per_step=t * 1e6,
+                tflops=flops / t / 1e12, frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS), d, y
+
+
 def bench_pack(steps, warmup):
     import torch
     import bf16_activation_quantized_amd as w4
@@ -290,7 +312,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default=None,
-                    choices=["decode_gemv", "decode_splitk", "prefill", "grouped", "pack", "tiny", "dispatch"],
+                    choices=["decode_gemv", "decode_splitk", "prefill", "grouped", "batched", "pack", "tiny",
+                             "dispatch"],
                     help="measure one workload only and print its record (for profiling)")
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--variant", type=int, default=None)
@@ -326,6 +349,8 @@ def main():
             r, _, _ = bench_prefill("prefill", args.steps, args.warmup, args.variant)
         elif args.only == "grouped":
             r, _, _ = bench_grouped("grouped", args.steps, args.warmup, args.variant)
+        elif args.only == "batched":
+            r, _, _ = bench_batched("batched", args.steps, args.warmup, args.variant, args.split_k)
         else:
             r = bench_pack(args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **r}), flush=True)
@@ -361,6 +386,8 @@ def main():
         workloads["prefill"], _, _ = bench_prefill("prefill", steps2, args.warmup)
         log("bench: grouped")
         workloads["grouped"], _, _ = bench_grouped("grouped", steps2, args.warmup)
+        log("bench: batched")
+        workloads["batched"], _, _ = bench_batched("batched", steps2, args.warmup)
         log("bench: pack")
         workloads["pack_int4"] = bench_pack(steps2, args.warmup)
         torch.cuda.empty_cache()

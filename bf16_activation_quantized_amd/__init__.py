@@ -63,6 +63,10 @@ def _lib():
         "w4a16_gemm_grouped": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I64, I32, P, SZ, P]),
         "w4a16_gemm_grouped_ex": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I64, I32, P, SZ, P, P]),
         "w4a16_splitk_reduce": (ctypes.c_int, [P, P, I32, I64, I64, P]),
+        "w4a16_gemm_batched_workspace_bytes": (SZ, [I32, I64, I64, I64, I32]),
+        "w4a16_gemm_batched_workspace_bytes_ex": (SZ, [I32, I64, I64, I64, I32, P]),
+        "w4a16_gemm_batched": (ctypes.c_int, [P, P, P, P, I32, I64, I64, I64, I32, I32, P, SZ, P]),
+        "w4a16_gemm_batched_ex": (ctypes.c_int, [P, P, P, P, I32, I64, I64, I64, I32, I32, P, SZ, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -213,6 +217,44 @@ def w4a16_gemm_grouped(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Te
         st = L.w4a16_gemm_grouped_ex(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(m_sizes), _ptr(y), G, M_total, N,
                                      K, GROUP_SIZE, _ptr(workspace), wbytes, _stream(stream), cfg)
     _raise(st, "w4a16_gemm_grouped")
+    return y
+
+
+def w4a16_gemm_batched_workspace_bytes(B: int, M: int, N: int, K: int, split_k: int = 0,
+                                       variant: Optional[int] = None) -> int:
+    L = _lib()
+    if variant is None:
+        return int(L.w4a16_gemm_batched_workspace_bytes(B, M, N, K, split_k))
+    return int(L.w4a16_gemm_batched_workspace_bytes_ex(B, M, N, K, split_k, _cfg(PATH_TILE, variant)))
+
+
+def w4a16_gemm_batched(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
+                       y: Optional[torch.Tensor] = None, split_k: int = 0,
+                       workspace: Optional[torch.Tensor] = None, variant: Optional[int] = None,
+                       stream=None) -> torch.Tensor:
+    """Y[b] = X[b] . dequant(W[b])^T for B independent problems, one launch."""
+    _check(x, "x", torch.bfloat16)
+    B, M, K = x.shape
+    N = w_packed.shape[1]
+    _check(w_packed, "w_packed", torch.uint8, (B, N, K // 2))
+    _check(scales, "scales", torch.bfloat16, (B, N, K // GROUP_SIZE))
+    if y is None:
+        y = torch.empty((B, M, N), dtype=torch.bfloat16, device=x.device)
+    _check(y, "y", torch.bfloat16, (B, M, N))
+    need = w4a16_gemm_batched_workspace_bytes(B, M, N, K, split_k, variant)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4 + 1, dtype=torch.float32, device=x.device)
+    if workspace is not None:
+        _check(workspace, "workspace", torch.float32)
+    wbytes = 0 if workspace is None else workspace.numel() * 4
+    L = _lib()
+    if variant is None:
+        st = L.w4a16_gemm_batched(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(y), B, M, N, K, GROUP_SIZE, split_k,
+                                  _ptr(workspace), wbytes, _stream(stream))
+    else:
+        st = L.w4a16_gemm_batched_ex(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(y), B, M, N, K, GROUP_SIZE,
+                                     split_k, _ptr(workspace), wbytes, _stream(stream), _cfg(PATH_TILE, variant))
+    _raise(st, "w4a16_gemm_batched")
     return y
 
 

@@ -187,6 +187,43 @@ int default_grouped_tile_cfg(int64_t G, int64_t M_total, int64_t N, int64_t K) {
       [](int64_t) { return (int64_t)1; });
 }
 
+// Batched: B problems of M rows on the tile kernel (weight group b = problem
+// b, its M rows at b * M), tile height and split-K as for one problem of B x
+// ceil(M / h) row tiles per column.
+struct BatchedPlan {
+  int cfg;
+  int32_t sk, gps;
+  uint64_t ws_split, ws_sx;
+  int64_t ld;
+};
+
+w4a16_status make_batched_plan(int32_t B, int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg,
+                               BatchedPlan* p) {
+  const int64_t Gk = K / kGroup, nt = ceil_div(N, 256), Mt = (int64_t)B * M;
+  int tile_cfg = -1;
+  if (cfg != nullptr) {
+    if (cfg->path != 0 && cfg->path != kPathTile) return W4A16_ERR_SHAPE;
+    tile_cfg = cfg->variant;
+  }
+  if (tile_cfg < 0)
+    tile_cfg = pick_tile_cfg(
+        Gk, [&](int bm) { return (int64_t)B * ceil_div(M, bm) * nt; },
+        [&](int64_t t) { return split_k > 0 ? (int64_t)split_k : (int64_t)tile_split(M, t, Gk); });
+  if (tile_cfg >= w4a16::tile_num_cfgs()) return W4A16_ERR_SHAPE;
+  const int64_t tiles =
+      (int64_t)B * ceil_div(M, w4a16::tile_bm(tile_cfg)) * ceil_div(N, w4a16::tile_bn(tile_cfg));
+  int32_t sk = split_k > 0 ? split_k : tile_split(M, tiles, Gk);
+  if (sk > Gk && split_k == 0) sk = 1;
+  p->cfg = tile_cfg;
+  p->sk = sk;
+  p->gps = (int32_t)ceil_div(Gk, sk);
+  p->ws_split = sk > 1 ? (uint64_t)sk * (uint64_t)Mt * (uint64_t)N * 4u : 0u;
+  p->ld = (int64_t)round_up((uint64_t)Mt, 4);
+  p->ws_sx = (uint64_t)Gk * (uint64_t)p->ld * 4u;
+  return W4A16_OK;
+}
+
+
 w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg, Plan* p) {
   const int64_t Gk = K / kGroup;
   Path path = auto_path(M, K, split_k);
@@ -228,6 +265,16 @@ w4a16_status check_dims(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if ((uint64_t)N * (uint64_t)K / 2u > kMaxBytes) return W4A16_ERR_SHAPE;
   if ((uint64_t)M * (uint64_t)K * 2u > kMaxBytes) return W4A16_ERR_SHAPE;
   if ((uint64_t)M * (uint64_t)N * 4u > kMaxBytes) return W4A16_ERR_SHAPE;
+  return W4A16_OK;
+}
+
+w4a16_status check_batched(int32_t B, int64_t M, int64_t N, int64_t K, int32_t group_size) {
+  if (B < 1 || M < 0) return W4A16_ERR_SHAPE;
+  if ((uint64_t)B * (uint64_t)M > (uint64_t)kMaxDim) return W4A16_ERR_SHAPE;
+  w4a16_status st = check_dims((int64_t)B * M, N, K, group_size);
+  if (st != W4A16_OK) return st;
+  // one buffer resource covers the scales of all problems
+  if ((uint64_t)B * (uint64_t)N * (uint64_t)(K / kGroup) * 2u > kMaxBytes) return W4A16_ERR_SHAPE;
   return W4A16_OK;
 }
 
@@ -280,7 +327,7 @@ w4a16_status run_gemm(const uint16_t* x, const uint8_t* w, const uint16_t* s, ui
     case kPathTile: {
       e = w4a16::launch_rowsum_neg136(x, ws_sx, iM, iK, (int)p.ld, strm);
       if (e == hipSuccess)
-        e = w4a16::launch_tile(x, w, s, ws_sx, y, ws_split, nullptr, iM, iN, iK, 1, (int)p.ld, p.gps, p.sk,
+        e = w4a16::launch_tile(x, w, s, ws_sx, y, ws_split, nullptr, 0, iM, iN, iK, 1, (int)p.ld, p.gps, p.sk,
                                p.variant, strm);
       break;
     }
@@ -389,8 +436,57 @@ w4a16_status w4a16_gemm_grouped_ex(const uint16_t* x, const uint8_t* w_packed, c
   const int Gk = (int)(K / kGroup);
   hipError_t e = w4a16::launch_rowsum_neg136(x, workspace, (int)M_total, (int)K, ld, strm);
   if (e != hipSuccess) return W4A16_ERR_LAUNCH;
-  return launched(w4a16::launch_tile(x, w_packed, scales, workspace, y, nullptr, m_sizes, (int)M_total, (int)N,
+  return launched(w4a16::launch_tile(x, w_packed, scales, workspace, y, nullptr, m_sizes, 0, (int)M_total, (int)N,
                                      (int)K, G, ld, Gk, 1, tile_cfg, strm));
+}
+
+size_t w4a16_gemm_batched_workspace_bytes_ex(int32_t B, int64_t M, int64_t N, int64_t K, int32_t split_k,
+                                             const w4a16_config* cfg) {
+  if (!valid_split(split_k) || check_batched(B, M, N, K, 128) != W4A16_OK || M == 0) return 0;
+  BatchedPlan p;
+  if (make_batched_plan(B, M, N, K, split_k, cfg, &p) != W4A16_OK) return 0;
+  return (size_t)(round_up(p.ws_split, 256) + p.ws_sx);
+}
+
+size_t w4a16_gemm_batched_workspace_bytes(int32_t B, int64_t M, int64_t N, int64_t K, int32_t split_k) {
+  return w4a16_gemm_batched_workspace_bytes_ex(B, M, N, K, split_k, nullptr);
+}
+
+w4a16_status w4a16_gemm_batched_ex(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales, uint16_t* y,
+                                   int32_t B, int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t split_k,
+                                   float* workspace, size_t workspace_bytes, void* stream, const w4a16_config* cfg) {
+  if (!valid_split(split_k)) return W4A16_ERR_SPLIT_K;
+  w4a16_status st = check_batched(B, M, N, K, group_size);
+  if (st != W4A16_OK) return st;
+  if (M == 0) return W4A16_OK;   // empty problems: nothing to read or write
+  if (x == nullptr || w_packed == nullptr || scales == nullptr || y == nullptr) return W4A16_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_packed) || !aligned16(scales) || !aligned16(y)) return W4A16_ERR_ALIGN;
+  BatchedPlan p;
+  st = make_batched_plan(B, M, N, K, split_k, cfg, &p);
+  if (st != W4A16_OK) return st;
+  if (p.ws_split > kMaxBytes) return W4A16_ERR_SHAPE;
+  const uint64_t need = round_up(p.ws_split, 256) + p.ws_sx;
+  if (workspace == nullptr) return W4A16_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
+  if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  float* ws_split = p.sk > 1 ? workspace : nullptr;
+  float* ws_sx = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + round_up(p.ws_split, 256));
+  const int Mt = (int)((int64_t)B * M);
+  hipError_t e = w4a16::launch_rowsum_neg136(x, ws_sx, Mt, (int)K, (int)p.ld, strm);
+  if (e != hipSuccess) return W4A16_ERR_LAUNCH;
+  e = w4a16::launch_tile(x, w_packed, scales, ws_sx, y, ws_split, nullptr, (int)M, Mt, (int)N, (int)K, B, (int)p.ld,
+                         p.gps, p.sk, p.cfg, strm);
+  if (e != hipSuccess) return W4A16_ERR_LAUNCH;
+  if (p.sk > 1) return launched(w4a16::launch_splitk_reduce(ws_split, y, (uint64_t)Mt * (uint64_t)N, p.sk, strm));
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_gemm_batched(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales, uint16_t* y,
+                                int32_t B, int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t split_k,
+                                float* workspace, size_t workspace_bytes, void* stream) {
+  return w4a16_gemm_batched_ex(x, w_packed, scales, y, B, M, N, K, group_size, split_k, workspace, workspace_bytes,
+                               stream, nullptr);
 }
 
 w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y, int32_t split_k, int64_t M, int64_t N,

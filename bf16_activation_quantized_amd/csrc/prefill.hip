@@ -61,6 +61,7 @@ struct PrefillArgs {
   uint16_t* y;             // [M_total, N]
   float* ws;               // [SK, M_total, N] fp32 split-K partials, or nullptr
   const int32_t* m_sizes;  // [G] on device, or nullptr
+  int m_uniform;           // batched: rows per weight group (M_sizes not used), else 0
   int M_total, N, K, G, ld;
   int gps;                 // 128-groups per split-K slice
   int mtiles, ntiles;
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     if ((int)blockIdx.x >= nblocks) return;
   }
   tile_coords(blockIdx.x, nblocks, MT, args.ntiles, &mt, &nt);
-  const TileRows tr = tile_rows(mt, BM, args.M_total, args.m_sizes, args.G);
+  const TileRows tr = tile_rows(mt, BM, args.M_total, args.m_sizes, args.G, args.m_uniform);
   if (tr.rows <= 0) return;
   const int row0 = tr.row0, rows = tr.rows;
   const int n0 = nt * kPN;
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   // scales: the whole tensor (word-aligned reads, see make_scale_rsrc); columns
   // past N read other scales or zeros and are never stored
   const __amdgpu_buffer_rsrc_t rs =
-      make_scale_rsrc(args.s, (uint32_t)((size_t)(args.m_sizes != nullptr ? args.G : 1) * args.N * Gk));
+      make_scale_rsrc(args.s, (uint32_t)((size_t)args.G * args.N * Gk));
   const __amdgpu_buffer_rsrc_t rsx =
       make_rsrc(args.sxn + row0, (uint32_t)(((size_t)Gk * args.ld - row0) * 4u));
   const int slice = blockIdx.y;
@@ -337,7 +338,8 @@ static hipError_t launch_prefill_t(PrefillArgs a, int sk, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  a.mtiles = (a.M_total + BM - 1) / BM + (a.m_sizes != nullptr ? a.G : 0);
+  a.mtiles = a.m_uniform > 0 ? a.G * ((a.m_uniform + BM - 1) / BM)
+                             : (a.M_total + BM - 1) / BM + (a.m_sizes != nullptr ? a.G : 0);
   a.ntiles = (a.N + kPN - 1) / kPN;
   const long long blocks = (long long)a.mtiles * a.ntiles;
   if (blocks <= 0) return hipSuccess;
@@ -347,10 +349,10 @@ static hipError_t launch_prefill_t(PrefillArgs a, int sk, hipStream_t stream) {
 }
 
 hipError_t launch_prefill(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
-                          float* ws, const int32_t* m_sizes, int M_total, int N, int K, int G, int ld, int gps,
-                          int sk, int row_tiles, hipStream_t stream) {
+                          float* ws, const int32_t* m_sizes, int m_uniform, int M_total, int N, int K, int G,
+                          int ld, int gps, int sk, int row_tiles, hipStream_t stream) {
   PrefillArgs a;
-  a.x = x; a.w = w; a.s = s; a.sxn = sxn; a.y = y; a.ws = ws; a.m_sizes = m_sizes;
+  a.x = x; a.w = w; a.s = s; a.sxn = sxn; a.y = y; a.ws = ws; a.m_sizes = m_sizes; a.m_uniform = m_uniform;
   a.M_total = M_total; a.N = N; a.K = K; a.G = G; a.ld = ld; a.gps = gps;
   a.mtiles = 0; a.ntiles = 0;
   switch (row_tiles) {

@@ -68,6 +68,7 @@ struct TileArgs {
   uint16_t* y;            // [M_total, N]
   float* ws;              // [SK, M_total, N] fp32 split-K partials, or nullptr
   const int32_t* m_sizes; // [G] on device, or nullptr for one group of M_total rows
+  int m_uniform;          // batched: rows per weight group (M_sizes not used), else 0
   int M_total, N, K, G, ld;
   int gps;                // 128-groups per split-K slice (gridDim.y slices)
   int mtiles;             // linear M-tiles covered by the grid
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tile_kernel(const TileArgs args)
     if ((int)blockIdx.x >= nblocks) return;
   }
   tile_coords(blockIdx.x, nblocks, MT, args.ntiles, &mt_lin, &nt);
-  const TileRows tr = tile_rows(mt_lin, BM, args.M_total, args.m_sizes, args.G);
+  const TileRows tr = tile_rows(mt_lin, BM, args.M_total, args.m_sizes, args.G, args.m_uniform);
   const int wg = tr.wg, row0 = tr.row0, rows = tr.rows;
   if (rows <= 0) return;
   const int n0 = nt * BN;
@@ -327,17 +328,19 @@ int tile_bm(int cfg) { return kTileCfgs[cfg].bm; }
 int tile_bn(int cfg) { return kTileCfgs[cfg].bn; }
 
 hipError_t launch_tile(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
-                       float* ws, const int32_t* m_sizes, int M_total, int N, int K, int G, int ld, int gps,
-                       int sk, int cfg, hipStream_t stream) {
+                       float* ws, const int32_t* m_sizes, int m_uniform, int M_total, int N, int K, int G, int ld,
+                       int gps, int sk, int cfg, hipStream_t stream) {
   if (cfg < 0 || cfg >= tile_num_cfgs()) return hipErrorInvalidValue;
   if (cfg >= 2)   // LDS-DMA kernel: 8 (cfg 2), 6 (cfg 3), 7 (cfg 4), 5 (cfg 5) or 9 (cfg 6) row tiles of 16
-    return launch_prefill(x, w, s, sxn, y, ws, m_sizes, M_total, N, K, G, ld, gps, sk, kTileCfgs[cfg].bm / 16, stream);
+    return launch_prefill(x, w, s, sxn, y, ws, m_sizes, m_uniform, M_total, N, K, G, ld, gps, sk,
+                          kTileCfgs[cfg].bm / 16, stream);
   TileArgs a;
-  a.x = x; a.w = w; a.s = s; a.sxn = sxn; a.y = y; a.ws = ws; a.m_sizes = m_sizes;
+  a.x = x; a.w = w; a.s = s; a.sxn = sxn; a.y = y; a.ws = ws; a.m_sizes = m_sizes; a.m_uniform = m_uniform;
   a.M_total = M_total; a.N = N; a.K = K; a.G = G; a.ld = ld; a.gps = gps;
   a.mtiles = 0; a.ntiles = 0;
   const int bm = tile_bm(cfg);
-  const int mt = (M_total + bm - 1) / bm + (m_sizes != nullptr ? G : 0);
+  const int mt = m_uniform > 0 ? G * ((m_uniform + bm - 1) / bm)
+                               : (M_total + bm - 1) / bm + (m_sizes != nullptr ? G : 0);
   switch (cfg) {
     case 0: return launch_tile_t<128, 256, 2, 4>(a, mt, sk, stream);
     case 1: return launch_tile_t<128, 128, 2, 2>(a, mt, sk, stream);

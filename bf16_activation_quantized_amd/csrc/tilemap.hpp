@@ -29,8 +29,19 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int MT, int NT
 struct TileRows {
   int wg, row0, rows;
 };
-__device__ __forceinline__ TileRows tile_rows(int mt, int BM, int M_total, const int32_t* m_sizes, int G) {
+// Batched (m_uniform > 0, no M_sizes): G weight groups of m_uniform rows
+// each, ceil(m_uniform / BM) m-tiles per group, all computed from the tile id.
+__device__ __forceinline__ TileRows tile_rows(int mt, int BM, int M_total, const int32_t* m_sizes, int G,
+                                              int m_uniform) {
   TileRows t{0, mt * BM, min(BM, M_total - mt * BM)};
+  if (m_uniform > 0) {
+    const int tpg = (m_uniform + BM - 1) / BM;
+    const int g = mt / tpg, r = (mt - g * tpg) * BM;
+    t.wg = g;
+    t.row0 = g * m_uniform + r;
+    t.rows = g < G ? min(BM, m_uniform - r) : 0;
+    return t;
+  }
   if (m_sizes == nullptr) return t;
   int cnt = 0, start = 0;
   bool found = false;

@@ -167,6 +167,44 @@ w4a16_status w4a16_gemm_grouped(const uint16_t* x, const uint8_t* w_packed,
                                 void* stream);
 
 /*
+ * Bytes of workspace w4a16_gemm_batched needs at this shape and split_k (0 =
+ * auto): SK * B * M * N * 4 (rounded up to 256) when the effective split
+ * factor SK > 1, plus (K/128) * round_up(B * M, 4) * 4 for the per-row group
+ * sums of X. Returns 0 for invalid arguments or M == 0.
+ */
+size_t w4a16_gemm_batched_workspace_bytes(int32_t B, int64_t M, int64_t N, int64_t K,
+                                          int32_t split_k);
+
+/*
+ * Batched GEMM ("Add Triton BF16xINT4 rowwise GEMM for ROCm gfx942/gfx950",
+ * Summary: the batched op beside the plain and grouped ones): B independent
+ * problems of the same shape, Y[b] = X[b] . dequant(W[b])^T, in one launch
+ * of the tile kernel with split-K ("Split-K without atomics").
+ *   x         : [B, M, K] bf16, device
+ *   w_packed  : [B, N, K/2] uint8, device
+ *   scales    : [B, N, K/group_size] bf16, device
+ *   y         : [B, M, N] bf16, device, written
+ *   B >= 1, M >= 0 (0: W4A16_OK, nothing enqueued), B * M < 2^31, N >= 1,
+ *   K >= 128, group_size == 128, K % 128 == 0; the scales of all B problems
+ *   together must be smaller than 2^32 bytes.
+ *   split_k   : 0 (auto: the tile height and split chosen together, as for
+ *               w4a16_gemm with B x ceil(M/h) row tiles per column) or 1, 2,
+ *               4, 8, 16.
+ *   workspace : fp32 device scratch of workspace_bytes >= the value of
+ *               w4a16_gemm_batched_workspace_bytes; overwritten.
+ * Enqueues the per-row group sums of X, the tile kernel (weight group b =
+ * problem b, its rows at b * M), and for SK > 1 the split-K reduce. Every
+ * row of Y is written exactly once, no atomics: bitwise reproducible for a
+ * given shape and split_k.
+ */
+w4a16_status w4a16_gemm_batched(const uint16_t* x, const uint8_t* w_packed,
+                                const uint16_t* scales, uint16_t* y,
+                                int32_t B, int64_t M, int64_t N, int64_t K,
+                                int32_t group_size, int32_t split_k,
+                                float* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * The reduce step of split-K on its own ("Split-K without atomics"):
  *   y[m, n] = bf16_rne( ((ws[0,m,n] + ws[1,m,n]) + ws[2,m,n]) + ... )
  * summed in fp32 in slice order s = 0..SK-1.
@@ -245,6 +283,18 @@ w4a16_status w4a16_gemm_grouped_ex(const uint16_t* x, const uint8_t* w_packed,
                                    const uint16_t* scales, const int32_t* m_sizes,
                                    uint16_t* y, int32_t G, int64_t M_total,
                                    int64_t N, int64_t K, int32_t group_size,
+                                   float* workspace, size_t workspace_bytes,
+                                   void* stream, const w4a16_config* cfg);
+
+/* w4a16_gemm_batched_workspace_bytes for an explicit tile configuration. */
+size_t w4a16_gemm_batched_workspace_bytes_ex(int32_t B, int64_t M, int64_t N, int64_t K,
+                                             int32_t split_k, const w4a16_config* cfg);
+
+/* w4a16_gemm_batched with an explicit tile configuration (path must be 0 or 3). */
+w4a16_status w4a16_gemm_batched_ex(const uint16_t* x, const uint8_t* w_packed,
+                                   const uint16_t* scales, uint16_t* y,
+                                   int32_t B, int64_t M, int64_t N, int64_t K,
+                                   int32_t group_size, int32_t split_k,
                                    float* workspace, size_t workspace_bytes,
                                    void* stream, const w4a16_config* cfg);
 

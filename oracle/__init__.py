@@ -17,5 +17,6 @@ from .w4a16_ref import (  # noqa: F401
     splitk_reduce_bf16,
     group_starts,
     gemm_grouped,
+    gemm_batched,
     gate,
 )

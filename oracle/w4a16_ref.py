@@ -28,6 +28,8 @@ the output. Sources (pages by title; sections in quotes):
 * Grouped: same page, Implementation "Native fused grouped kernel" -- group g
   owns rows ``[start_g, start_g + M_sizes[g])`` with
   ``start = cumsum(M_sizes) - M_sizes``.
+* Batched: same page, Summary (the batched op beside the plain and grouped
+  ones) -- B independent problems of one shape, ``Y[b] = X[b] . Wd_b^T``.
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): split-K slices are contiguous runs of whole 128-groups, each
@@ -198,6 +200,16 @@ def gemm_grouped(x_bits: np.ndarray, p: np.ndarray, s_bits: np.ndarray,
         if r1 > r0:
             y[r0:r1] = gemm(x_bits[r0:r1], p[g], s_bits[g], group)
     return y
+
+
+def gemm_batched(x_bits: np.ndarray, p: np.ndarray, s_bits: np.ndarray,
+                 group: int = GROUP) -> np.ndarray:
+    """Y[b] = X[b] . Wd_b^T for X [B, M, K], P [B, N, K/2], S [B, N, K/g]:
+    each problem is the plain definition on its own operands."""
+    B = x_bits.shape[0]
+    if p.shape[0] != B or s_bits.shape[0] != B:
+        raise ValueError("X, P and S must hold the same number of problems")
+    return np.stack([gemm(x_bits[b], p[b], s_bits[b], group) for b in range(B)])
 
 
 # ---------------------------------------------------------------- the gate

@@ -11,7 +11,8 @@ Recipe, per workload, with one fresh ``numpy.random.default_rng(seed)``
 (PCG64) and this fixed draw order:
 
 1. grouped only: ``M_sizes`` -- a multinomial split of ``M_total`` over the
-   non-empty groups (equal probabilities), forced-empty groups get 0;
+   non-empty groups (equal probabilities), forced-empty groups get 0 (the
+   batched workload: B groups of M rows, no draw);
 2. ``X``: float32 standard normal ``[M, K]``, rounded to bf16;
 3. ``q``: uniform integers 0..15 ``[N, K]`` (``[G, N, K]`` grouped), one
    unsigned nibble per byte, not packed;
@@ -33,13 +34,15 @@ import torch
 
 GROUP = 128
 
-# The five workloads, by what they are.
+# The six workloads, by what they are.
 CONFIGS = {
     "tiny": dict(M=1, N=256, K=512),
     "decode_gemv": dict(M=1, N=17408, K=5120),
     "decode_splitk": dict(M=16, N=8192, K=8192),
     "prefill": dict(M=1322, N=19456, K=2560),
     "grouped": dict(G=8, M_total=2048, N=2048, K=4096, empty=(2, 5)),
+    # B independent problems of M rows (the grouped shape, split evenly)
+    "batched": dict(B=8, M=256, N=2048, K=4096),
 }
 
 
@@ -108,6 +111,9 @@ def make_inputs(M: int, N: int, K: int, seed: int = 0, *,
 
 def make_config(name: str, seed: int = 0) -> Inputs:
     c = CONFIGS[name]
+    if "B" in c:   # batched: the grouped layout with B groups of M rows each
+        return make_inputs(c["B"] * c["M"], c["N"], c["K"], seed, G=c["B"],
+                           m_sizes=[c["M"]] * c["B"])
     if "G" in c:
         return make_inputs(c["M_total"], c["N"], c["K"], seed, G=c["G"],
                            empty=c["empty"])

@@ -404,6 +404,32 @@ def pin_grouped_matches_plain(o):
         r += mg
 
 
+# ------------------------------------------------------------------ batched
+
+def pin_batched_matches_plain(o):
+    """B = 1 equals the plain GEMM; B > 1 equals the per-problem plain GEMMs,
+    each problem with its own weights (not a neighbour's), and equals the
+    grouped GEMM with equal group sizes on the flattened rows; permuting the
+    problems permutes the outputs."""
+    c1 = rand_case(5, 7, 256, seed=93, G=1, m_sizes=[5])
+    p1 = o.pack_int4(c1.q)
+    x1 = c1.x.reshape(1, 5, 256)
+    assert np.array_equal(o.gemm_batched(x1, p1, c1.s)[0], o.gemm(c1.x, p1[0], c1.s[0]))
+    B, M, N, K = 3, 4, 6, 384
+    c = rand_case(B * M, N, K, seed=94, G=B, m_sizes=[M] * B)
+    p = o.pack_int4(c.q)
+    xb = c.x.reshape(B, M, K)
+    y = o.gemm_batched(xb, p, c.s)
+    assert y.shape == (B, M, N)
+    for b in range(B):
+        assert np.array_equal(y[b], o.gemm(xb[b], p[b], c.s[b]))
+        other = (b + 1) % B
+        assert not np.array_equal(y[b], o.gemm(xb[b], p[other], c.s[other]))
+    assert np.array_equal(y.reshape(B * M, N), o.gemm_grouped(c.x, p, c.s, [M] * B))
+    perm = [2, 0, 1]
+    assert np.array_equal(o.gemm_batched(xb[perm], p[perm], c.s[perm]), y[perm])
+
+
 # ------------------------------------------------------------------ gate
 
 def pin_gate(o):

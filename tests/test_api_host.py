@@ -91,6 +91,26 @@ def test_grouped_argument_errors(kw, want):
     assert grouped(**kw) == want
 
 
+def batched(x=A, w=B, s=C, y=D, Bn=3, M=5, N=64, K=128, g=128, sk=0, ws=A, wsb=1 << 20):
+    return L().w4a16_gemm_batched(x, w, s, y, Bn, M, N, K, g, sk, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(Bn=0), ERR_SHAPE), (dict(Bn=-1), ERR_SHAPE), (dict(M=-1), ERR_SHAPE), (dict(N=0), ERR_SHAPE),
+    (dict(K=130), ERR_GROUP), (dict(g=64), ERR_GROUP),
+    (dict(sk=3), ERR_SPLIT), (dict(sk=32), ERR_SPLIT),
+    (dict(x=None), ERR_NULL), (dict(w=None), ERR_NULL), (dict(s=None), ERR_NULL), (dict(y=None), ERR_NULL),
+    (dict(x=MIS), ERR_ALIGN), (dict(s=MIS), ERR_ALIGN), (dict(ws=MIS), ERR_ALIGN),
+    (dict(ws=None), ERR_WS), (dict(wsb=8), ERR_WS),
+    (dict(Bn=1 << 16, M=1 << 16), ERR_SHAPE),              # B * M >= 2^31
+    (dict(Bn=1 << 12, N=1 << 16, K=1 << 12), ERR_SHAPE),   # scales of all problems >= 4 GiB
+    (dict(M=0), OK),
+    (dict(M=0, x=None, w=None, s=None, y=None, ws=None), OK),   # empty: pointers unused
+])
+def test_batched_argument_errors(kw, want):
+    assert batched(**kw) == want
+
+
 def test_pack_argument_errors():
     f = L().w4a16_pack_int4
     assert f(A, B, 4, 3, None) == ERR_SHAPE          # odd K
@@ -158,6 +178,12 @@ def test_workspace_sizes():
     assert w4.w4a16_gemm_grouped_workspace_bytes(8, 2047, 2048, 4096) == 32 * 2048 * 4
     assert w4.w4a16_gemm_grouped_workspace_bytes(0, 2048, 2048, 4096) == 0
     assert w4.w4a16_gemm_workspace_bytes(16, 64, 100, 1) == 0     # invalid K
+    # batched: [SK, B*M, N] partials (SK > 1) + row sums [K/128, round_up(B*M, 4)]
+    assert w4.w4a16_gemm_batched_workspace_bytes(8, 256, 2048, 4096, 1) == 32 * 2048 * 4
+    bsk = w4.w4a16_gemm_batched_workspace_bytes(3, 5, 64, 256, 2)
+    assert bsk == ((2 * 15 * 64 * 4 + 255) // 256) * 256 + 2 * 16 * 4
+    assert w4.w4a16_gemm_batched_workspace_bytes(0, 5, 64, 256, 1) == 0
+    assert w4.w4a16_gemm_batched_workspace_bytes(2, 0, 64, 256, 1) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -20,5 +20,5 @@ def test_no_pin_is_missing():
             "bf16_to_f64", "f32_to_bf16_rne", "pack_int4", "unpack_int4",
             "dequant", "gemm", "gemm_entries", "splitk_group_ranges",
             "gemm_splitk_partials", "splitk_reduce_bf16", "group_starts",
-            "gemm_grouped", "gate"]:
+            "gemm_grouped", "gemm_batched", "gate"]:
         assert f"o.{name}(" in src, name

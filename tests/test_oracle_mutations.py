@@ -42,6 +42,10 @@ MUTATIONS = {
     "starts_inclusive": ("return np.cumsum(ms) - ms", "return np.cumsum(ms)"),
     "grouped_wrong_weights": ("y[r0:r1] = gemm(x_bits[r0:r1], p[g], s_bits[g], group)",
                               "y[r0:r1] = gemm(x_bits[r0:r1], p[0], s_bits[0], group)"),
+    "batched_wrong_weights": ("gemm(x_bits[b], p[b], s_bits[b], group) for b in range(B)",
+                              "gemm(x_bits[b], p[0], s_bits[b], group) for b in range(B)"),
+    "batched_wrong_scales": ("gemm(x_bits[b], p[b], s_bits[b], group) for b in range(B)",
+                             "gemm(x_bits[b], p[b], s_bits[B - 1 - b], group) for b in range(B)"),
     "gate_no_abs": ("max_err = float(np.max(np.abs(y - r)))", "max_err = float(np.max(y - r))"),
 }
 

@@ -256,6 +256,52 @@ def test_grouped_parity(ms, N, K, cfg):
     check_gate(bits_host(y), oracle.gemm_grouped(c.x, d.p_host, c.s, c.m_sizes), f"grouped {ms} N={N} K={K}")
 
 
+# ------------------------------------------------------------------ batched
+
+BATCHED_CASES = [
+    # B, M, N, K, split_k, tile configuration (None = automatic)
+    (1, 17, 100, 128, 0, None),
+    (3, 1, 256, 512, 0, None),      # one row per problem
+    (4, 16, 300, 640, 2, None),     # N tail, split-K
+    (2, 130, 513, 384, 0, None),    # M tail across tiles, N * G odd per problem
+    (3, 97, 257, 256, 4, None),     # more slices than groups per slice of 1
+    (5, 33, 129, 1280, 8, None),
+    (2, 64, 256, 2560, 16, 2),      # 16 slices of 20 groups
+    (2, 144, 256, 256, 1, 6),       # 144-row tiles: exactly one per problem
+    (3, 100, 300, 384, 1, 5),       # 80-row tiles: a problem spans two tiles
+    (2, 113, 300, 256, 2, 4),
+    (3, 50, 200, 256, 2, 0),        # the LDS-dequant tile kernel
+    (2, 70, 130, 384, 1, 1),
+]
+
+
+@pytest.mark.parametrize("B,M,N,K,sk,cfg", BATCHED_CASES)
+def test_batched_parity(B, M, N, K, sk, cfg):
+    c = make_inputs(B * M, N, K, seed=B * 1000 + M + N + K, G=B, m_sizes=[M] * B)
+    d = DevCase(c)
+    assert d.packed_matches_oracle()
+    x = d.x.view(B, M, K)
+    y = w4.w4a16_gemm_batched(x, d.w, d.s, split_k=sk, variant=cfg)
+    torch.cuda.synchronize()
+    ref = oracle.gemm_batched(c.x.reshape(B, M, K), d.p_host, c.s)
+    check_gate(bits_host(y.view(B * M, N)), ref.reshape(B * M, N), f"batched B={B} M={M} N={N} K={K} sk={sk}")
+    # every problem on its own gate too (a swapped problem would pass the joint gate only by luck)
+    yb = bits_host(y.view(B * M, N)).reshape(B, M, N)
+    for b in range(B):
+        check_gate(yb[b], ref[b], f"batched problem {b}")
+
+
+def test_batched_repeat_bitwise():
+    B, M, N, K = 3, 40, 300, 640
+    c = make_inputs(B * M, N, K, seed=7, G=B, m_sizes=[M] * B)
+    d = DevCase(c)
+    x = d.x.view(B, M, K)
+    y0 = bits_host(w4.w4a16_gemm_batched(x, d.w, d.s, split_k=4).view(B * M, N))
+    y1 = bits_host(w4.w4a16_gemm_batched(x, d.w, d.s, split_k=4).view(B * M, N))
+    torch.cuda.synchronize()
+    assert np.array_equal(y0, y1)
+
+
 # ------------------------------------------------------------------ full sizes, sampled outputs
 
 def _sample_entries(rng, M, N, n_random, row_edges=(), col_edges=()):
@@ -312,6 +358,27 @@ def test_grouped_full_size_sampled():
         all_ref.append(ref)
     _gate_sampled(y, np.concatenate(all_rows), np.concatenate(all_cols), np.concatenate(all_ref),
                   f"grouped G=8 {list(ms)} sampled")
+
+
+def test_batched_full_size_sampled():
+    # the batched workload in the launch configuration bench.py times
+    # (automatic tile height and split), checked on sampled entries per problem
+    c = make_config("batched")
+    B, M, N, K = c.G, c.M // c.G, c.N, c.K
+    d = DevCase(c)
+    y = bits_host(w4.w4a16_gemm_batched(d.x.view(B, M, K), d.w, d.s).view(B * M, N))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    all_rows, all_cols, all_ref = [], [], []
+    for b in range(B):
+        r0 = b * M
+        rows, cols = _sample_entries(rng, M, N, 300, row_edges=(79, 80, 127, 128), col_edges=(255, 256))
+        ref = oracle.gemm_entries(c.x[r0:r0 + M], d.p_host[b], c.s[b], rows, cols)
+        all_rows.append(rows + r0)
+        all_cols.append(cols)
+        all_ref.append(ref)
+    _gate_sampled(y, np.concatenate(all_rows), np.concatenate(all_cols), np.concatenate(all_ref),
+                  f"batched B={B} {M}x{N}x{K} sampled")
 
 
 def test_grouped_empty_total_is_noop():
