@@ -72,26 +72,60 @@ int device_cus() {
   return cache[dev];
 }
 
-// Split-K of the tile path for `tiles` output tiles: the largest power of two
-// (at most 16 and at most the group count) that keeps tiles x SK within one
-// workgroup per compute unit, so the slices run in one round; 1 from M = 1024
-// on (the pages prune split-K at M >= 512; here the one-round rule already
-// stops it wherever the tiles fill the GPU, and at 512 x 8192 x 8192 a split
-// of 2 over 128 tiles is 13 % faster). (Doubling until tiles x SK reaches the
-// compute-unit count overshoots into a second, mostly idle round: at M =
-// 96..384, N x K = 17408 x 5120 that cost 24-52 %.)
-int32_t tile_split(int64_t M, int64_t tiles, int64_t Gk) {
-  int32_t sk = 1;
-  if (M >= 1024) return 1;   // split-K only for small M ("Split-K without atomics")
+// Cost model of the tile path, in units of one row x one 128-group of work on
+// one compute unit at the 128-row tile's rate (≈0.0162 us on MI355X: the
+// 144-row tile runs 20 groups in 48.7 us). One workgroup per compute unit:
+// a launch takes ceil(tiles x SK / CUs) rounds of (rows / rate) x groups per
+// slice. A split adds its fp32 partials, written by the tile kernel and read
+// by the reduce (8 x SK x M x N bytes at ≈5 TB/s) and the reduce launch
+// (≈2 us). Splits only where tiles x SK fit one round (a second, mostly idle
+// round of slices never pays: at M = 96..384, N x K = 17408 x 5120 doubling
+// past it cost 24-52 %).
+constexpr double kUnitUs = 0.0162, kReduceBytesPerUs = 5.0e6, kReduceLaunchUs = 2.0;
+
+double tile_cost(int64_t M, int64_t N, int64_t Gk, int64_t tiles, int bm, double rate, int64_t sk, int64_t cus) {
+  double c = (double)ceil_div(tiles * sk, cus) * bm / rate * (double)ceil_div(Gk, sk);
+  if (sk > 1) c += (8.0 * (double)sk * (double)M * (double)N / kReduceBytesPerUs + kReduceLaunchUs) / kUnitUs;
+  return c;
+}
+
+// The split of least cost for `tiles` tiles of bm rows (rate: per-row rate of
+// the height): 1, or a power of two up to 16 (and the group count) whose
+// slices fit one round.
+int32_t tile_split_rate(int64_t M, int64_t N, int64_t Gk, int64_t tiles, int bm, double rate) {
   const int64_t cus = device_cus();
-  while (sk < 16 && tiles * sk * 2 <= cus && sk * 2 <= Gk) sk <<= 1;
-  return sk;
+  int32_t best = 1;
+  double best_cost = tile_cost(M, N, Gk, tiles, bm, rate, 1, cus);
+  for (int32_t sk = 2; sk <= 16 && sk <= Gk && tiles * sk <= cus; sk <<= 1) {
+    const double c = tile_cost(M, N, Gk, tiles, bm, rate, sk, cus);
+    if (c < best_cost * (1.0 - 1e-9)) {
+      best = sk;
+      best_cost = c;
+    }
+  }
+  return best;
+}
+
+// per-row rates of the tile heights, relative to the 128-row tile (shorter
+// tiles amortise the per-group dequantisation and barrier over fewer rows;
+// at 1322 x 19456 x 2560 on one box: 4 rounds of 128 rows 166 us, 4 of 112
+// rows 161 us, 3 of 144 rows 146 us, 5 of 96 rows 176 us)
+struct TileCand { int cfg, bm; double rate; };
+constexpr TileCand kTileCands[] = {{2, 128, 1.0}, {6, 144, 0.96}, {4, 112, 0.91}, {3, 96, 0.907}, {5, 80, 0.85}};
+
+double tile_rate(int cfg) {
+  for (const TileCand& c : kTileCands)
+    if (c.cfg == cfg) return c.rate;
+  return 0.9;   // tile configurations 0 and 1
+}
+
+int32_t tile_split(int64_t M, int64_t N, int64_t Gk, int64_t tiles, int cfg) {
+  return tile_split_rate(M, N, Gk, tiles, w4a16::tile_bm(cfg), tile_rate(cfg));
 }
 
 int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg, int variant) {
   const int64_t Gk = K / kGroup;
   int32_t sk = 1;
-  if (M >= 1024) return 1;   // split-K only for small M ("Split-K without atomics")
   switch (path) {
     case kPathGemv: {
       // only what the register budget for x needs (at most 64 groups per
@@ -117,7 +151,7 @@ int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg, int
     }
     case kPathTile: {
       const int64_t tiles = ceil_div(M, w4a16::tile_bm(tile_cfg)) * ceil_div(N, w4a16::tile_bn(tile_cfg));
-      sk = tile_split(M, tiles, Gk);
+      sk = tile_split(M, N, Gk, tiles, tile_cfg);
       break;
     }
     default:
@@ -142,25 +176,18 @@ struct Plan {
 // tile (group boundaries split tiles). Shorter tiles (96 rows, configuration
 // 3) when that whole grid still fits one wave of workgroups over the compute
 // units: each tile then finishes sooner and no tile waits for a second round.
-// Tile height of the LDS-DMA kernel (and, with automatic split-K, the split):
-// one workgroup per compute unit, so the time is the rounds of tiles x slices
-// times one unit's time, taken proportional to its rows x groups and divided
-// by each height's measured per-row rate relative to the 128-row tile
-// (shorter tiles amortise the per-group dequantisation and barrier over fewer
-// rows; at 1322 x 19456 x 2560 on one box: 4 rounds of 128 rows 166 us, 4 of
-// 112 rows 161 us, 3 of 144 rows 146 us, 5 of 96 rows 176 us). `tiles(bm)`
-// counts the output tiles, `split(tiles)` gives the split for a tile count.
-template <class T, class S>
-int pick_tile_cfg(int64_t Gk, T tiles, S split) {
-  struct Cand { int cfg, bm; double rate; };
-  static const Cand cands[] = {{2, 128, 1.0}, {6, 144, 0.96}, {4, 112, 0.91}, {3, 96, 0.907}, {5, 80, 0.85}};
+// Tile height of the LDS-DMA kernel: the candidate of least cost (above),
+// with its own best split when split_k is automatic (`split` < 0) or the
+// given one. `tiles(bm)` counts the output tiles of a height.
+template <class T>
+int pick_tile_cfg(int64_t M, int64_t N, int64_t Gk, T tiles, int64_t split) {
   const int64_t cus = device_cus();
   int best = 2;
   double best_cost = 0.0;
-  for (const Cand& c : cands) {
+  for (const TileCand& c : kTileCands) {
     const int64_t t = tiles(c.bm);
-    const int64_t sk = std::max<int64_t>(1, split(t));
-    const double cost = (double)ceil_div(t * sk, cus) * c.bm / c.rate * (double)ceil_div(Gk, sk);
+    const int64_t sk = split > 0 ? split : tile_split_rate(M, N, Gk, t, c.bm, c.rate);
+    const double cost = tile_cost(M, N, Gk, t, c.bm, c.rate, sk, cus);
     if (best_cost == 0.0 || cost < best_cost * (1.0 - 1e-9)) {
       best = c.cfg;
       best_cost = cost;
@@ -169,12 +196,11 @@ int pick_tile_cfg(int64_t Gk, T tiles, S split) {
   return best;
 }
 
-// split_k = 0: automatic, chosen with the height (tile_split); otherwise fixed
+// split_k = 0: automatic, chosen with the height; otherwise fixed
 int default_tile_cfg(int64_t M, int64_t N, int64_t K, int32_t split_k) {
   const int64_t nt = ceil_div(N, 256), Gk = K / kGroup;
   return pick_tile_cfg(
-      Gk, [&](int bm) { return ceil_div(std::max<int64_t>(M, 1), bm) * nt; },
-      [&](int64_t t) { return split_k > 0 ? (int64_t)split_k : (int64_t)tile_split(M, t, Gk); });
+      M, N, Gk, [&](int bm) { return ceil_div(std::max<int64_t>(M, 1), bm) * nt; }, split_k > 0 ? split_k : -1);
 }
 
 // grouped (no split-K): M_sizes stays on the device, so the tile count is
@@ -183,8 +209,7 @@ int default_tile_cfg(int64_t M, int64_t N, int64_t K, int32_t split_k) {
 int default_grouped_tile_cfg(int64_t G, int64_t M_total, int64_t N, int64_t K) {
   const int64_t nt = ceil_div(N, 256);
   return pick_tile_cfg(
-      K / kGroup, [&](int bm) { return (ceil_div(std::max<int64_t>(M_total, 1), bm) + G / 2) * nt; },
-      [](int64_t) { return (int64_t)1; });
+      M_total, N, K / kGroup, [&](int bm) { return (ceil_div(std::max<int64_t>(M_total, 1), bm) + G / 2) * nt; }, 1);
 }
 
 // Batched: B problems of M rows on the tile kernel (weight group b = problem
@@ -207,12 +232,11 @@ w4a16_status make_batched_plan(int32_t B, int64_t M, int64_t N, int64_t K, int32
   }
   if (tile_cfg < 0)
     tile_cfg = pick_tile_cfg(
-        Gk, [&](int bm) { return (int64_t)B * ceil_div(M, bm) * nt; },
-        [&](int64_t t) { return split_k > 0 ? (int64_t)split_k : (int64_t)tile_split(M, t, Gk); });
+        Mt, N, Gk, [&](int bm) { return (int64_t)B * ceil_div(M, bm) * nt; }, split_k > 0 ? split_k : -1);
   if (tile_cfg >= w4a16::tile_num_cfgs()) return W4A16_ERR_SHAPE;
   const int64_t tiles =
       (int64_t)B * ceil_div(M, w4a16::tile_bm(tile_cfg)) * ceil_div(N, w4a16::tile_bn(tile_cfg));
-  int32_t sk = split_k > 0 ? split_k : tile_split(M, tiles, Gk);
+  int32_t sk = split_k > 0 ? split_k : tile_split(Mt, N, Gk, tiles, tile_cfg);
   if (sk > Gk && split_k == 0) sk = 1;
   p->cfg = tile_cfg;
   p->sk = sk;

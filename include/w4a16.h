@@ -78,13 +78,14 @@ w4a16_status w4a16_pack_int4(const uint8_t* q, uint8_t* w_packed,
 
 /*
  * The split-K factor the library uses for w4a16_gemm when split_k == 0
- * (auto) at this shape: 1 for M >= 1024 (split-K is restricted to small M,
- * "Split-K without atomics", on the MI350X Triton page); below that, for the
- * M = 1 GEMV only what its register budget for x needs (at most 64 groups per
- * slice), for the M <= 16 kernel enough slices for one workgroup per compute
- * unit, and for the tile kernel the largest power of two (at most 16) that
- * keeps tiles x SK within one workgroup per compute unit, chosen together
- * with the tile height. Returns 0 on invalid dimensions.
+ * (auto) at this shape: for the M = 1 GEMV only what its register budget for
+ * x needs (at most 64 groups per slice), for the M <= 16 kernel enough slices
+ * for one workgroup per compute unit, and for the tile kernel the power of
+ * two (at most 16) of least estimated time among those that keep tiles x SK
+ * within one workgroup per compute unit, counting the fp32 partials and the
+ * reduce, chosen together with the tile height (so, unlike the MI350X Triton
+ * page's prune of split-K at M >= 512, a tall-K shape with few tiles splits
+ * at any M). Returns 0 on invalid dimensions.
  */
 int32_t w4a16_gemm_auto_split_k(int64_t M, int64_t N, int64_t K);
 

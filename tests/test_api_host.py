@@ -144,14 +144,17 @@ def test_explicit_path_errors():
 
 
 def test_auto_split_rule():
-    # split-K is used only below M = 1024 ("Split-K without atomics" prunes
-    # at 512; the tile kernel's one-round rule stops it earlier on wide N)
-    for M in (1024, 1322, 4096):
-        assert w4.w4a16_gemm_auto_split_k(M, 64, 8192) == 1
-    # the tile kernel: tiles x SK stay within one workgroup per compute unit
-    # (256 on the host without a device): 1322 x 19456 has 760+ tiles
-    assert w4.w4a16_gemm_auto_split_k(1322, 19456, 2560) == 1
+    # the tile kernel splits only where tiles x SK fit one round of one
+    # workgroup per compute unit (256 on the host without a device), and only
+    # when the shorter slices pay for the partials and the reduce
+    assert w4.w4a16_gemm_auto_split_k(1322, 19456, 2560) == 1    # 760+ tiles: no room
+    assert w4.w4a16_gemm_auto_split_k(4096, 17408, 5120) == 1
     assert w4.w4a16_gemm_auto_split_k(128, 17408, 5120) == 2     # 68 tiles of 128 x 256
+    assert w4.w4a16_gemm_auto_split_k(1322, 2560, 9728) == 2     # tall K: 120 tiles of 112 rows
+    assert w4.w4a16_gemm_auto_split_k(4096, 64, 8192) > 1        # 32 tiles, 64 groups
+    for M, N, K in ((100, 256, 8192), (1322, 2560, 9728), (4096, 64, 8192)):
+        sk = w4.w4a16_gemm_auto_split_k(M, N, K)
+        assert sk in (1, 2, 4, 8, 16)
     # the decode GEMV splits only for its register budget (<= 64 groups per slice)
     assert w4.w4a16_gemm_auto_split_k(1, 17408, 5120) == 1
     assert w4.w4a16_gemm_auto_split_k(1, 256, 512) == 1
