@@ -7,7 +7,8 @@ fp32 accumulation, bf16 output), reported as effective weight bandwidth:
 (N*K/2 packed bytes + N*K/128*2 scale bytes) per step / time per step.
 
 All inputs are synthetic (seeded, see synth/gen.py) and resident in HBM
-before the timed region. Weights and scales are rotated over enough copies
+before the timed region, which is one graph replay of exactly K steps after
+W eager warm-up steps and untimed replays that let the GPU clocks settle. Weights and scales are rotated over enough copies
 (>= 512 MB) that the 256 MB Infinity Cache cannot serve them from one step
 to the next. The other workloads (small-batch split-K decode, deep prefill,
 grouped) are measured the same way and reported under "workloads".
@@ -77,12 +78,14 @@ class Dev:
         torch.cuda.synchronize()
 
 
-def time_steps(step, steps, warmup):
+def time_steps(step, steps, warmup, settle_s=0.03):
     """W untimed eager warmup steps; then the K steps are captured once in a
     HIP graph on a side stream (the library enqueues only kernels, so the
-    capture is exact), replayed once untimed (graph upload), and the timed
-    region is one replay of exactly K steps bracketed by synchronisations and
-    HIP events on that stream. Returns (total seconds, seconds per step)."""
+    capture is exact) and replayed untimed (graph upload, then until about
+    `settle_s` of GPU work has run, so that the clocks have left their idle
+    state; at most 20 replays), and the timed region is one replay of exactly
+    K steps bracketed by synchronisations and HIP events on that stream.
+    Returns (total seconds, seconds per step)."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -96,6 +99,12 @@ def time_steps(step, steps, warmup):
                 step(i)
         g.replay()
         torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for _ in range(20):
+            if time.perf_counter() - w0 >= settle_s:
+                break
+            g.replay()
+            torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(s)
