@@ -146,7 +146,7 @@ int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg, int
       const int v = variant > 0 ? variant : kSkinnyDefaultVariant;
       const int nt = v % 10, waves = v / 10;
       const int64_t wgs = ceil_div(N, 16 * (int64_t)std::max(nt, 1));
-      while (sk < 16 && wgs * sk < 256 && ceil_div(Gk, (int64_t)sk * 2) >= waves) sk <<= 1;
+      while (sk < 16 && wgs * sk < device_cus() && ceil_div(Gk, (int64_t)sk * 2) >= waves) sk <<= 1;
       break;
     }
     case kPathTile: {
