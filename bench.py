@@ -11,7 +11,8 @@ before the timed region, which is one graph replay of exactly K steps after
 W eager warm-up steps and untimed replays that let the GPU clocks settle. Weights and scales are rotated over enough copies
 (>= 512 MB) that the 256 MB Infinity Cache cannot serve them from one step
 to the next. The other workloads (small-batch split-K decode, deep prefill,
-grouped) are measured the same way and reported under "workloads".
+grouped, batched, the four decoder GEMMs of a layer at M=1322 with group
+sizes 32 and 128) are measured the same way and reported under "workloads".
 
 Output: one JSON line on stdout. `--gpus N` with N > 1 exits with a message:
 the library is single-GPU.
@@ -203,6 +204,43 @@ def bench_batched(name, steps, warmup, variant=None, split_k=0):
                 tflops=flops / t / 1e12, frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS), d, y
 
 
+# the four decoder GEMMs of one layer at M = 1322 (N, K), after the per-GEMM
+# table of the gfx1151 skinny-GEMM page (its model quantises with one scale
+# per 32 k)
+LAYER_GEMMS = (("gate_up", 19456, 2560), ("qkv", 6144, 2560), ("o_proj", 4096, 2560), ("down", 2560, 9728))
+LAYER_M = 1322
+
+
+def bench_layers(steps, warmup, group):
+    """Each of the four layer GEMMs on its own (default path and tile choice)
+    at the given group size, and the per-layer aggregate: total flops / total
+    time of the four."""
+    import torch
+    import bf16_activation_quantized_amd as w4
+    from synth import make_inputs
+    M = LAYER_M
+    out, tot_flops, tot_s = {}, 0.0, 0.0
+    for name, N, K in LAYER_GEMMS:
+        c = make_inputs(M, N, K, 1322 + N + K, group=group)
+        d = Dev(c, 1)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        need = w4.w4a16_gemm_workspace_bytes(M, N, K, 0, group_size=group)
+        ws = torch.empty(max(need // 4, 1) + 4, dtype=torch.float32, device="cuda")
+
+        def step(i, d=d, y=y, ws=ws):
+            w4.w4a16_gemm(d.x, d.w[0], d.s[0], y=y, workspace=ws, group_size=group)
+
+        _, t = time_steps(step, steps, warmup)
+        flops = 2.0 * M * N * K
+        out[name] = dict(N=N, K=K, us_per_step=round(t * 1e6, 2), tflops=round(flops / t / 1e12, 1))
+        tot_flops += flops
+        tot_s += t
+        del d, y, ws
+    out["per_layer"] = dict(us=round(tot_s * 1e6, 2), tflops=round(tot_flops / tot_s / 1e12, 1),
+                            frac_bf16=round(tot_flops / tot_s / 1e12 / BF16_PEAK_TFLOPS, 4))
+    return dict(M=M, group_size=group, gemms=out)
+
+
 def bench_pack(steps, warmup):
     import torch
     import bf16_activation_quantized_amd as w4
@@ -329,7 +367,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default=None,
                     choices=["decode_gemv", "decode_splitk", "prefill", "grouped", "batched", "pack", "tiny",
-                             "dispatch"],
+                             "dispatch", "layers"],
                     help="measure one workload only and print its record (for profiling)")
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--variant", type=int, default=None)
@@ -367,6 +405,8 @@ def main():
             r, _, _ = bench_grouped("grouped", args.steps, args.warmup, args.variant)
         elif args.only == "batched":
             r, _, _ = bench_batched("batched", args.steps, args.warmup, args.variant, args.split_k)
+        elif args.only == "layers":
+            r = {f"g{g}": bench_layers(args.steps, args.warmup, g) for g in (32, 128)}
         else:
             r = bench_pack(args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **r}), flush=True)
@@ -404,6 +444,9 @@ def main():
         workloads["grouped"], _, _ = bench_grouped("grouped", steps2, args.warmup)
         log("bench: batched")
         workloads["batched"], _, _ = bench_batched("batched", steps2, args.warmup)
+        for g in (32, 128):
+            log(f"bench: layer GEMMs group {g}")
+            workloads[f"layers_g{g}"] = bench_layers(steps2, args.warmup, g)
         log("bench: pack")
         workloads["pack_int4"] = bench_pack(steps2, args.warmup)
         torch.cuda.empty_cache()

@@ -65,6 +65,9 @@ def _lib():
         "w4a16_splitk_reduce": (ctypes.c_int, [P, P, I32, I64, I64, P]),
         "w4a16_gemm_batched_workspace_bytes": (SZ, [I32, I64, I64, I64, I32]),
         "w4a16_gemm_batched_workspace_bytes_ex": (SZ, [I32, I64, I64, I64, I32, P]),
+        "w4a16_gemm_workspace_bytes_gs": (SZ, [I64, I64, I64, I32, I32, P]),
+        "w4a16_gemm_grouped_workspace_bytes_gs": (SZ, [I32, I64, I64, I64, I32]),
+        "w4a16_gemm_batched_workspace_bytes_gs": (SZ, [I32, I64, I64, I64, I32, I32, P]),
         "w4a16_gemm_batched": (ctypes.c_int, [P, P, P, P, I32, I64, I64, I64, I32, I32, P, SZ, P]),
         "w4a16_gemm_batched_ex": (ctypes.c_int, [P, P, P, P, I32, I64, I64, I64, I32, I32, P, SZ, P, P]),
     }
@@ -146,8 +149,11 @@ def w4a16_gemm_auto_split_k(M: int, N: int, K: int) -> int:
 
 
 def w4a16_gemm_workspace_bytes(M: int, N: int, K: int, split_k: int = 0,
-                               path: Optional[int] = None, variant: Optional[int] = None) -> int:
+                               path: Optional[int] = None, variant: Optional[int] = None,
+                               group_size: int = GROUP_SIZE) -> int:
     cfg = _cfg(path, variant)
+    if group_size != GROUP_SIZE:
+        return int(_lib().w4a16_gemm_workspace_bytes_gs(M, N, K, group_size, split_k, cfg))
     if cfg is None:
         return int(_lib().w4a16_gemm_workspace_bytes(M, N, K, split_k))
     return int(_lib().w4a16_gemm_workspace_bytes_ex(M, N, K, split_k, cfg))
@@ -156,17 +162,17 @@ def w4a16_gemm_workspace_bytes(M: int, N: int, K: int, split_k: int = 0,
 def w4a16_gemm(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
                y: Optional[torch.Tensor] = None, split_k: int = 0,
                workspace: Optional[torch.Tensor] = None, path: Optional[int] = None,
-               variant: Optional[int] = None, stream=None) -> torch.Tensor:
+               variant: Optional[int] = None, stream=None, group_size: int = GROUP_SIZE) -> torch.Tensor:
     """Y[M, N] = X[M, K] . dequant(W)[N, K]^T (bf16 out, fp32 accumulation)."""
     _check(x, "x", torch.bfloat16)
     M, K = x.shape
     N = w_packed.shape[0]
     _check(w_packed, "w_packed", torch.uint8, (N, K // 2))
-    _check(scales, "scales", torch.bfloat16, (N, K // GROUP_SIZE))
+    _check(scales, "scales", torch.bfloat16, (N, K // group_size))
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _check(y, "y", torch.bfloat16, (M, N))
-    need = w4a16_gemm_workspace_bytes(M, N, K, split_k, path, variant)
+    need = w4a16_gemm_workspace_bytes(M, N, K, split_k, path, variant, group_size)
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4 + 1, dtype=torch.float32, device=x.device)
     if workspace is not None:
@@ -175,34 +181,37 @@ def w4a16_gemm(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
     cfg = _cfg(path, variant)
     L = _lib()
     if cfg is None:
-        st = L.w4a16_gemm(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(y), M, N, K, GROUP_SIZE, split_k,
+        st = L.w4a16_gemm(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(y), M, N, K, group_size, split_k,
                           _ptr(workspace), wbytes, _stream(stream))
     else:
-        st = L.w4a16_gemm_ex(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(y), M, N, K, GROUP_SIZE, split_k,
+        st = L.w4a16_gemm_ex(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(y), M, N, K, group_size, split_k,
                              _ptr(workspace), wbytes, _stream(stream), cfg)
     _raise(st, "w4a16_gemm")
     return y
 
 
-def w4a16_gemm_grouped_workspace_bytes(G: int, M_total: int, N: int, K: int) -> int:
+def w4a16_gemm_grouped_workspace_bytes(G: int, M_total: int, N: int, K: int,
+                                       group_size: int = GROUP_SIZE) -> int:
+    if group_size != GROUP_SIZE:
+        return int(_lib().w4a16_gemm_grouped_workspace_bytes_gs(G, M_total, N, K, group_size))
     return int(_lib().w4a16_gemm_grouped_workspace_bytes(G, M_total, N, K))
 
 
 def w4a16_gemm_grouped(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
                        m_sizes: torch.Tensor, y: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, variant: Optional[int] = None,
-                       stream=None) -> torch.Tensor:
+                       stream=None, group_size: int = GROUP_SIZE) -> torch.Tensor:
     """Grouped GEMM in one launch; m_sizes stays on the device."""
     _check(x, "x", torch.bfloat16)
     M_total, K = x.shape
     G, N = w_packed.shape[0], w_packed.shape[1]
     _check(w_packed, "w_packed", torch.uint8, (G, N, K // 2))
-    _check(scales, "scales", torch.bfloat16, (G, N, K // GROUP_SIZE))
+    _check(scales, "scales", torch.bfloat16, (G, N, K // group_size))
     _check(m_sizes, "m_sizes", torch.int32, (G,))
     if y is None:
         y = torch.empty((M_total, N), dtype=torch.bfloat16, device=x.device)
     _check(y, "y", torch.bfloat16, (M_total, N))
-    need = w4a16_gemm_grouped_workspace_bytes(G, M_total, N, K)
+    need = w4a16_gemm_grouped_workspace_bytes(G, M_total, N, K, group_size)
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4 + 1, dtype=torch.float32, device=x.device)
     if workspace is not None:
@@ -212,17 +221,20 @@ def w4a16_gemm_grouped(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Te
     cfg = _cfg(PATH_TILE, variant) if variant is not None else None
     if cfg is None:
         st = L.w4a16_gemm_grouped(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(m_sizes), _ptr(y), G, M_total, N, K,
-                                  GROUP_SIZE, _ptr(workspace), wbytes, _stream(stream))
+                                  group_size, _ptr(workspace), wbytes, _stream(stream))
     else:
         st = L.w4a16_gemm_grouped_ex(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(m_sizes), _ptr(y), G, M_total, N,
-                                     K, GROUP_SIZE, _ptr(workspace), wbytes, _stream(stream), cfg)
+                                     K, group_size, _ptr(workspace), wbytes, _stream(stream), cfg)
     _raise(st, "w4a16_gemm_grouped")
     return y
 
 
 def w4a16_gemm_batched_workspace_bytes(B: int, M: int, N: int, K: int, split_k: int = 0,
-                                       variant: Optional[int] = None) -> int:
+                                       variant: Optional[int] = None, group_size: int = GROUP_SIZE) -> int:
     L = _lib()
+    if group_size != GROUP_SIZE:
+        cfg = None if variant is None else _cfg(PATH_TILE, variant)
+        return int(L.w4a16_gemm_batched_workspace_bytes_gs(B, M, N, K, group_size, split_k, cfg))
     if variant is None:
         return int(L.w4a16_gemm_batched_workspace_bytes(B, M, N, K, split_k))
     return int(L.w4a16_gemm_batched_workspace_bytes_ex(B, M, N, K, split_k, _cfg(PATH_TILE, variant)))
@@ -231,17 +243,17 @@ def w4a16_gemm_batched_workspace_bytes(B: int, M: int, N: int, K: int, split_k: 
 def w4a16_gemm_batched(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
                        y: Optional[torch.Tensor] = None, split_k: int = 0,
                        workspace: Optional[torch.Tensor] = None, variant: Optional[int] = None,
-                       stream=None) -> torch.Tensor:
+                       stream=None, group_size: int = GROUP_SIZE) -> torch.Tensor:
     """Y[b] = X[b] . dequant(W[b])^T for B independent problems, one launch."""
     _check(x, "x", torch.bfloat16)
     B, M, K = x.shape
     N = w_packed.shape[1]
     _check(w_packed, "w_packed", torch.uint8, (B, N, K // 2))
-    _check(scales, "scales", torch.bfloat16, (B, N, K // GROUP_SIZE))
+    _check(scales, "scales", torch.bfloat16, (B, N, K // group_size))
     if y is None:
         y = torch.empty((B, M, N), dtype=torch.bfloat16, device=x.device)
     _check(y, "y", torch.bfloat16, (B, M, N))
-    need = w4a16_gemm_batched_workspace_bytes(B, M, N, K, split_k, variant)
+    need = w4a16_gemm_batched_workspace_bytes(B, M, N, K, split_k, variant, group_size)
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4 + 1, dtype=torch.float32, device=x.device)
     if workspace is not None:
@@ -249,10 +261,10 @@ def w4a16_gemm_batched(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Te
     wbytes = 0 if workspace is None else workspace.numel() * 4
     L = _lib()
     if variant is None:
-        st = L.w4a16_gemm_batched(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(y), B, M, N, K, GROUP_SIZE, split_k,
+        st = L.w4a16_gemm_batched(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(y), B, M, N, K, group_size, split_k,
                                   _ptr(workspace), wbytes, _stream(stream))
     else:
-        st = L.w4a16_gemm_batched_ex(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(y), B, M, N, K, GROUP_SIZE,
+        st = L.w4a16_gemm_batched_ex(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(y), B, M, N, K, group_size,
                                      split_k, _ptr(workspace), wbytes, _stream(stream), _cfg(PATH_TILE, variant))
     _raise(st, "w4a16_gemm_batched")
     return y

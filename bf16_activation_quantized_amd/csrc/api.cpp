@@ -12,7 +12,8 @@
 
 namespace {
 
-constexpr int64_t kGroup = 128;
+constexpr int64_t kGroup = 128;   // k per pipeline stage (and the default scale group)
+constexpr int32_t kGroupSmall = 32;   // the other scale group size (tile path only)
 constexpr int64_t kMaxDim = 0x7FFFFFFFLL;
 constexpr uint64_t kMaxBytes = 0xFFFFFFFFULL;   // one buffer resource extent
 
@@ -179,12 +180,14 @@ struct Plan {
 // Tile height of the LDS-DMA kernel: the candidate of least cost (above),
 // with its own best split when split_k is automatic (`split` < 0) or the
 // given one. `tiles(bm)` counts the output tiles of a height.
+// Only heights that run the scale group size gs are candidates.
 template <class T>
-int pick_tile_cfg(int64_t M, int64_t N, int64_t Gk, T tiles, int64_t split) {
+int pick_tile_cfg(int64_t M, int64_t N, int64_t Gk, T tiles, int64_t split, int32_t gs) {
   const int64_t cus = device_cus();
   int best = 2;
   double best_cost = 0.0;
   for (const TileCand& c : kTileCands) {
+    if (!w4a16::tile_group_ok(c.cfg, gs)) continue;
     const int64_t t = tiles(c.bm);
     const int64_t sk = split > 0 ? split : tile_split_rate(M, N, Gk, t, c.bm, c.rate);
     const double cost = tile_cost(M, N, Gk, t, c.bm, c.rate, sk, cus);
@@ -197,19 +200,26 @@ int pick_tile_cfg(int64_t M, int64_t N, int64_t Gk, T tiles, int64_t split) {
 }
 
 // split_k = 0: automatic, chosen with the height; otherwise fixed
-int default_tile_cfg(int64_t M, int64_t N, int64_t K, int32_t split_k) {
+int default_tile_cfg(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t gs) {
   const int64_t nt = ceil_div(N, 256), Gk = K / kGroup;
   return pick_tile_cfg(
-      M, N, Gk, [&](int bm) { return ceil_div(std::max<int64_t>(M, 1), bm) * nt; }, split_k > 0 ? split_k : -1);
+      M, N, Gk, [&](int bm) { return ceil_div(std::max<int64_t>(M, 1), bm) * nt; }, split_k > 0 ? split_k : -1,
+      gs);
 }
 
 // grouped (no split-K): M_sizes stays on the device, so the tile count is
 // estimated as ceil(M_total / bm) + G / 2 per column (each group's partial
 // last tile adds half a tile on average; the kernel maps only the real tiles)
-int default_grouped_tile_cfg(int64_t G, int64_t M_total, int64_t N, int64_t K) {
+int default_grouped_tile_cfg(int64_t G, int64_t M_total, int64_t N, int64_t K, int32_t gs) {
   const int64_t nt = ceil_div(N, 256);
   return pick_tile_cfg(
-      M_total, N, K / kGroup, [&](int bm) { return (ceil_div(std::max<int64_t>(M_total, 1), bm) + G / 2) * nt; }, 1);
+      M_total, N, K / kGroup, [&](int bm) { return (ceil_div(std::max<int64_t>(M_total, 1), bm) + G / 2) * nt; }, 1,
+      gs);
+}
+
+// bytes of the [K / gs, ld] fp32 row sums of the tile path
+uint64_t rowsum_bytes(int64_t M, int64_t K, int32_t gs) {
+  return (uint64_t)(K / gs) * round_up((uint64_t)M, 4) * 4u;
 }
 
 // Batched: B problems of M rows on the tile kernel (weight group b = problem
@@ -223,7 +233,7 @@ struct BatchedPlan {
 };
 
 w4a16_status make_batched_plan(int32_t B, int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg,
-                               BatchedPlan* p) {
+                               int32_t gs, BatchedPlan* p) {
   const int64_t Gk = K / kGroup, nt = ceil_div(N, 256), Mt = (int64_t)B * M;
   int tile_cfg = -1;
   if (cfg != nullptr) {
@@ -232,8 +242,9 @@ w4a16_status make_batched_plan(int32_t B, int64_t M, int64_t N, int64_t K, int32
   }
   if (tile_cfg < 0)
     tile_cfg = pick_tile_cfg(
-        Mt, N, Gk, [&](int bm) { return (int64_t)B * ceil_div(M, bm) * nt; }, split_k > 0 ? split_k : -1);
+        Mt, N, Gk, [&](int bm) { return (int64_t)B * ceil_div(M, bm) * nt; }, split_k > 0 ? split_k : -1, gs);
   if (tile_cfg >= w4a16::tile_num_cfgs()) return W4A16_ERR_SHAPE;
+  if (!w4a16::tile_group_ok(tile_cfg, gs)) return W4A16_ERR_GROUP_SIZE;
   const int64_t tiles =
       (int64_t)B * ceil_div(M, w4a16::tile_bm(tile_cfg)) * ceil_div(N, w4a16::tile_bn(tile_cfg));
   int32_t sk = split_k > 0 ? split_k : tile_split(Mt, N, Gk, tiles, tile_cfg);
@@ -243,14 +254,17 @@ w4a16_status make_batched_plan(int32_t B, int64_t M, int64_t N, int64_t K, int32
   p->gps = (int32_t)ceil_div(Gk, sk);
   p->ws_split = sk > 1 ? (uint64_t)sk * (uint64_t)Mt * (uint64_t)N * 4u : 0u;
   p->ld = (int64_t)round_up((uint64_t)Mt, 4);
-  p->ws_sx = (uint64_t)Gk * (uint64_t)p->ld * 4u;
+  p->ws_sx = rowsum_bytes(Mt, K, gs);
   return W4A16_OK;
 }
 
 
-w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg, Plan* p) {
+// Group size 32 runs on the tile path only (the GEMV and skinny kernels take
+// one scale per 128 k), whatever M is.
+w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg, int32_t gs,
+                       Plan* p) {
   const int64_t Gk = K / kGroup;
-  Path path = auto_path(M, K, split_k);
+  Path path = gs == kGroup ? auto_path(M, K, split_k) : kPathTile;
   int variant = -1;
   if (cfg != nullptr) {
     if (cfg->path < 0 || cfg->path > 3) return W4A16_ERR_SHAPE;
@@ -259,10 +273,12 @@ w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w
   }
   if (path == kPathGemv && M != 1) return W4A16_ERR_SHAPE;
   if (path == kPathSkinny && M > 16) return W4A16_ERR_SHAPE;
+  if (path != kPathTile && gs != kGroup) return W4A16_ERR_GROUP_SIZE;
   int tile_cfg = 0;
   if (path == kPathTile) {
-    tile_cfg = variant >= 0 ? variant : default_tile_cfg(M, N, K, split_k);
+    tile_cfg = variant >= 0 ? variant : default_tile_cfg(M, N, K, split_k, gs);
     if (tile_cfg >= w4a16::tile_num_cfgs()) return W4A16_ERR_SHAPE;
+    if (!w4a16::tile_group_ok(tile_cfg, gs)) return W4A16_ERR_GROUP_SIZE;
   }
   int32_t sk = split_k > 0 ? split_k : auto_split(path, M, N, K, tile_cfg, variant);
   if (sk > Gk && split_k == 0) sk = 1;
@@ -276,7 +292,7 @@ w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w
   p->variant = path == kPathTile ? tile_cfg : variant;
   p->ws_split = sk > 1 ? (uint64_t)sk * (uint64_t)M * (uint64_t)N * 4u : 0u;
   p->ld = (int64_t)round_up((uint64_t)M, 4);
-  p->ws_sx = path == kPathTile ? (uint64_t)Gk * (uint64_t)p->ld * 4u : 0u;
+  p->ws_sx = path == kPathTile ? rowsum_bytes(M, K, gs) : 0u;
   return W4A16_OK;
 }
 
@@ -284,7 +300,7 @@ uint64_t plan_bytes(const Plan& p) { return round_up(p.ws_split, 256) + p.ws_sx;
 
 w4a16_status check_dims(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if (M < 0 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return W4A16_ERR_SHAPE;
-  if (group_size != kGroup || K % kGroup != 0) return W4A16_ERR_GROUP_SIZE;
+  if ((group_size != kGroup && group_size != kGroupSmall) || K % kGroup != 0) return W4A16_ERR_GROUP_SIZE;
   // buffer extents of one resource
   if ((uint64_t)N * (uint64_t)K / 2u > kMaxBytes) return W4A16_ERR_SHAPE;
   if ((uint64_t)M * (uint64_t)K * 2u > kMaxBytes) return W4A16_ERR_SHAPE;
@@ -298,7 +314,7 @@ w4a16_status check_batched(int32_t B, int64_t M, int64_t N, int64_t K, int32_t g
   w4a16_status st = check_dims((int64_t)B * M, N, K, group_size);
   if (st != W4A16_OK) return st;
   // one buffer resource covers the scales of all problems
-  if ((uint64_t)B * (uint64_t)N * (uint64_t)(K / kGroup) * 2u > kMaxBytes) return W4A16_ERR_SHAPE;
+  if ((uint64_t)B * (uint64_t)N * (uint64_t)(K / group_size) * 2u > kMaxBytes) return W4A16_ERR_SHAPE;
   return W4A16_OK;
 }
 
@@ -314,7 +330,7 @@ w4a16_status run_gemm(const uint16_t* x, const uint8_t* w, const uint16_t* s, ui
   if (x == nullptr || w == nullptr || s == nullptr || y == nullptr) return W4A16_ERR_NULL;
   if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(y)) return W4A16_ERR_ALIGN;
   Plan p;
-  st = make_plan(M, N, K, split_k, cfg, &p);
+  st = make_plan(M, N, K, split_k, cfg, group_size, &p);
   if (st != W4A16_OK) return st;
   if (p.ws_split > kMaxBytes) return W4A16_ERR_SHAPE;
   const uint64_t need = plan_bytes(p);
@@ -349,10 +365,10 @@ w4a16_status run_gemm(const uint16_t* x, const uint8_t* w, const uint16_t* s, ui
       break;
     }
     case kPathTile: {
-      e = w4a16::launch_rowsum_neg136(x, ws_sx, iM, iK, (int)p.ld, strm);
+      e = w4a16::launch_rowsum_neg136(x, ws_sx, iM, iK, (int)p.ld, group_size, strm);
       if (e == hipSuccess)
         e = w4a16::launch_tile(x, w, s, ws_sx, y, ws_split, nullptr, 0, iM, iN, iK, 1, (int)p.ld, p.gps, p.sk,
-                               p.variant, strm);
+                               p.variant, group_size, strm);
       break;
     }
     default:
@@ -372,7 +388,8 @@ const char* w4a16_status_string(int status) {
     case W4A16_OK: return "W4A16_OK";
     case W4A16_ERR_NULL: return "W4A16_ERR_NULL: a required pointer is NULL";
     case W4A16_ERR_SHAPE: return "W4A16_ERR_SHAPE: invalid dimension or size limit exceeded";
-    case W4A16_ERR_GROUP_SIZE: return "W4A16_ERR_GROUP_SIZE: group_size must be 128 and divide K";
+    case W4A16_ERR_GROUP_SIZE:
+      return "W4A16_ERR_GROUP_SIZE: group_size must be 128 or 32 (32: tile path only) and K a multiple of 128";
     case W4A16_ERR_SPLIT_K: return "W4A16_ERR_SPLIT_K: split_k must be 0, 1, 2, 4, 8 or 16";
     case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE: workspace missing or too small";
     case W4A16_ERR_ALIGN: return "W4A16_ERR_ALIGN: pointers must be 16-byte aligned";
@@ -393,18 +410,23 @@ w4a16_status w4a16_pack_int4(const uint8_t* q, uint8_t* w_packed, int64_t rows, 
 int32_t w4a16_gemm_auto_split_k(int64_t M, int64_t N, int64_t K) {
   if (check_dims(M, N, K, 128) != W4A16_OK || M == 0) return 0;
   Plan p;
-  if (make_plan(M, N, K, 0, nullptr, &p) != W4A16_OK) return 0;
+  if (make_plan(M, N, K, 0, nullptr, kGroup, &p) != W4A16_OK) return 0;
   return p.sk;
 }
 
 size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t split_k) {
-  return w4a16_gemm_workspace_bytes_ex(M, N, K, split_k, nullptr);
+  return w4a16_gemm_workspace_bytes_gs(M, N, K, kGroup, split_k, nullptr);
 }
 
 size_t w4a16_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg) {
-  if (!valid_split(split_k) || check_dims(M, N, K, 128) != W4A16_OK || M == 0) return 0;
+  return w4a16_gemm_workspace_bytes_gs(M, N, K, kGroup, split_k, cfg);
+}
+
+size_t w4a16_gemm_workspace_bytes_gs(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t split_k,
+                                     const w4a16_config* cfg) {
+  if (!valid_split(split_k) || check_dims(M, N, K, group_size) != W4A16_OK || M == 0) return 0;
   Plan p;
-  if (make_plan(M, N, K, split_k, cfg, &p) != W4A16_OK) return 0;
+  if (make_plan(M, N, K, split_k, cfg, group_size, &p) != W4A16_OK) return 0;
   return (size_t)plan_bytes(p);
 }
 
@@ -421,8 +443,12 @@ w4a16_status w4a16_gemm_ex(const uint16_t* x, const uint8_t* w_packed, const uin
 }
 
 size_t w4a16_gemm_grouped_workspace_bytes(int32_t G, int64_t M_total, int64_t N, int64_t K) {
-  if (G < 1 || M_total <= 0 || check_dims(M_total, N, K, 128) != W4A16_OK) return 0;
-  return (size_t)((uint64_t)(K / kGroup) * round_up((uint64_t)M_total, 4) * 4u);
+  return w4a16_gemm_grouped_workspace_bytes_gs(G, M_total, N, K, kGroup);
+}
+
+size_t w4a16_gemm_grouped_workspace_bytes_gs(int32_t G, int64_t M_total, int64_t N, int64_t K, int32_t group_size) {
+  if (G < 1 || M_total <= 0 || check_dims(M_total, N, K, group_size) != W4A16_OK) return 0;
+  return (size_t)rowsum_bytes(M_total, K, group_size);
 }
 
 w4a16_status w4a16_gemm_grouped(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales,
@@ -440,36 +466,44 @@ w4a16_status w4a16_gemm_grouped_ex(const uint16_t* x, const uint8_t* w_packed, c
   w4a16_status st = check_dims(M_total, N, K, group_size);
   if (st != W4A16_OK) return st;
   if ((uint64_t)N * (uint64_t)K / 2u * (uint64_t)G > (uint64_t)INT64_MAX / 2) return W4A16_ERR_SHAPE;
+  // one buffer resource covers the scales of all groups
+  if ((uint64_t)G * (uint64_t)N * (uint64_t)(K / group_size) * 2u > kMaxBytes) return W4A16_ERR_SHAPE;
   if (M_total == 0) return W4A16_OK;   // empty problem: nothing to read or write
   if (x == nullptr || w_packed == nullptr || scales == nullptr || m_sizes == nullptr || y == nullptr)
     return W4A16_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_packed) || !aligned16(scales) || !aligned16(y)) return W4A16_ERR_ALIGN;
   if (((uintptr_t)m_sizes & 3u) != 0) return W4A16_ERR_ALIGN;
-  int tile_cfg = default_grouped_tile_cfg(G, M_total, N, K);
+  int tile_cfg = default_grouped_tile_cfg(G, M_total, N, K, group_size);
   if (cfg != nullptr) {
     if (cfg->path != 0 && cfg->path != kPathTile) return W4A16_ERR_SHAPE;
     if (cfg->variant >= 0) tile_cfg = cfg->variant;
     if (tile_cfg >= w4a16::tile_num_cfgs()) return W4A16_ERR_SHAPE;
   }
-  const uint64_t need = w4a16_gemm_grouped_workspace_bytes(G, M_total, N, K);
+  if (!w4a16::tile_group_ok(tile_cfg, group_size)) return W4A16_ERR_GROUP_SIZE;
+  const uint64_t need = rowsum_bytes(M_total, K, group_size);
   if (workspace == nullptr) return W4A16_ERR_WORKSPACE;
   if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
   if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
   const int ld = (int)round_up((uint64_t)M_total, 4);
   const int Gk = (int)(K / kGroup);
-  hipError_t e = w4a16::launch_rowsum_neg136(x, workspace, (int)M_total, (int)K, ld, strm);
+  hipError_t e = w4a16::launch_rowsum_neg136(x, workspace, (int)M_total, (int)K, ld, group_size, strm);
   if (e != hipSuccess) return W4A16_ERR_LAUNCH;
   return launched(w4a16::launch_tile(x, w_packed, scales, workspace, y, nullptr, m_sizes, 0, (int)M_total, (int)N,
-                                     (int)K, G, ld, Gk, 1, tile_cfg, strm));
+                                     (int)K, G, ld, Gk, 1, tile_cfg, group_size, strm));
+}
+
+size_t w4a16_gemm_batched_workspace_bytes_gs(int32_t B, int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                             int32_t split_k, const w4a16_config* cfg) {
+  if (!valid_split(split_k) || check_batched(B, M, N, K, group_size) != W4A16_OK || M == 0) return 0;
+  BatchedPlan p;
+  if (make_batched_plan(B, M, N, K, split_k, cfg, group_size, &p) != W4A16_OK) return 0;
+  return (size_t)(round_up(p.ws_split, 256) + p.ws_sx);
 }
 
 size_t w4a16_gemm_batched_workspace_bytes_ex(int32_t B, int64_t M, int64_t N, int64_t K, int32_t split_k,
                                              const w4a16_config* cfg) {
-  if (!valid_split(split_k) || check_batched(B, M, N, K, 128) != W4A16_OK || M == 0) return 0;
-  BatchedPlan p;
-  if (make_batched_plan(B, M, N, K, split_k, cfg, &p) != W4A16_OK) return 0;
-  return (size_t)(round_up(p.ws_split, 256) + p.ws_sx);
+  return w4a16_gemm_batched_workspace_bytes_gs(B, M, N, K, kGroup, split_k, cfg);
 }
 
 size_t w4a16_gemm_batched_workspace_bytes(int32_t B, int64_t M, int64_t N, int64_t K, int32_t split_k) {
@@ -486,7 +520,7 @@ w4a16_status w4a16_gemm_batched_ex(const uint16_t* x, const uint8_t* w_packed, c
   if (x == nullptr || w_packed == nullptr || scales == nullptr || y == nullptr) return W4A16_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_packed) || !aligned16(scales) || !aligned16(y)) return W4A16_ERR_ALIGN;
   BatchedPlan p;
-  st = make_batched_plan(B, M, N, K, split_k, cfg, &p);
+  st = make_batched_plan(B, M, N, K, split_k, cfg, group_size, &p);
   if (st != W4A16_OK) return st;
   if (p.ws_split > kMaxBytes) return W4A16_ERR_SHAPE;
   const uint64_t need = round_up(p.ws_split, 256) + p.ws_sx;
@@ -497,10 +531,10 @@ w4a16_status w4a16_gemm_batched_ex(const uint16_t* x, const uint8_t* w_packed, c
   float* ws_split = p.sk > 1 ? workspace : nullptr;
   float* ws_sx = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + round_up(p.ws_split, 256));
   const int Mt = (int)((int64_t)B * M);
-  hipError_t e = w4a16::launch_rowsum_neg136(x, ws_sx, Mt, (int)K, (int)p.ld, strm);
+  hipError_t e = w4a16::launch_rowsum_neg136(x, ws_sx, Mt, (int)K, (int)p.ld, group_size, strm);
   if (e != hipSuccess) return W4A16_ERR_LAUNCH;
   e = w4a16::launch_tile(x, w_packed, scales, ws_sx, y, ws_split, nullptr, (int)M, Mt, (int)N, (int)K, B, (int)p.ld,
-                         p.gps, p.sk, p.cfg, strm);
+                         p.gps, p.sk, p.cfg, group_size, strm);
   if (e != hipSuccess) return W4A16_ERR_LAUNCH;
   if (p.sk > 1) return launched(w4a16::launch_splitk_reduce(ws_split, y, (uint64_t)Mt * (uint64_t)N, p.sk, strm));
   return W4A16_OK;

@@ -41,6 +41,9 @@ __device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 __device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
+__device__ __forceinline__ u32x2 ld64(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+}
 __device__ __forceinline__ uint16_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }

@@ -29,23 +29,28 @@ hipError_t launch_skinny_stream(const uint16_t* x, const uint8_t* w, const uint1
                                 int M, int N, int K, int gps, int sk, int nt, int depth, int waves, int gb,
                                 hipStream_t stream);
 
-// out[g * ld + m] = -136 * sum_{k in group g} x[m, k]
-hipError_t launch_rowsum_neg136(const uint16_t* x, float* out, int M, int K, int ld, hipStream_t stream);
+// out[g * ld + m] = -136 * sum_{k in group g} x[m, k], groups of gsize = 128 or 32 k
+hipError_t launch_rowsum_neg136(const uint16_t* x, float* out, int M, int K, int ld, int gsize,
+                                hipStream_t stream);
 
-// Tile GEMM: plain (m_sizes == nullptr, m_uniform == 0, G == 1), grouped
-// (rows per weight group in m_sizes on the device) or batched (G weight groups
-// of m_uniform rows each). With ws != nullptr (plain and batched) slice s of
+// Tile GEMM (scale groups of gsize = 128 or, where tile_group_ok, 32 k):
+// plain (m_sizes == nullptr, m_uniform == 0, G == 1), grouped (rows per
+// weight group in m_sizes on the device) or batched (G weight groups of
+// m_uniform rows each). With ws != nullptr (plain and batched) slice s of
 // gridDim.y = sk writes fp32 partials ws[s, :, :].
 hipError_t launch_tile(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
                        float* ws, const int32_t* m_sizes, int m_uniform, int M_total, int N, int K, int G, int ld,
-                       int gps, int sk, int cfg, hipStream_t stream);
+                       int gps, int sk, int cfg, int gsize, hipStream_t stream);
 // LDS-DMA tile kernel: (16 row_tiles) x 256 output tiles (row_tiles = 5 .. 9);
 // same contract as launch_tile.
 hipError_t launch_prefill(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
                           float* ws, const int32_t* m_sizes, int m_uniform, int M_total, int N, int K, int G,
-                          int ld, int gps, int sk, int row_tiles, hipStream_t stream);
+                          int ld, int gps, int sk, int row_tiles, int gsize, hipStream_t stream);
 int tile_bm(int cfg);
 int tile_bn(int cfg);
+// whether configuration cfg runs scale groups of gsize k (128: all; 32: the
+// LDS-DMA configurations of at most 128 rows)
+bool tile_group_ok(int cfg, int gsize);
 int tile_num_cfgs();
 
 }  // namespace w4a16

@@ -31,6 +31,8 @@
 //  * one barrier per group, after an explicit wait for the next group's DMA.
 // The M tail and N tail read zeros through the exact buffer extents; stores
 // past the last row are dropped and columns >= N are skipped.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "tilemap.hpp"
@@ -43,21 +45,22 @@ constexpr int kPN = 256;                    // columns per tile (8 waves x 32)
 constexpr int kNW = 8;                      // waves per workgroup
 constexpr int kWStage = kPN * 64;           // packed W: 256 rows x 128 k / 2
 
-// LDS stage of a tile with MS row tiles of 16: X, packed W, row sums
-template <int MS>
+// LDS stage of a tile with MS row tiles of 16 (one 128-k stage): X, packed
+// W, the row sums of its 128 / GS scale groups
+template <int MS, int GS = 128>
 struct Stage {
   static constexpr int kRows = 16 * MS;
   static constexpr int kX = kRows * 256;     // X: rows x 128 k x 2 B
   static constexpr int kW = kWStage;
-  static constexpr int kR = kRows * 4;       // -136 * row sums, fp32
+  static constexpr int kR = kRows * 4 * (128 / GS);   // -136 * row sums, fp32, [128 / GS][rows]
   static constexpr int kBytes = kX + kW + kR;
 };
 
 struct PrefillArgs {
   const uint16_t* x;       // [M_total, K]
   const uint8_t* w;        // [G, N, K/2]
-  const uint16_t* s;       // [G, N, K/128]
-  const float* sxn;        // [K/128, ld]
+  const uint16_t* s;       // [G, N, K/GS]
+  const float* sxn;        // [K/GS, ld]
   uint16_t* y;             // [M_total, N]
   float* ws;               // [SK, M_total, N] fp32 split-K partials, or nullptr
   const int32_t* m_sizes;  // [G] on device, or nullptr
@@ -82,11 +85,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst
 
 }  // namespace
 
-template <int NSTAGE, int MS>
+template <int NSTAGE, int MS, int GS>
 __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs args) {
   static_assert(NSTAGE == 2 || NSTAGE == 3, "stages");
   static_assert(MS >= 2 && MS <= 16, "row tiles");
-  using ST = Stage<MS>;
+  static_assert(GS == 128 || GS == 32, "scale group");
+  constexpr int NSG = 128 / GS;         // scale groups per 128-k stage
+  using ST = Stage<MS, GS>;
   constexpr int BM = ST::kRows;
   constexpr int TN = kPN / kNW;         // columns per wave (32)
   constexpr int SN = TN / 16;           // 16-column MFMA tiles per wave (2)
@@ -99,7 +104,8 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int Gk = args.K / kGroup;
+  const int Gk = args.K / kGroup;       // 128-k stages
+  const int Gs = args.K / GS;           // scale groups
 
   int mt, nt;
   int MT = args.mtiles, nblocks = (int)gridDim.x;
@@ -123,9 +129,9 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   // scales: the whole tensor (word-aligned reads, see make_scale_rsrc); columns
   // past N read other scales or zeros and are never stored
   const __amdgpu_buffer_rsrc_t rs =
-      make_scale_rsrc(args.s, (uint32_t)((size_t)args.G * args.N * Gk));
+      make_scale_rsrc(args.s, (uint32_t)((size_t)args.G * args.N * Gs));
   const __amdgpu_buffer_rsrc_t rsx =
-      make_rsrc(args.sxn + row0, (uint32_t)(((size_t)Gk * args.ld - row0) * 4u));
+      make_rsrc(args.sxn + row0, (uint32_t)(((size_t)Gs * args.ld - row0) * 4u));
   const int slice = blockIdx.y;
   const int gb = slice * args.gps;
   const int ge = min(Gk, gb + args.gps);
@@ -170,23 +176,36 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     const uint32_t wo = wvo();
 #pragma unroll
     for (int i = 0; i < QW; ++i) dma16(rw, base + ST::kX + 1024 * (QW * wv + i), wo + (uint32_t)i * 16u * K2, gw);
-    if (wv == 0 && lane < RL)
-      dma16(rsx, base + ST::kX + ST::kW, rvo() + (uint32_t)g * (uint32_t)args.ld * 4u, 0u);
+    // wave sg < NSG fetches the row sums of scale group sg of the stage
+    if (wv < NSG && lane < RL)
+      dma16(rsx, base + ST::kX + ST::kW + ST::kRows * 4 * wv,
+            rvo() + (uint32_t)(NSG * g + wv) * (uint32_t)args.ld * 4u, 0u);
   };
 
-  // ---- scales: the aligned word holding s[n][g] for this lane's SN columns
+  // ---- scales: GS = 128: the aligned word holding s[n][g] for this lane's
+  // SN columns; GS = 32: the stage's four scales s[n][4 g .. 4 g + 3], one
+  // 8-byte load (aligned: K / 32 is a multiple of 4)
   const int m16 = lane & 15, kb = lane >> 4;
+  using SW = typename std::conditional<GS == 128, uint32_t, u32x2>::type;
   uint32_t soff[SN];
 #pragma unroll
   for (int ns = 0; ns < SN; ++ns)
-    soff[ns] = (uint32_t)((size_t)tr.wg * args.N + n0 + TN * wv + 16 * ns + m16) * (uint32_t)Gk * 2u;
-  auto load_scales = [&](uint32_t (&sw)[SN], int g) {
+    soff[ns] = (uint32_t)((size_t)tr.wg * args.N + n0 + TN * wv + 16 * ns + m16) * (uint32_t)Gs * 2u;
+  auto load_scales = [&](SW (&sw)[SN], int g) {
 #pragma unroll
-    for (int ns = 0; ns < SN; ++ns) sw[ns] = ld32(rs, (soff[ns] + 2u * (uint32_t)g) & ~3u);
+    for (int ns = 0; ns < SN; ++ns) {
+      if constexpr (GS == 128) sw[ns] = ld32(rs, (soff[ns] + 2u * (uint32_t)g) & ~3u);
+      else sw[ns] = ld64(rs, soff[ns] + 8u * (uint32_t)g);
+    }
   };
   auto scale_of = [&](uint32_t word, int ns, int g) {
     const uint32_t o = soff[ns] + 2u * (uint32_t)g;
     return __uint_as_float((o & 2u) ? (word & 0xFFFF0000u) : (word << 16));
+  };
+  // scale group st (0..3) of a stage's four, GS = 32
+  auto scale32 = [](u32x2 w, int st) {
+    const uint32_t v = st < 2 ? w.x : w.y;
+    return __uint_as_float((st & 1) ? (v & 0xFFFF0000u) : (v << 16));
   };
 
   // ---- LDS operand offsets within a stage
@@ -207,9 +226,83 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
 #pragma unroll
     for (int ns = 0; ns < SN; ++ns) acc[ms][ns] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  uint32_t sc_cur[SN], sc_nxt[SN];
+  SW sc_cur[SN], sc_nxt[SN];
+
+  // GS = 32: MFMA step st covers scale group st of the stage (natural k
+  // order: lane (r, kb) of step st holds k = 32 st + 8 kb + 0..7 for both
+  // operands), each step starts from its group's row sums and is rescaled on
+  // its own. A: chunk 4 st + kb of the row, slot (4 st + kb) ^ (row & 7) =
+  // ((kb ^ (row & 7)) ^ 4 st); B: dword kb of chunk st of the packed row, slot
+  // st ^ ((row >> 1) & 3).
+  const uint32_t aoffN = (uint32_t)m16 * 256u + 16u * (uint32_t)(kb ^ (m16 & 7));
+  const uint32_t boffN = ST::kX + (uint32_t)(TN * wv + m16) * 64u + 4u * (uint32_t)kb + 16u * (uint32_t)((m16 >> 1) & 3);
+  auto compute32 = [&](int stage) {
+    if constexpr (GS == 32) {
+    const uint8_t* sb = lds + stage * ST::kBytes;
+    bf16x8 aq[2][4];
+    auto read_a = [&](int ms, bf16x8 (&a)[4]) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        a[st] = *reinterpret_cast<const bf16x8*>(sb + (aoffN ^ (64u * (uint32_t)st)) + 4096u * (uint32_t)ms);
+    };
+    read_a(0, aq[0]);
+    bf16x8 bd[SN][4];
+#pragma unroll
+    for (int ns = 0; ns < SN; ++ns)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const uint32_t w0 = *reinterpret_cast<const uint32_t*>(sb + (boffN ^ (16u * (uint32_t)st)) + 1024u * (uint32_t)ns);
+        const uint32_t w4 = w0 >> 4;
+        u32x4 o;
+        o.x = and_or_sv(__builtin_amdgcn_perm(w4, w0, 0x0C040C00u), mask, magic);
+        o.y = and_or_sv(__builtin_amdgcn_perm(w4, w0, 0x0C050C01u), mask, magic);
+        o.z = and_or_sv(__builtin_amdgcn_perm(w4, w0, 0x0C060C02u), mask, magic);
+        o.w = and_or_sv(__builtin_amdgcn_perm(w4, w0, 0x0C070C03u), mask, magic);
+        bd[ns][st] = __builtin_bit_cast(bf16x8, o);
+      }
+    float scv[SN][4];
+#pragma unroll
+    for (int ns = 0; ns < SN; ++ns)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) scv[ns][st] = scale32(sc_cur[ns], st);
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const int cur = ms & 1;
+      // this row tile's four initial C (row sums of the stage's 4 groups)
+      f32x4 cq[NSG];
+#pragma unroll
+      for (int st = 0; st < NSG; ++st)
+        cq[st] = *reinterpret_cast<const f32x4*>(sb + roff + (uint32_t)(ST::kRows * 4 * st) + 64u * (uint32_t)ms);
+      if (ms + 1 < MS) read_a(ms + 1, aq[(ms + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      // step st's products are rescaled after step st + 1's MFMAs are issued
+      // (the MFMA result is not read right behind its issue); the empty asm
+      // pins each rescale there, otherwise all 4 steps' products stay live
+      f32x4 t[2][SN];
+      auto rescale = [&](const f32x4 (&u)[SN], int st) {
+#pragma unroll
+        for (int ns = 0; ns < SN; ++ns) {
+          acc[ms][ns].x = fmaf(scv[ns][st], u[ns].x, acc[ms][ns].x);
+          acc[ms][ns].y = fmaf(scv[ns][st], u[ns].y, acc[ms][ns].y);
+          acc[ms][ns].z = fmaf(scv[ns][st], u[ns].z, acc[ms][ns].z);
+          acc[ms][ns].w = fmaf(scv[ns][st], u[ns].w, acc[ms][ns].w);
+          asm volatile("" : "+v"(acc[ms][ns]));
+        }
+      };
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int ns = 0; ns < SN; ++ns)
+          t[st & 1][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[cur][st], bd[ns][st], cq[st], 0, 0, 0);
+        if (st > 0) rescale(t[(st - 1) & 1], st - 1);
+      }
+      rescale(t[1], 3);
+    }
+    }
+  };
 
   auto compute = [&](int stage, int g) {
+    if constexpr (GS == 128) {
     const uint8_t* sb = lds + stage * ST::kBytes;
     // row tile ms's operands: initial C and the 4 steps' A fragments; the next
     // row tile's reads go out before this tile's MFMAs (two register sets)
@@ -264,6 +357,7 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
         acc[ms][ns].w = fmaf(scv[ns], t[ns].w, acc[ms][ns].w);
       }
     }
+      }
   };
 
   // ---- pipeline: group j + NSTAGE - 1 is loaded while group j is computed.
@@ -284,7 +378,8 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     const bool ahead = j + NSTAGE - 1 < ng;
     if (ahead) issue(g + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
     if (j + 1 < ng) load_scales(sc_nxt, g + 1);
-    compute(j % NSTAGE, g);
+    if constexpr (GS == 128) compute(j % NSTAGE, g);
+    else compute32(j % NSTAGE);
     if (j + 1 < ng) {
       wait_vm_barrier<0>();
 #pragma unroll
@@ -327,13 +422,13 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   }
 }
 
-template <int NSTAGE, int MS>
+template <int NSTAGE, int MS, int GS = 128>
 static hipError_t launch_prefill_t(PrefillArgs a, int sk, hipStream_t stream) {
-  constexpr int BM = Stage<MS>::kRows;
-  const int lds_bytes = NSTAGE * Stage<MS>::kBytes;
+  constexpr int BM = Stage<MS, GS>::kRows;
+  const int lds_bytes = NSTAGE * Stage<MS, GS>::kBytes;
   static bool attr_set = false;   // per instantiation; the attribute is per function
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NSTAGE, MS>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NSTAGE, MS, GS>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -344,17 +439,29 @@ static hipError_t launch_prefill_t(PrefillArgs a, int sk, hipStream_t stream) {
   const long long blocks = (long long)a.mtiles * a.ntiles;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<NSTAGE, MS>), dim3((unsigned)blocks, sk), dim3(64 * kNW), lds_bytes, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<NSTAGE, MS, GS>), dim3((unsigned)blocks, sk), dim3(64 * kNW), lds_bytes, stream,
+                     a);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
                           float* ws, const int32_t* m_sizes, int m_uniform, int M_total, int N, int K, int G,
-                          int ld, int gps, int sk, int row_tiles, hipStream_t stream) {
+                          int ld, int gps, int sk, int row_tiles, int gsize, hipStream_t stream) {
   PrefillArgs a;
   a.x = x; a.w = w; a.s = s; a.sxn = sxn; a.y = y; a.ws = ws; a.m_sizes = m_sizes; a.m_uniform = m_uniform;
   a.M_total = M_total; a.N = N; a.K = K; a.G = G; a.ld = ld; a.gps = gps;
   a.mtiles = 0; a.ntiles = 0;
+  if (gsize == 32) {
+    // four row-sum sets per stage: 144-row tiles would not fit 3 stages in LDS
+    switch (row_tiles) {
+      case 8: return launch_prefill_t<3, 8, 32>(a, sk, stream);   // 3 x 50 KiB stages
+      case 7: return launch_prefill_t<3, 7, 32>(a, sk, stream);
+      case 6: return launch_prefill_t<3, 6, 32>(a, sk, stream);
+      case 5: return launch_prefill_t<3, 5, 32>(a, sk, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (gsize != 128) return hipErrorInvalidValue;
   switch (row_tiles) {
     case 9: return launch_prefill_t<3, 9>(a, sk, stream);     // 144 x 256 tiles, 3 x 52.6 KiB stages
     case 8: return launch_prefill_t<3, 8>(a, sk, stream);     // 128 x 256 tiles, 3 x 48.5 KiB stages

@@ -32,14 +32,17 @@
 namespace w4a16 {
 
 // ---------------------------------------------------------------- row sums
-// out[g * ld + m] = -136 * sum_{k in group g} x[m, k], fp32. One wave per
-// row; a wave instruction covers 512 consecutive k (4 groups) and up to 8 of
-// them are in flight before any is reduced; a group's 16 lanes are summed
-// with DPP row sums. Loads past the row read zeros (exact buffer extent).
+// out[g * ld + m] = -136 * sum_{k in group g} x[m, k], fp32, for groups of GS
+// = 128 or 32 k. One wave per row; a wave instruction covers 512 consecutive
+// k and up to 8 of them are in flight before any is reduced; a group's lanes
+// (16 for 128 k, 4 for 32 k) are summed with DPP. Loads past the row read
+// zeros (exact buffer extent).
+template <int GS>
 __global__ __launch_bounds__(256) void rowsum_neg136_kernel(const uint16_t* __restrict__ x,
                                                            float* __restrict__ out, int M, int K,
                                                            int ld) {
   constexpr int U = 8;
+  constexpr int LPG = GS / 8;   // lanes per group
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
@@ -53,8 +56,13 @@ __global__ __launch_bounds__(256) void rowsum_neg136_kernel(const uint16_t* __re
       const int k = base + 512 * u + 8 * lane;
       float p = (bf16lo(v[u].x) + bf16hi(v[u].x)) + (bf16lo(v[u].y) + bf16hi(v[u].y)) +
                 (bf16lo(v[u].z) + bf16hi(v[u].z)) + (bf16lo(v[u].w) + bf16hi(v[u].w));
-      p = row16_sum(p);
-      if ((lane & 15) == 0 && k < K) out[(size_t)(k / kGroup) * ld + m] = -136.0f * p;
+      if constexpr (LPG == 16) {
+        p = row16_sum(p);
+      } else {
+        p += dpp_f<0xB1>(p);   // quad_perm [1,0,3,2]
+        p += dpp_f<0x4E>(p);   // quad_perm [2,3,0,1]
+      }
+      if ((lane & (LPG - 1)) == 0 && k < K) out[(size_t)(k / GS) * ld + m] = -136.0f * p;
     }
   }
 }
@@ -299,9 +307,15 @@ __global__ __launch_bounds__(64 * WM * WN) void tile_kernel(const TileArgs args)
   }
 }
 
-hipError_t launch_rowsum_neg136(const uint16_t* x, float* out, int M, int K, int ld, hipStream_t stream) {
+hipError_t launch_rowsum_neg136(const uint16_t* x, float* out, int M, int K, int ld, int gsize,
+                                hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rowsum_neg136_kernel, dim3((M + 3) / 4), dim3(256), 0, stream, x, out, M, K, ld);
+  if (gsize == 128)
+    hipLaunchKernelGGL(rowsum_neg136_kernel<128>, dim3((M + 3) / 4), dim3(256), 0, stream, x, out, M, K, ld);
+  else if (gsize == 32)
+    hipLaunchKernelGGL(rowsum_neg136_kernel<32>, dim3((M + 3) / 4), dim3(256), 0, stream, x, out, M, K, ld);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -326,14 +340,19 @@ static const TileCfg kTileCfgs[] = {{128, 256}, {128, 128}, {128, 256}, {96, 256
 int tile_num_cfgs() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0])); }
 int tile_bm(int cfg) { return kTileCfgs[cfg].bm; }
 int tile_bn(int cfg) { return kTileCfgs[cfg].bn; }
+bool tile_group_ok(int cfg, int gsize) {
+  if (cfg < 0 || cfg >= tile_num_cfgs()) return false;
+  return gsize == 128 || (gsize == 32 && cfg >= 2 && kTileCfgs[cfg].bm <= 128);
+}
 
 hipError_t launch_tile(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
                        float* ws, const int32_t* m_sizes, int m_uniform, int M_total, int N, int K, int G, int ld,
-                       int gps, int sk, int cfg, hipStream_t stream) {
+                       int gps, int sk, int cfg, int gsize, hipStream_t stream) {
   if (cfg < 0 || cfg >= tile_num_cfgs()) return hipErrorInvalidValue;
   if (cfg >= 2)   // LDS-DMA kernel: 8 (cfg 2), 6 (cfg 3), 7 (cfg 4), 5 (cfg 5) or 9 (cfg 6) row tiles of 16
     return launch_prefill(x, w, s, sxn, y, ws, m_sizes, m_uniform, M_total, N, K, G, ld, gps, sk,
-                          kTileCfgs[cfg].bm / 16, stream);
+                          kTileCfgs[cfg].bm / 16, gsize, stream);
+  if (gsize != 128) return hipErrorInvalidValue;   // configs 0 and 1: 128-groups only
   TileArgs a;
   a.x = x; a.w = w; a.s = s; a.sxn = sxn; a.y = y; a.ws = ws; a.m_sizes = m_sizes; a.m_uniform = m_uniform;
   a.M_total = M_total; a.N = N; a.K = K; a.G = G; a.ld = ld; a.gps = gps;

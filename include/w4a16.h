@@ -1,11 +1,12 @@
 /*
  * w4a16.h -- C ABI of a W4A16 GEMM library for AMD Instinct MI355X (gfx950).
  *
- *   Y[M,N] = X[M,K] . dequant(W)[N,K]^T,   dequant(W)[n,k] = S[n, k/128] * (q[n,k] - 8)
+ *   Y[M,N] = X[M,K] . dequant(W)[N,K]^T,   dequant(W)[n,k] = S[n, k/g] * (q[n,k] - 8)
  *
  * X and Y are bf16, W is packed unsigned int4 (two nibbles per byte), S holds
- * one bf16 scale per output row per 128-wide K group, accumulation is fp32 and
- * the output is rounded to bf16 (round to nearest even).
+ * one bf16 scale per output row per g-wide K group (group_size g = 128, or 32
+ * on the tile kernel), accumulation is fp32 and the output is rounded to bf16
+ * (round to nearest even).
  *
  * Sources for the operation (pages by title, section in quotes):
  *  - "Add Triton BF16xINT4 rowwise GEMM for ROCm gfx942/gfx950": Summary (bf16
@@ -18,7 +19,8 @@
  *  - "[ROCm][Kernel] W4A16 skinny GEMM: hand-asm kernel for gfx1151": section 1
  *    "Magic-constant bf16 dequant" (a nibble decodes as scale * (n - 8),
  *    symmetric), section 3 "Exact buffer-descriptor sizing" (weight and scale
- *    buffers bounded by their exact byte sizes).
+ *    buffers bounded by their exact byte sizes), "Benchmark results
+ *    (per-GEMM)" (the decoder GEMMs quantised with one scale per 32 k).
  *
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers to caller-owned, contiguous, row-major
@@ -52,7 +54,8 @@ typedef enum {
   W4A16_ERR_NULL = 1,        /* a required pointer is NULL                       */
   W4A16_ERR_SHAPE = 2,       /* a dimension is negative, zero where not allowed,
                                 odd K, or a size limit is exceeded               */
-  W4A16_ERR_GROUP_SIZE = 3,  /* group_size != 128 or K % group_size != 0         */
+  W4A16_ERR_GROUP_SIZE = 3,  /* group_size not 128 or 32, K % 128 != 0, or group
+                                size 32 with a kernel that takes 128 only        */
   W4A16_ERR_SPLIT_K = 4,     /* split_k not in {0, 1, 2, 4, 8, 16}               */
   W4A16_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required          */
   W4A16_ERR_ALIGN = 6,       /* a tensor pointer is not 16-byte aligned          */
@@ -77,8 +80,8 @@ w4a16_status w4a16_pack_int4(const uint8_t* q, uint8_t* w_packed,
                              int64_t rows, int64_t K, void* stream);
 
 /*
- * The split-K factor the library uses for w4a16_gemm when split_k == 0
- * (auto) at this shape: for the M = 1 GEMV only what its register budget for
+ * The split-K factor the library uses for w4a16_gemm with group_size 128
+ * when split_k == 0 (auto) at this shape: for the M = 1 GEMV only what its register budget for
  * x needs (at most 64 groups per slice), for the M <= 16 kernel enough slices
  * for one workgroup per compute unit, and for the tile kernel the power of
  * two (at most 16) of least estimated time among those that keep tiles x SK
@@ -90,11 +93,12 @@ w4a16_status w4a16_pack_int4(const uint8_t* q, uint8_t* w_packed,
 int32_t w4a16_gemm_auto_split_k(int64_t M, int64_t N, int64_t K);
 
 /*
- * Bytes of workspace w4a16_gemm needs at this shape and split_k (0 = auto):
- * SK * M * N * 4 (rounded up to 256) when the effective split factor SK > 1,
- * plus, when M > 16 (the tile kernel), (K/128) * round_up(M, 4) * 4 for the
- * per-row group sums of X. Returns 0 when none is needed and for invalid
- * arguments.
+ * Bytes of workspace w4a16_gemm needs at this shape and split_k (0 = auto)
+ * with group_size 128: SK * M * N * 4 (rounded up to 256) when the effective
+ * split factor SK > 1, plus, when M > 16 (the tile kernel), (K/128) *
+ * round_up(M, 4) * 4 for the per-row group sums of X. Returns 0 when none is
+ * needed and for invalid arguments. w4a16_gemm_workspace_bytes_gs gives it
+ * for either group size.
  */
 size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K,
                                   int32_t split_k);
@@ -108,17 +112,20 @@ size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K,
  *   y         : [M, N] bf16, device, written (bf16 round-to-nearest-even of
  *               the fp32 accumulator)
  *   M >= 0 (M == 0: returns W4A16_OK, nothing enqueued), N >= 1, K >= 128.
- *   group_size: must be 128; K % 128 == 0.
- *   split_k   : 0 = auto, or 1, 2, 4, 8, 16. With SK > 1 the K groups are cut
- *               into SK contiguous slices of ceil((K/128)/SK) groups (trailing
- *               slices may be empty); slice s writes its fp32 partial sums to
+ *   group_size: 128, or 32; K % 128 == 0 either way. Group size 32 always
+ *               runs the tile kernel (path 3, configurations 2 to 5), at any
+ *               M: the M = 1 and M <= 16 kernels take 128-groups only.
+ *   split_k   : 0 = auto, or 1, 2, 4, 8, 16. With SK > 1 the K range is cut
+ *               into SK contiguous slices of ceil((K/128)/SK) blocks of 128 k
+ *               (trailing slices may be empty); slice s writes its fp32 partial sums to
  *               workspace[s, :, :] with plain stores (an empty slice writes
  *               zeros) and a second kernel sums the slices in order
  *               s = 0..SK-1 in fp32 and rounds once to bf16.
  *   workspace : fp32 device scratch, overwritten; may be NULL when
- *               w4a16_gemm_workspace_bytes is 0. With SK > 1 its first
+ *               w4a16_gemm_workspace_bytes_gs is 0. With SK > 1 its first
  *               SK * M * N floats hold the [SK, M, N] partials after the call.
- *   workspace_bytes: its size in bytes (>= w4a16_gemm_workspace_bytes).
+ *   workspace_bytes: its size in bytes (>= w4a16_gemm_workspace_bytes_gs for
+ *               this group_size).
  * Rows of Y are written exactly once; no atomics are used, so the result is
  * bitwise reproducible for a given shape and split_k.
  */
@@ -129,9 +136,10 @@ w4a16_status w4a16_gemm(const uint16_t* x, const uint8_t* w_packed,
                         size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of workspace w4a16_gemm_grouped needs: (K/128) * round_up(M_total, 4)
- * * 4 (one fp32 row sum per row and 128-group). Returns 0 for invalid
- * arguments or M_total == 0.
+ * Bytes of workspace w4a16_gemm_grouped needs with group_size 128: (K/128) *
+ * round_up(M_total, 4) * 4 (one fp32 row sum per row and 128-group). Returns
+ * 0 for invalid arguments or M_total == 0. w4a16_gemm_grouped_workspace_bytes_gs
+ * gives it for either group size.
  */
 size_t w4a16_gemm_grouped_workspace_bytes(int32_t G, int64_t M_total, int64_t N, int64_t K);
 
@@ -152,9 +160,10 @@ size_t w4a16_gemm_grouped_workspace_bytes(int32_t G, int64_t M_total, int64_t N,
  *               m_sizes[g] == 0 contributes nothing.
  *   y         : [M_total, N] bf16, device, written
  *   G >= 1, M_total >= 0 (0: W4A16_OK, nothing enqueued), N >= 1, K >= 128,
- *   group_size == 128, K % 128 == 0.
+ *   group_size 128 or 32 (tile configurations 2 to 5), K % 128 == 0; the
+ *   scales of all groups together must be smaller than 2^32 bytes.
  *   workspace : fp32 device scratch of workspace_bytes >= the value of
- *               w4a16_gemm_grouped_workspace_bytes; overwritten.
+ *               w4a16_gemm_grouped_workspace_bytes_gs; overwritten.
  * Two kernels are enqueued: a pass over X computing per-row group sums, and
  * the grouped tile kernel. The tile grid is sized from the host value
  * M_total: (ceil(M_total/BM) + G) * ceil(N/BN) workgroups; workgroups past
@@ -169,9 +178,10 @@ w4a16_status w4a16_gemm_grouped(const uint16_t* x, const uint8_t* w_packed,
 
 /*
  * Bytes of workspace w4a16_gemm_batched needs at this shape and split_k (0 =
- * auto): SK * B * M * N * 4 (rounded up to 256) when the effective split
- * factor SK > 1, plus (K/128) * round_up(B * M, 4) * 4 for the per-row group
- * sums of X. Returns 0 for invalid arguments or M == 0.
+ * auto) with group_size 128: SK * B * M * N * 4 (rounded up to 256) when the
+ * effective split factor SK > 1, plus (K/128) * round_up(B * M, 4) * 4 for
+ * the per-row group sums of X. Returns 0 for invalid arguments or M == 0.
+ * w4a16_gemm_batched_workspace_bytes_gs gives it for either group size.
  */
 size_t w4a16_gemm_batched_workspace_bytes(int32_t B, int64_t M, int64_t N, int64_t K,
                                           int32_t split_k);
@@ -186,13 +196,14 @@ size_t w4a16_gemm_batched_workspace_bytes(int32_t B, int64_t M, int64_t N, int64
  *   scales    : [B, N, K/group_size] bf16, device
  *   y         : [B, M, N] bf16, device, written
  *   B >= 1, M >= 0 (0: W4A16_OK, nothing enqueued), B * M < 2^31, N >= 1,
- *   K >= 128, group_size == 128, K % 128 == 0; the scales of all B problems
- *   together must be smaller than 2^32 bytes.
+ *   K >= 128, group_size 128 or 32 (tile configurations 2 to 5), K % 128 ==
+ *   0; the scales of all B problems together must be smaller than 2^32
+ *   bytes.
  *   split_k   : 0 (auto: the tile height and split chosen together, as for
  *               w4a16_gemm with B x ceil(M/h) row tiles per column) or 1, 2,
  *               4, 8, 16.
  *   workspace : fp32 device scratch of workspace_bytes >= the value of
- *               w4a16_gemm_batched_workspace_bytes; overwritten.
+ *               w4a16_gemm_batched_workspace_bytes_gs; overwritten.
  * Enqueues the per-row group sums of X, the tile kernel (weight group b =
  * problem b, its rows at b * M), and for SK > 1 the split-K reduce. Every
  * row of Y is written exactly once, no atomics: bitwise reproducible for a
@@ -254,13 +265,15 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  *            configuration index (0: 128x256 and 1: 128x128 with weights
  *            dequantised into LDS; 2: 128x256 with LDS-DMA staging, 8
  *            waves, 3 LDS stages; 3, 4, 5, 6: the same with 96x256,
- *            112x256, 80x256 and 144x256 tiles). By default the call picks
- *            among 2 to 6 the tile height with the fewest rounds of one
+ *            112x256, 80x256 and 144x256 tiles; group_size 32 runs on 2 to
+ *            5 only, W4A16_ERR_GROUP_SIZE otherwise). By default the call
+ *            picks among 2 to 6 (2 to 5 for group_size 32) the tile height with the fewest rounds of one
  *            workgroup per compute unit times rows per tile, weighted by
  *            each height's measured per-row rate (the grouped call
  *            estimates ceil(M_total/h) + G/2 row tiles per column).
  * An unavailable combination (e.g. path 1 with M != 1, path 2 with M > 16)
- * returns W4A16_ERR_SHAPE.
+ * returns W4A16_ERR_SHAPE; path 1 or 2 with group_size 32 returns
+ * W4A16_ERR_GROUP_SIZE.
  */
 typedef struct {
   int32_t path;
@@ -290,6 +303,21 @@ w4a16_status w4a16_gemm_grouped_ex(const uint16_t* x, const uint8_t* w_packed,
 /* w4a16_gemm_batched_workspace_bytes for an explicit tile configuration. */
 size_t w4a16_gemm_batched_workspace_bytes_ex(int32_t B, int64_t M, int64_t N, int64_t K,
                                              int32_t split_k, const w4a16_config* cfg);
+
+/*
+ * Workspace bytes for either group size (128 or 32; the functions above are
+ * these with 128). With group_size 32 the tile kernel runs at every M and its
+ * row sums take (K/32) * round_up(rows, 4) * 4 bytes. cfg NULL = automatic.
+ * Return 0 for invalid arguments (including a group size the selected kernel
+ * does not take) and when no workspace is needed.
+ */
+size_t w4a16_gemm_workspace_bytes_gs(int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                     int32_t split_k, const w4a16_config* cfg);
+size_t w4a16_gemm_grouped_workspace_bytes_gs(int32_t G, int64_t M_total, int64_t N, int64_t K,
+                                             int32_t group_size);
+size_t w4a16_gemm_batched_workspace_bytes_gs(int32_t B, int64_t M, int64_t N, int64_t K,
+                                             int32_t group_size, int32_t split_k,
+                                             const w4a16_config* cfg);
 
 /* w4a16_gemm_batched with an explicit tile configuration (path must be 0 or 3). */
 w4a16_status w4a16_gemm_batched_ex(const uint16_t* x, const uint8_t* w_packed,

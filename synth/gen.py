@@ -17,7 +17,8 @@ Recipe, per workload, with one fresh ``numpy.random.default_rng(seed)``
 3. ``q``: uniform integers 0..15 ``[N, K]`` (``[G, N, K]`` grouped), one
    unsigned nibble per byte, not packed;
 4. ``S``: uniform on [0.005, 0.02) in float64, cast to float32, rounded to
-   bf16, ``[N, K/128]`` (``[G, N, K/128]`` grouped).
+   bf16, ``[N, K/g]`` (``[G, N, K/g]`` grouped) for the group size g (128,
+   or 32 for the per-layer workloads at group 32).
 
 The float32 -> bf16 rounding of the draws is done by PyTorch's CPU
 conversion (round to nearest even), i.e. by a library routine, so this module
@@ -81,12 +82,13 @@ def make_inputs(M: int, N: int, K: int, seed: int = 0, *,
                 m_sizes: Optional[Sequence[int]] = None,
                 empty: Sequence[int] = (),
                 x_scale: float = 1.0,
-                s_range=(0.005, 0.02)) -> Inputs:
+                s_range=(0.005, 0.02),
+                group: int = GROUP) -> Inputs:
     """Draw one workload. For grouped inputs give ``G`` and either explicit
     ``m_sizes`` (then ``M`` must equal their sum) or ``M`` as ``M_total`` to
     split multinomially over the groups not listed in ``empty``."""
-    if K % GROUP:
-        raise ValueError("K must be a multiple of 128")
+    if K % GROUP or GROUP % group:
+        raise ValueError("K must be a multiple of 128 and the group size divide 128")
     rng = np.random.default_rng(seed)
     ms = None
     if G is not None:
@@ -104,9 +106,9 @@ def make_inputs(M: int, N: int, K: int, seed: int = 0, *,
         x = (x * np.float32(x_scale)).astype(np.float32)
     wshape = (N, K) if G is None else (G, N, K)
     q = rng.integers(0, 16, wshape, dtype=np.uint8)
-    s = rng.uniform(s_range[0], s_range[1], wshape[:-1] + (K // GROUP,))
+    s = rng.uniform(s_range[0], s_range[1], wshape[:-1] + (K // group,))
     return Inputs(x=_to_bf16_bits(x), q=q,
-                  s=_to_bf16_bits(s.astype(np.float32)), m_sizes=ms)
+                  s=_to_bf16_bits(s.astype(np.float32)), m_sizes=ms, group_size=group)
 
 
 def make_config(name: str, seed: int = 0) -> Inputs:

@@ -54,9 +54,9 @@ def read_golden(name):
     return rows
 
 
-def rand_case(M, N, K, seed, G=None, m_sizes=None):
+def rand_case(M, N, K, seed, G=None, m_sizes=None, group=128):
     from synth import make_inputs
-    return make_inputs(M, N, K, seed, G=G, m_sizes=m_sizes)
+    return make_inputs(M, N, K, seed, G=G, m_sizes=m_sizes, group=group)
 
 
 def bf16_scale_samples():
@@ -204,7 +204,7 @@ def pin_one_hot_rows(o):
             assert y[i, n] == want, (k, n, y[i, n], want)
 
 
-def _brute(x_bits, p, s_bits):
+def _brute(x_bits, p, s_bits, group=128):
     M, K = x_bits.shape
     N = p.shape[0]
     y = [[Fraction(0)] * N for _ in range(M)]
@@ -215,7 +215,7 @@ def _brute(x_bits, p, s_bits):
             am = Fraction(0)
             for k in range(K):
                 xv = Fraction(bf16_value(int(x_bits[m, k])))
-                wv = Fraction(bf16_value(int(s_bits[n, k // 128]))) * (nibble(p[n], k) - 8)
+                wv = Fraction(bf16_value(int(s_bits[n, k // group]))) * (nibble(p[n], k) - 8)
                 acc += xv * wv
                 am += abs(xv * wv)
             y[m][n] = acc
@@ -311,6 +311,75 @@ def pin_gemm_entries(o):
     ref, mag = _brute(c.x[:, :], p, c.s)
     for i in range(5):
         assert abs(e[i] - float(ref[rows[i]][cols[i]])) <= 1e-12 * float(mag[rows[i]][cols[i]])
+
+
+# ------------------------------------------------------------------ group 32
+# The first page's kernel quantises with one scale per 32 k (its per-GEMM
+# table, section "Results"); the definition is the same with k // 32.
+
+def pin_group32_one_hot_rows(o):
+    """X = e_k at group 32 gives S[n, k // 32] * (nibble - 8): pins the scale
+    index at every 32-group boundary of a 128-k stage."""
+    c = rand_case(1, 5, 256, seed=61, group=32)
+    assert c.s.shape == (5, 8)
+    p = o.pack_int4(c.q)
+    ks = [0, 31, 32, 33, 63, 64, 95, 96, 127, 128, 160, 255]
+    x = np.zeros((len(ks), 256), dtype=np.uint16)
+    for i, k in enumerate(ks):
+        x[i, k] = 0x3F80
+    y = o.gemm(x, p, c.s, 32)
+    e = o.gemm_entries(x, p, c.s, np.arange(len(ks)), np.full(len(ks), 3), 32)
+    for i, k in enumerate(ks):
+        for n in range(5):
+            want = bf16_value(int(c.s[n, k // 32])) * (nibble(p[n], k) - 8)
+            assert y[i, n] == want, (k, n, y[i, n], want)
+        assert e[i] == y[i, 3]
+
+
+def pin_group32_brute_force(o):
+    """Exact rational triple loop at group 32 (random and all-15 weights) vs
+    the oracle's gemm and gemm_entries; bound 1e-12 * sum|x*w|."""
+    for idx, (M, N, K) in enumerate([(1, 3, 128), (2, 4, 256), (3, 2, 384)]):
+        c = rand_case(M, N, K, seed=200 + idx, group=32)
+        for q in (c.q, np.full_like(c.q, 15)):
+            p = o.pack_int4(q)
+            y = o.gemm(c.x, p, c.s, 32)
+            ref, mag = _brute(c.x, p, c.s, 32)
+            rows = np.repeat(np.arange(M), N)
+            cols = np.tile(np.arange(N), M)
+            e = o.gemm_entries(c.x, p, c.s, rows, cols, 32)
+            for i, (m, n) in enumerate(zip(rows, cols)):
+                bound = 1e-12 * float(mag[m][n]) + 1e-300
+                assert abs(y[m, n] - float(ref[m][n])) <= bound, (M, N, K, m, n)
+                assert abs(e[i] - float(ref[m][n])) <= bound, (M, N, K, m, n)
+
+
+def pin_group32_closed_form_ones(o):
+    """X = all ones and a constant nibble c_g per (row, 32-group):
+    Y[0, n] = sum_g 32 * s[n, g] * (c_g - 8), exactly."""
+    N, K = 4, 384
+    rng = np.random.default_rng(71)
+    cg = rng.integers(0, 16, (N, K // 32), dtype=np.uint8)
+    q = np.repeat(cg, 32, axis=1)
+    s = np.array([[f32_bits(f32_round(v)) >> 16 for v in row]
+                  for row in rng.uniform(0.005, 0.02, (N, K // 32))],
+                 dtype=np.uint16)
+    x = np.full((1, K), 0x3F80, dtype=np.uint16)
+    y = o.gemm(x, o.pack_int4(q), s, 32)
+    for n in range(N):
+        want = sum(Fraction(32) * Fraction(bf16_value(int(s[n, g]))) * (int(cg[n, g]) - 8)
+                   for g in range(K // 32))
+        assert y[0, n] == float(want)
+
+
+def pin_group32_refines_128(o):
+    """Scales equal over each run of four 32-groups give exactly the group-128
+    result with those scales (the dequantised weights are the same)."""
+    c = rand_case(3, 6, 512, seed=81)
+    s32 = np.repeat(c.s, 4, axis=1)
+    p = o.pack_int4(c.q)
+    assert np.array_equal(o.dequant(p, s32, 32), o.dequant(p, c.s, 128))
+    assert np.array_equal(o.gemm(c.x, p, s32, 32), o.gemm(c.x, p, c.s, 128))
 
 
 # ------------------------------------------------------------------ split-K

@@ -52,7 +52,8 @@ def gemm(x=A, w=B, s=C, y=D, M=1, N=64, K=128, g=128, sk=0, ws=None, wsb=0):
 @pytest.mark.parametrize("kw,want", [
     (dict(M=-1), ERR_SHAPE), (dict(N=0), ERR_SHAPE), (dict(K=0), ERR_SHAPE),
     (dict(K=100), ERR_GROUP), (dict(K=192), ERR_GROUP), (dict(g=64), ERR_GROUP),
-    (dict(g=32, K=128), ERR_GROUP),
+    (dict(g=32, K=96), ERR_GROUP), (dict(g=16, K=128), ERR_GROUP),
+    (dict(g=32, K=128), ERR_WS),                             # group 32: tile path at any M, row sums needed
     (dict(sk=3), ERR_SPLIT), (dict(sk=-1), ERR_SPLIT), (dict(sk=32), ERR_SPLIT),
     (dict(x=None), ERR_NULL), (dict(w=None), ERR_NULL), (dict(s=None), ERR_NULL), (dict(y=None), ERR_NULL),
     (dict(x=MIS), ERR_ALIGN), (dict(y=MIS), ERR_ALIGN), (dict(w=MIS), ERR_ALIGN), (dict(s=MIS), ERR_ALIGN),
@@ -80,7 +81,9 @@ def grouped(x=A, w=B, s=C, ms=A, y=D, G=2, Mt=10, N=64, K=128, g=128, ws=A, wsb=
 
 @pytest.mark.parametrize("kw,want", [
     (dict(G=0), ERR_SHAPE), (dict(G=-3), ERR_SHAPE), (dict(Mt=-1), ERR_SHAPE),
-    (dict(K=130), ERR_GROUP), (dict(g=256), ERR_GROUP),
+    (dict(K=130), ERR_GROUP), (dict(g=256), ERR_GROUP), (dict(g=32, K=96), ERR_GROUP),
+    (dict(g=32, wsb=2 * 12 * 4), ERR_WS),                    # row sums of 32-groups: K/32 x round_up(10, 4)
+    (dict(G=1 << 10, N=1 << 16, K=1 << 12, g=32), ERR_SHAPE),   # scales of all groups >= 4 GiB
     (dict(ms=None), ERR_NULL), (dict(x=None), ERR_NULL), (dict(y=None), ERR_NULL),
     (dict(ms=ctypes.c_void_p(0x10002)), ERR_ALIGN), (dict(x=MIS), ERR_ALIGN),
     (dict(ws=None), ERR_WS), (dict(wsb=8), ERR_WS),
@@ -101,6 +104,7 @@ def batched(x=A, w=B, s=C, y=D, Bn=3, M=5, N=64, K=128, g=128, sk=0, ws=A, wsb=1
     (dict(sk=3), ERR_SPLIT), (dict(sk=32), ERR_SPLIT),
     (dict(x=None), ERR_NULL), (dict(w=None), ERR_NULL), (dict(s=None), ERR_NULL), (dict(y=None), ERR_NULL),
     (dict(x=MIS), ERR_ALIGN), (dict(s=MIS), ERR_ALIGN), (dict(ws=MIS), ERR_ALIGN),
+    (dict(g=32, sk=1, wsb=4 * 16 * 4 - 4), ERR_WS),           # row sums of 32-groups: K/32 x round_up(15, 4)
     (dict(ws=None), ERR_WS), (dict(wsb=8), ERR_WS),
     (dict(Bn=1 << 16, M=1 << 16), ERR_SHAPE),              # B * M >= 2^31
     (dict(Bn=1 << 12, N=1 << 16, K=1 << 12), ERR_SHAPE),   # scales of all problems >= 4 GiB
@@ -141,6 +145,17 @@ def test_explicit_path_errors():
     cfg = w4._Config(7, -1)
     st = L().w4a16_gemm_ex(A, B, C, D, 2, 64, 128, 128, 0, None, 0, None, ctypes.byref(cfg))
     assert st == ERR_SHAPE
+    # group size 32: only the LDS-DMA tile configurations 2..5
+    for path, variant in ((1, -1), (2, -1), (3, 0), (3, 1), (3, 6)):
+        cfg = w4._Config(path, variant)
+        st = L().w4a16_gemm_ex(A, B, C, D, 1, 64, 128, 32, 0, A, 1 << 20, None, ctypes.byref(cfg))
+        assert st == ERR_GROUP, (path, variant)
+    for v in (0, 1, 6):
+        cfg = w4._Config(3, v)
+        st = L().w4a16_gemm_grouped_ex(A, B, C, A, D, 2, 10, 64, 128, 32, A, 1 << 20, None, ctypes.byref(cfg))
+        assert st == ERR_GROUP, v
+        st = L().w4a16_gemm_batched_ex(A, B, C, D, 3, 5, 64, 128, 32, 0, A, 1 << 20, None, ctypes.byref(cfg))
+        assert st == ERR_GROUP, v
 
 
 def test_auto_split_rule():
@@ -187,6 +202,17 @@ def test_workspace_sizes():
     assert bsk == ((2 * 15 * 64 * 4 + 255) // 256) * 256 + 2 * 16 * 4
     assert w4.w4a16_gemm_batched_workspace_bytes(0, 5, 64, 256, 1) == 0
     assert w4.w4a16_gemm_batched_workspace_bytes(2, 0, 64, 256, 1) == 0
+    # group size 32: the tile kernel at every M, row sums [K/32, round_up(rows, 4)]
+    assert w4.w4a16_gemm_workspace_bytes(1322, 19456, 2560, 1, group_size=32) == 80 * 1324 * 4
+    assert w4.w4a16_gemm_workspace_bytes(1, 17408, 5120, 1, group_size=32) == 160 * 4 * 4
+    g32 = w4.w4a16_gemm_workspace_bytes(100, 64, 256, 2, group_size=32)
+    assert g32 == ((2 * 100 * 64 * 4 + 255) // 256) * 256 + 8 * 100 * 4
+    assert w4.w4a16_gemm_workspace_bytes(16, 64, 256, 1, group_size=64) == 0
+    assert w4.w4a16_gemm_workspace_bytes(16, 64, 256, 1, w4.PATH_SKINNY, group_size=32) == 0
+    assert w4.w4a16_gemm_workspace_bytes(16, 64, 256, 1, w4.PATH_TILE, 6, group_size=32) == 0
+    assert w4.w4a16_gemm_grouped_workspace_bytes(8, 2047, 2048, 4096, group_size=32) == 128 * 2048 * 4
+    assert w4.w4a16_gemm_batched_workspace_bytes(8, 256, 2048, 4096, 1, group_size=32) == 128 * 2048 * 4
+    assert w4.w4a16_gemm_batched_workspace_bytes(8, 256, 2048, 4096, 1, 6, group_size=32) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

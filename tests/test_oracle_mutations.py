@@ -29,6 +29,10 @@ MUTATIONS = {
                        "np.tile(np.repeat(s, group // 2, axis=-1), 2)"),
     "scale_tiled_not_repeated": ("np.repeat(s, group, axis=-1)",
                                  "np.tile(s, group)"),
+    "gemm_group_ignored": ("wd = dequant(p, s_bits, group)\n    if x.shape[1]",
+                           "wd = dequant(p, np.repeat(s_bits[..., ::128 // group], 1, axis=-1), 128)\n    if x.shape[1]"),
+    "entries_group_ignored": ("wd = dequant(p[ucols], s_bits[ucols], group)",
+                              "wd = dequant(p[ucols], s_bits[ucols][..., ::128 // group], 128)"),
     "transposed_operand": ("return x @ wd.T", "return (wd @ x.T).T[:, ::-1]"),
     "bf16_low_half": ("astype(np.uint32) << np.uint32(16)",
                       "astype(np.uint32) << np.uint32(15)"),
