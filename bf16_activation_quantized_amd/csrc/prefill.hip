@@ -239,13 +239,20 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   auto compute32 = [&](int stage) {
     if constexpr (GS == 32) {
     const uint8_t* sb = lds + stage * ST::kBytes;
+    // row tile ms's operands: the 4 steps' initial C (row sums of the
+    // stage's four 32-groups) and A fragments; the next row tile's reads go
+    // out before this tile's MFMAs (two register sets)
+    f32x4 cq[2][NSG];
     bf16x8 aq[2][4];
-    auto read_a = [&](int ms, bf16x8 (&a)[4]) {
+    auto read_rows = [&](int ms, f32x4 (&c)[NSG], bf16x8 (&a)[4]) {
+#pragma unroll
+      for (int st = 0; st < NSG; ++st)
+        c[st] = *reinterpret_cast<const f32x4*>(sb + roff + (uint32_t)(ST::kRows * 4 * st) + 64u * (uint32_t)ms);
 #pragma unroll
       for (int st = 0; st < 4; ++st)
         a[st] = *reinterpret_cast<const bf16x8*>(sb + (aoffN ^ (64u * (uint32_t)st)) + 4096u * (uint32_t)ms);
     };
-    read_a(0, aq[0]);
+    read_rows(0, cq[0], aq[0]);
     bf16x8 bd[SN][4];
 #pragma unroll
     for (int ns = 0; ns < SN; ++ns)
@@ -265,39 +272,36 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     for (int ns = 0; ns < SN; ++ns)
 #pragma unroll
       for (int st = 0; st < 4; ++st) scv[ns][st] = scale32(sc_cur[ns], st);
+    // step st's products are rescaled after the next step's MFMAs are issued
+    // (the last step's after the next row tile's first step), so no MFMA
+    // result is read right behind its issue; the empty asm pins each rescale
+    // there, otherwise all steps' products stay live
+    f32x4 t[2][SN];
+    auto rescale = [&](const f32x4 (&u)[SN], int ms, int st) {
+#pragma unroll
+      for (int ns = 0; ns < SN; ++ns) {
+        acc[ms][ns].x = fmaf(scv[ns][st], u[ns].x, acc[ms][ns].x);
+        acc[ms][ns].y = fmaf(scv[ns][st], u[ns].y, acc[ms][ns].y);
+        acc[ms][ns].z = fmaf(scv[ns][st], u[ns].z, acc[ms][ns].z);
+        acc[ms][ns].w = fmaf(scv[ns][st], u[ns].w, acc[ms][ns].w);
+        asm volatile("" : "+v"(acc[ms][ns]));
+      }
+    };
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
       const int cur = ms & 1;
-      // this row tile's four initial C (row sums of the stage's 4 groups)
-      f32x4 cq[NSG];
-#pragma unroll
-      for (int st = 0; st < NSG; ++st)
-        cq[st] = *reinterpret_cast<const f32x4*>(sb + roff + (uint32_t)(ST::kRows * 4 * st) + 64u * (uint32_t)ms);
-      if (ms + 1 < MS) read_a(ms + 1, aq[(ms + 1) & 1]);
+      if (ms + 1 < MS) read_rows(ms + 1, cq[(ms + 1) & 1], aq[(ms + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      // step st's products are rescaled after step st + 1's MFMAs are issued
-      // (the MFMA result is not read right behind its issue); the empty asm
-      // pins each rescale there, otherwise all 4 steps' products stay live
-      f32x4 t[2][SN];
-      auto rescale = [&](const f32x4 (&u)[SN], int st) {
-#pragma unroll
-        for (int ns = 0; ns < SN; ++ns) {
-          acc[ms][ns].x = fmaf(scv[ns][st], u[ns].x, acc[ms][ns].x);
-          acc[ms][ns].y = fmaf(scv[ns][st], u[ns].y, acc[ms][ns].y);
-          acc[ms][ns].z = fmaf(scv[ns][st], u[ns].z, acc[ms][ns].z);
-          acc[ms][ns].w = fmaf(scv[ns][st], u[ns].w, acc[ms][ns].w);
-          asm volatile("" : "+v"(acc[ms][ns]));
-        }
-      };
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
 #pragma unroll
         for (int ns = 0; ns < SN; ++ns)
-          t[st & 1][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[cur][st], bd[ns][st], cq[st], 0, 0, 0);
-        if (st > 0) rescale(t[(st - 1) & 1], st - 1);
+          t[st & 1][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[cur][st], bd[ns][st], cq[cur][st], 0, 0, 0);
+        if (st > 0) rescale(t[(st - 1) & 1], ms, st - 1);
+        else if (ms > 0) rescale(t[1], ms - 1, 3);
       }
-      rescale(t[1], 3);
     }
+    rescale(t[1], MS - 1, 3);
     }
   };
 
