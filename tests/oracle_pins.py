@@ -382,6 +382,44 @@ def pin_group32_refines_128(o):
     assert np.array_equal(o.gemm(c.x, p, s32, 32), o.gemm(c.x, p, c.s, 128))
 
 
+def pin_group32_grouped_and_batched_one_hot(o):
+    """Grouped and batched at group 32 with one-hot rows: row i of group g
+    (problem b) gives S_g[n, k_i // 32] * (nibble(P_g[n], k_i) - 8) with that
+    group's own weights and scales; empty groups contribute no rows."""
+    K, N = 256, 3
+    ks = [0, 31, 32, 63, 64, 100, 127, 128, 159, 160, 200, 255]
+    ms = [2, 0, 3, 4]
+    c = rand_case(sum(ms), N, K, seed=91, G=len(ms), m_sizes=ms, group=32)
+    p = o.pack_int4(c.q)
+    x = np.zeros((sum(ms), K), dtype=np.uint16)
+    row_k = [ks[(3 * i + 1) % len(ks)] for i in range(sum(ms))]
+    for i, k in enumerate(row_k):
+        x[i, k] = 0x3F80
+    y = o.gemm_grouped(x, p, c.s, ms, 32)
+    r = 0
+    for g, m in enumerate(ms):
+        for _ in range(m):
+            k = row_k[r]
+            for n in range(N):
+                want = bf16_value(int(c.s[g, n, k // 32])) * (nibble(p[g, n], k) - 8)
+                assert y[r, n] == want, (g, r, n, k)
+            r += 1
+    B, M = 3, 4
+    cb = rand_case(B * M, N, K, seed=92, G=B, m_sizes=[M] * B, group=32)
+    pb = o.pack_int4(cb.q)
+    xb = np.zeros((B, M, K), dtype=np.uint16)
+    for b in range(B):
+        for i in range(M):
+            xb[b, i, ks[(5 * b + 2 * i) % len(ks)]] = 0x3F80
+    yb = o.gemm_batched(xb, pb, cb.s, 32)
+    for b in range(B):
+        for i in range(M):
+            k = ks[(5 * b + 2 * i) % len(ks)]
+            for n in range(N):
+                want = bf16_value(int(cb.s[b, n, k // 32])) * (nibble(pb[b, n], k) - 8)
+                assert yb[b, i, n] == want, (b, i, n, k)
+
+
 # ------------------------------------------------------------------ split-K
 
 def pin_splitk_ranges(o):

@@ -33,6 +33,10 @@ MUTATIONS = {
                            "wd = dequant(p, np.repeat(s_bits[..., ::128 // group], 1, axis=-1), 128)\n    if x.shape[1]"),
     "entries_group_ignored": ("wd = dequant(p[ucols], s_bits[ucols], group)",
                               "wd = dequant(p[ucols], s_bits[ucols][..., ::128 // group], 128)"),
+    "grouped_group_dropped": ("y[r0:r1] = gemm(x_bits[r0:r1], p[g], s_bits[g], group)",
+                              "y[r0:r1] = gemm(x_bits[r0:r1], p[g], s_bits[g][..., ::128 // group])"),
+    "batched_group_dropped": ("gemm(x_bits[b], p[b], s_bits[b], group) for b in range(B)",
+                              "gemm(x_bits[b], p[b], s_bits[b][..., ::128 // group]) for b in range(B)"),
     "transposed_operand": ("return x @ wd.T", "return (wd @ x.T).T[:, ::-1]"),
     "bf16_low_half": ("astype(np.uint32) << np.uint32(16)",
                       "astype(np.uint32) << np.uint32(15)"),
