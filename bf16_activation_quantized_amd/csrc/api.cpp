@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include <stddef.h>
 #include <stdint.h>
@@ -60,17 +61,18 @@ Path auto_path(int64_t M, int64_t K, int32_t sk) {
   return kPathTile;
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; safe to call from
+// several host threads).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int v = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cache[dev] = v;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
 }
 
 // Cost model of the tile path, in units of one row x one 128-group of work on

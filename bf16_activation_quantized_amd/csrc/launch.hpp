@@ -4,7 +4,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace w4a16 {
+
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per device: `done` is the caller's per-kernel set of devices already set
+// (bit d = device d; a device index past 63 sets it on every call).
+inline hipError_t ensure_dyn_lds(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 hipError_t launch_pack_int4(const uint8_t* q, uint8_t* out, uint64_t total_in, hipStream_t stream);
 hipError_t launch_splitk_reduce(const float* ws, uint16_t* y, uint64_t mn, int sk, hipStream_t stream);

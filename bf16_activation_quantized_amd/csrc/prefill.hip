@@ -430,13 +430,10 @@ template <int NSTAGE, int MS, int GS = 128>
 static hipError_t launch_prefill_t(PrefillArgs a, int sk, hipStream_t stream) {
   constexpr int BM = Stage<MS, GS>::kRows;
   const int lds_bytes = NSTAGE * Stage<MS, GS>::kBytes;
-  static bool attr_set = false;   // per instantiation; the attribute is per function
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NSTAGE, MS, GS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};   // per instantiation and device
+  const hipError_t ea =
+      ensure_dyn_lds(reinterpret_cast<const void*>(&prefill_kernel<NSTAGE, MS, GS>), lds_bytes, lds_set);
+  if (ea != hipSuccess) return ea;
   a.mtiles = a.m_uniform > 0 ? a.G * ((a.m_uniform + BM - 1) / BM)
                              : (a.M_total + BM - 1) / BM + (a.m_sizes != nullptr ? a.G : 0);
   a.ntiles = (a.N + kPN - 1) / kPN;

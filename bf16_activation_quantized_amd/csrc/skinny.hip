@@ -470,13 +470,10 @@ template <int NT, int D, int WAVES, int GB>
 static hipError_t launch_stream_t(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                                   int M, int N, int K, int gps, int sk, hipStream_t stream) {
   const size_t lds = skinny_stream_lds(gps);
-  static bool attr_set = false;   // per instantiation
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_stream_kernel<NT, D, WAVES, GB>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)skinny_stream_lds(kSkinnyStreamMaxGroups));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};   // per instantiation and device
+  const hipError_t ea = ensure_dyn_lds(reinterpret_cast<const void*>(&skinny_stream_kernel<NT, D, WAVES, GB>),
+                                       (int)skinny_stream_lds(kSkinnyStreamMaxGroups), lds_set);
+  if (ea != hipSuccess) return ea;
   // one workgroup per compute unit over the slices (at least one per slice)
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
@@ -514,14 +511,10 @@ hipError_t launch_skinny(const uint16_t* x, const uint8_t* w, const uint16_t* s,
     dim3 grid((N + 16 * NTT - 1) / (16 * NTT), sk);                                                    \
     if (slds) {                                                                                        \
       const size_t dyn = ((size_t)16 * NTT * gps * 2 + 15) & ~(size_t)15;                              \
-      static bool attr = false; /* per instantiation: the attribute is per function */                \
-      if (!attr) {                                                                                     \
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<NTT, WV, true>), \
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,                \
-                                           16 * NTT * kSkinnyMaxScaleGroups * 2);                      \
-        if (e != hipSuccess) return e;                                                                 \
-        attr = true;                                                                                   \
-      }                                                                                                \
+      static std::atomic<uint64_t> lds_set{0}; /* per instantiation and device */                    \
+      const hipError_t ea = ensure_dyn_lds(reinterpret_cast<const void*>(&skinny_kernel<NTT, WV, true>), \
+                                           16 * NTT * kSkinnyMaxScaleGroups * 2, lds_set);             \
+      if (ea != hipSuccess) return ea;                                                                 \
       hipLaunchKernelGGL((skinny_kernel<NTT, WV, true>), grid, dim3(64 * WV), dyn, stream, x, w, s, y, \
                          ws, M, N, K, gps);                                                            \
     } else {                                                                                           \
