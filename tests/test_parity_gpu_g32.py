@@ -56,6 +56,8 @@ TILE_CASES = [
     (1322, 512, 2560, 1, 5),
     (600, 700, 1280, 0, None),
     (64, 64, 1024, 4, None),
+    (130, 300, 16384, 0, None),   # 512 scale groups per row, automatic split
+    (40, 257, 16384, 16, 5),      # 16 slices of 8 stages, N * K/32 odd rows
 ]
 
 
@@ -100,6 +102,19 @@ def test_g32_degenerate_zero_outputs(sk):
     assert np.all((_gemm(zero_s, split_k=sk) & 0x7FFF) == 0)        # s == 0 -> +-0
     zero_x = DevCase(type(c)(x=np.zeros_like(c.x), q=c.q, s=c.s, group_size=G32))
     assert np.all((_gemm(zero_x, split_k=sk) & 0x7FFF) == 0)
+
+
+def test_g32_n1_k128_and_m0():
+    for M in (1, 3, 20):
+        c = make_inputs(M, 1, 128, seed=M + 32, group=G32)
+        d = DevCase(c)
+        check_gate(_gemm(d), oracle.gemm(c.x, d.p_host, c.s, G32), f"g32 N=1 K=128 M={M}")
+    # M = 0: nothing is enqueued and the output is left as it was
+    c = make_inputs(1, 64, 256, seed=5, group=G32)
+    d = DevCase(c)
+    y = torch.full((0, 64), 1.0, dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_gemm(d.x[:0], d.w, d.s, y=y, group_size=G32)
+    torch.cuda.synchronize()
 
 
 GROUPED_CASES = [
