@@ -39,7 +39,10 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
   return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
 }
 
-template <int NT, int WAVES, bool SLDS>
+// XR: row quads of X loaded per group (M <= 4 XR). The A-operand rows past
+// them are never written in the staging tile; they feed only output rows
+// >= M, which are not stored.
+template <int NT, int WAVES, bool SLDS, int XR = 4>
 __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __restrict__ x,
                                                             const uint8_t* __restrict__ w,
                                                             const uint16_t* __restrict__ s,
@@ -93,13 +96,13 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
 
   // double-buffered loads: x (4 x 16 B), weights (NT x 16 B), scales (NT).
   // Two named buffer sets, so that no register array is indexed at run time.
-  u32x4 xb0[4], xb1[4];
+  u32x4 xb0[XR], xb1[XR];
   u32x4 wb0[NT], wb1[NT];
   uint16_t sb0[NT], sb1[NT];
-  auto issue = [&](u32x4 (&xb)[4], u32x4 (&wb)[NT], uint16_t (&sb)[NT], int g) {
+  auto issue = [&](u32x4 (&xb)[XR], u32x4 (&wb)[NT], uint16_t (&sb)[NT], int g) {
     const uint32_t xo = xrow + (uint32_t)g * 256u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xb[j] = ld128(rx, xo + xrow4 * (uint32_t)j);
+    for (int j = 0; j < XR; ++j) xb[j] = ld128(rx, xo + xrow4 * (uint32_t)j);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       wb[t] = ld128(rw, wrow[t] + (uint32_t)g * 64u);
@@ -107,10 +110,10 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
       else sb[t] = (uint16_t)(16 * t + col) * (uint16_t)gs + (uint16_t)(g - g0);   // LDS index
     }
   };
-  auto compute = [&](const u32x4 (&xb)[4], const u32x4 (&wb)[NT], const uint16_t (&sb)[NT]) {
+  auto compute = [&](const u32x4 (&xb)[XR], const u32x4 (&wb)[NT], const uint16_t (&sb)[NT]) {
     u32x4* xw = xst[wave];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < XR; ++j) {
       const int r = 4 * j + (lane >> 4), pc = lane & 15;
       xw[16 * r + (pc ^ r)] = xb[j];
     }
@@ -502,26 +505,36 @@ hipError_t launch_skinny_stream(const uint16_t* x, const uint8_t* w, const uint1
   return hipErrorInvalidValue;
 }
 
+template <int NT, int WV, int XR>
+static hipError_t launch_skinny_t(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
+                                  int M, int N, int K, int gps, int sk, hipStream_t stream) {
+  dim3 grid((N + 16 * NT - 1) / (16 * NT), sk);
+  // scales staged in LDS while the slice's scale block stays small
+  if (gps <= kSkinnyMaxScaleGroups) {
+    const size_t dyn = ((size_t)16 * NT * gps * 2 + 15) & ~(size_t)15;
+    static std::atomic<uint64_t> lds_set{0};   // per instantiation and device
+    const hipError_t ea = ensure_dyn_lds(reinterpret_cast<const void*>(&skinny_kernel<NT, WV, true, XR>),
+                                         16 * NT * kSkinnyMaxScaleGroups * 2, lds_set);
+    if (ea != hipSuccess) return ea;
+    hipLaunchKernelGGL((skinny_kernel<NT, WV, true, XR>), grid, dim3(64 * WV), dyn, stream, x, w, s, y, ws, M, N,
+                       K, gps);
+  } else {
+    hipLaunchKernelGGL((skinny_kernel<NT, WV, false, XR>), grid, dim3(64 * WV), 0, stream, x, w, s, y, ws, M, N, K,
+                       gps);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_skinny(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                          int M, int N, int K, int gps, int sk, int nt, int waves, hipStream_t stream) {
-  // scales staged in LDS while the slice's scale block stays small
-  const bool slds = gps <= kSkinnyMaxScaleGroups;
-#define W4A16_SKINNY(NTT, WV)                                                                          \
-  if (nt == NTT && waves == WV) {                                                                      \
-    dim3 grid((N + 16 * NTT - 1) / (16 * NTT), sk);                                                    \
-    if (slds) {                                                                                        \
-      const size_t dyn = ((size_t)16 * NTT * gps * 2 + 15) & ~(size_t)15;                              \
-      static std::atomic<uint64_t> lds_set{0}; /* per instantiation and device */                    \
-      const hipError_t ea = ensure_dyn_lds(reinterpret_cast<const void*>(&skinny_kernel<NTT, WV, true>), \
-                                           16 * NTT * kSkinnyMaxScaleGroups * 2, lds_set);             \
-      if (ea != hipSuccess) return ea;                                                                 \
-      hipLaunchKernelGGL((skinny_kernel<NTT, WV, true>), grid, dim3(64 * WV), dyn, stream, x, w, s, y, \
-                         ws, M, N, K, gps);                                                            \
-    } else {                                                                                           \
-      hipLaunchKernelGGL((skinny_kernel<NTT, WV, false>), grid, dim3(64 * WV), 0, stream, x, w, s, y,  \
-                         ws, M, N, K, gps);                                                            \
-    }                                                                                                  \
-    return hipGetLastError();                                                                          \
+  if (M < 1 || M > 16) return hipErrorInvalidValue;
+  // only the row quads of X that hold rows < M are loaded
+#define W4A16_SKINNY(NTT, WV)                                                                   \
+  if (nt == NTT && waves == WV) {                                                               \
+    if (M <= 4) return launch_skinny_t<NTT, WV, 1>(x, w, s, y, ws, M, N, K, gps, sk, stream);  \
+    if (M <= 8) return launch_skinny_t<NTT, WV, 2>(x, w, s, y, ws, M, N, K, gps, sk, stream);  \
+    if (M <= 12) return launch_skinny_t<NTT, WV, 3>(x, w, s, y, ws, M, N, K, gps, sk, stream); \
+    return launch_skinny_t<NTT, WV, 4>(x, w, s, y, ws, M, N, K, gps, sk, stream);              \
   }
   W4A16_SKINNY(1, 4)
   W4A16_SKINNY(2, 4)

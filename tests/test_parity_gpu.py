@@ -126,6 +126,13 @@ SKINNY_CASES = [
     (16, 100, 384, 16, 44),   # more slices than groups
     (7, 300, 640, 1, 82),
     (16, 8192, 1024, 0, None),
+    # X row quads loaded per group follow M (1: M <= 4, 2: <= 8, 3: <= 12, 4)
+    (4, 300, 640, 1, 82),
+    (8, 300, 640, 2, 82),
+    (9, 513, 1024, 1, 82),
+    (12, 300, 640, 1, 41),
+    (13, 257, 384, 1, 84),
+    (4, 100, 40960, 1, 82),       # a slice too long to stage its scales in LDS (320 groups)
     # streaming layout: 1000 + 100 * row tiles + 10 * units in flight + waves / 4
     (1, 256, 512, 1, 1131),
     (3, 17, 384, 1, 1121),        # fewer rows than one 16-row block
