@@ -43,12 +43,13 @@ constexpr int kGemvDefaultVariant = 2110;
 // units in flight + waves / 4 is the streaming layout with units of 4 << (u - 1)
 // groups (one workgroup per compute unit, X of the slice in LDS, at most
 // kSkinnyStreamMaxGroups groups per slice). The default is the group-striped
-// layout: at the small-batch decode workload both run at the same rate.
-constexpr int kSkinnyNT = 2;
-constexpr int kSkinnyWaves = 8;
-constexpr int kSkinnyDefaultVariant = 10 * kSkinnyWaves + kSkinnyNT;
+// layout with 8 waves (at the small-batch decode workload the streaming one
+// runs at the same rate): one column tile per wave up to 8 rows, two above
+// (at 17408 x 5120 and 8192 x 8192, rotated weights: M = 2-4 7-10 % faster
+// with one tile, M >= 9 4-12 % faster with two).
+int skinny_default_variant(int64_t M) { return M <= 8 ? 81 : 82; }
 
-bool skinny_streaming(int variant) { return (variant > 0 ? variant : kSkinnyDefaultVariant) >= 1000; }
+bool skinny_streaming(int variant) { return variant >= 1000; }
 
 Path auto_path(int64_t M, int64_t K, int32_t sk) {
   const int64_t Gk = K / kGroup;
@@ -146,7 +147,7 @@ int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg, int
         break;
       }
       // one workgroup per compute unit or more; every wave keeps at least one group
-      const int v = variant > 0 ? variant : kSkinnyDefaultVariant;
+      const int v = variant > 0 ? variant : skinny_default_variant(M);
       const int nt = v % 10, waves = v / 10;
       const int64_t wgs = ceil_div(N, 16 * (int64_t)std::max(nt, 1));
       while (sk < 16 && wgs * sk < device_cus() && ceil_div(Gk, (int64_t)sk * 2) >= waves) sk <<= 1;
@@ -276,6 +277,7 @@ w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w
   if (path == kPathGemv && M != 1) return W4A16_ERR_SHAPE;
   if (path == kPathSkinny && M > 16) return W4A16_ERR_SHAPE;
   if (path != kPathTile && gs != kGroup) return W4A16_ERR_GROUP_SIZE;
+  if (path == kPathSkinny && variant <= 0) variant = skinny_default_variant(M);
   int tile_cfg = 0;
   if (path == kPathTile) {
     tile_cfg = variant >= 0 ? variant : default_tile_cfg(M, N, K, split_k, gs);
@@ -354,15 +356,15 @@ w4a16_status run_gemm(const uint16_t* x, const uint8_t* w, const uint16_t* s, ui
       break;
     }
     case kPathSkinny: {
-      const int v = p.variant > 0 ? p.variant : kSkinnyDefaultVariant;
+      const int v = p.variant > 0 ? p.variant : skinny_default_variant(M);
       if (v >= 1000 && p.gps <= w4a16::kSkinnyStreamMaxGroups) {
         e = w4a16::launch_skinny_stream(x, w, s, y, ws_split, iM, iN, iK, p.gps, p.sk, (v / 100) % 10,
                                         (v / 10) % 10, 4 * (v % 10), 4 << ((v / 1000) - 1), strm);
         break;
       }
       // group-striped layout (also for slices too long for the streaming one)
-      int nt = kSkinnyNT, waves = kSkinnyWaves;
-      if (v < 1000) { nt = v % 10; waves = v / 10; }
+      const int vs = v < 1000 ? v : skinny_default_variant(M);
+      const int nt = vs % 10, waves = vs / 10;
       e = w4a16::launch_skinny(x, w, s, y, ws_split, iM, iN, iK, p.gps, p.sk, nt, waves, strm);
       break;
     }

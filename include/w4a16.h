@@ -254,14 +254,15 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  *              1..4 (layout 1) = loads in flight, rows 1..9 = rows or row
  *              blocks per wave;
  *            path 2: 10 * waves_per_workgroup +
- *            column_tiles_per_wave (41, 42, 44, 81, 82 (default), 84): waves
+ *            column_tiles_per_wave (41, 42, 44, 81, 82, 84; default 81 for
+ *            M <= 8, 82 above): waves
  *            take a column block's groups in turn; or the streaming layout
  *            1000 * u + 100 * row_tiles + 10 * units_in_flight + waves / 4,
  *            units of 4 << (u - 1) groups (one workgroup per compute unit,
  *            X of the slice staged in LDS, each wave streaming blocks of
  *            16 * row_tiles weight rows): 1121, 1131, 1122, 1222, 2121,
  *            2122, 3121, 3112, 3131; with more than 32 groups per slice it
- *            runs variant 82; path 3: tile
+ *            runs the default of the first form; path 3: tile
  *            configuration index (0: 128x256 and 1: 128x128 with weights
  *            dequantised into LDS; 2: 128x256 with LDS-DMA staging, 8
  *            waves, 3 LDS stages; 3, 4, 5, 6: the same with 96x256,
