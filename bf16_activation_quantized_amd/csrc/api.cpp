@@ -38,7 +38,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // workgroup per compute unit, x held in registers, one weight block in
 // flight per wave (encoding in the dispatcher of gemv.hip).
 constexpr int kGemvDefaultVariant = 2110;
-// Skinny (M <= 16): variants below 1000 are the group-striped layout
+// Small batch (M <= 32, two row tiles of 16 past 16 rows): variants below
+// 1000 are the group-striped layout
 // (10 * waves + column tiles per wave); 1000 * u + 100 * row tiles + 10 *
 // units in flight + waves / 4 is the streaming layout with units of 4 << (u - 1)
 // groups (one workgroup per compute unit, X of the slice in LDS, at most
@@ -58,7 +59,9 @@ Path auto_path(int64_t M, int64_t K, int32_t sk) {
     const int64_t s = sk > 0 ? sk : 16;
     return ceil_div(Gk, s) <= 64 ? kPathGemv : kPathSkinny;
   }
-  if (M <= 16) return kPathSkinny;
+  // up to two row tiles of 16: at 17 <= M <= 32 the small-batch kernel ran
+  // 6-33 % faster than the tile kernel (17408 x 5120, 8192 x 8192, 2560 x 9728)
+  if (M <= w4a16::kSkinnyMaxRows) return kPathSkinny;
   return kPathTile;
 }
 
@@ -146,11 +149,14 @@ int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg, int
         while (sk < 16 && blocks * sk < 1024 && sk * 2 <= Gk) sk <<= 1;
         break;
       }
-      // one workgroup per compute unit or more; every wave keeps at least one group
+      // the most slices that still fit one round of one workgroup per compute
+      // unit (a second, partly filled round of slices costs more than it
+      // saves: 2560 x 9728 ran 20 % faster at SK 2 than at 4), every wave
+      // keeping at least one group
       const int v = variant > 0 ? variant : skinny_default_variant(M);
       const int nt = v % 10, waves = v / 10;
       const int64_t wgs = ceil_div(N, 16 * (int64_t)std::max(nt, 1));
-      while (sk < 16 && wgs * sk < device_cus() && ceil_div(Gk, (int64_t)sk * 2) >= waves) sk <<= 1;
+      while (sk < 16 && wgs * sk * 2 <= device_cus() && ceil_div(Gk, (int64_t)sk * 2) >= waves) sk <<= 1;
       break;
     }
     case kPathTile: {
@@ -275,9 +281,12 @@ w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w
     variant = cfg->variant;
   }
   if (path == kPathGemv && M != 1) return W4A16_ERR_SHAPE;
-  if (path == kPathSkinny && M > 16) return W4A16_ERR_SHAPE;
+  if (path == kPathSkinny && M > w4a16::kSkinnyMaxRows) return W4A16_ERR_SHAPE;
   if (path != kPathTile && gs != kGroup) return W4A16_ERR_GROUP_SIZE;
   if (path == kPathSkinny && variant <= 0) variant = skinny_default_variant(M);
+  // past 16 rows (two row tiles): the group-striped layout with 8 waves of
+  // 1 or 2 column tiles only
+  if (path == kPathSkinny && M > 16 && !(variant == 81 || variant == 82)) return W4A16_ERR_SHAPE;
   int tile_cfg = 0;
   if (path == kPathTile) {
     tile_cfg = variant >= 0 ? variant : default_tile_cfg(M, N, K, split_k, gs);

@@ -29,7 +29,8 @@ hipError_t launch_splitk_reduce(const float* ws, uint16_t* y, uint64_t mn, int s
 hipError_t launch_gemv_m1(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                           int N, int K, int gps, int sk, int variant, hipStream_t stream);
 
-// 1 <= M <= 16 decode on MFMA 16x16x32; nt column tiles of 16 per wave, `waves` per workgroup.
+// 1 <= M <= kSkinnyMaxRows decode on MFMA 16x16x32; nt column tiles of 16 per wave, `waves` per
+// workgroup (past 16 rows only 8 waves of 1 or 2 column tiles).
 hipError_t launch_skinny(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                          int M, int N, int K, int gps, int sk, int nt, int waves, hipStream_t stream);
 
@@ -40,6 +41,9 @@ constexpr int kSkinnyStreamMaxGroups = 32;
 // slices of at most this many groups stage their scales in LDS (16 NT x gps x 2
 // bytes, at most 32 KiB)
 constexpr int kSkinnyMaxScaleGroups = 256;
+// rows of the small-batch kernel: 16 per row tile, two row tiles with 8
+// waves of 1 or 2 column tiles
+constexpr int kSkinnyMaxRows = 32;
 hipError_t launch_skinny_stream(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                                 int M, int N, int K, int gps, int sk, int nt, int depth, int waves, int gb,
                                 hipStream_t stream);

@@ -39,20 +39,22 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
   return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
 }
 
-// XR: row quads of X loaded per group (M <= 4 XR). The A-operand rows past
-// them are never written in the staging tile; they feed only output rows
-// >= M, which are not stored.
-template <int NT, int WAVES, bool SLDS, int XR = 4>
+// MT: row tiles of 16 (M <= 16 MT); XR: row quads of X loaded per group
+// (M <= 4 XR <= 16 MT). The A-operand rows past them are never written in
+// the staging tile; they feed only output rows >= M, which are not stored.
+template <int NT, int WAVES, bool SLDS, int XR = 4, int MT = 1>
 __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __restrict__ x,
                                                             const uint8_t* __restrict__ w,
                                                             const uint16_t* __restrict__ s,
                                                             uint16_t* __restrict__ y,
                                                             float* __restrict__ ws,
                                                             int M, int N, int K, int gps) {
-  __shared__ f32x4 red[WAVES > 1 ? (WAVES - 1) : 1][NT][64];
-  // per-wave staging of one group of X: [16 rows][16 slots of 16 bytes], the
-  // piece p of row r in slot p ^ r (conflict-free for both access patterns)
-  __shared__ u32x4 xst[WAVES][16 * 16];
+  static_assert(XR >= 1 && XR <= 4 * MT && (MT == 1 || MT == 2), "row quads within the row tiles");
+  __shared__ f32x4 red[WAVES > 1 ? (WAVES - 1) : 1][MT][NT][64];
+  // per-wave staging of one group of X: [16 MT rows][16 slots of 16 bytes],
+  // the piece p of row r in slot p ^ (r & 15) (conflict-free for both access
+  // patterns)
+  __shared__ u32x4 xst[WAVES][16 * 16 * MT];
   // SLDS: the slice's scales of the workgroup's 16 NT columns, [column][group]
   // (dynamic size 16 NT x gps x 2 bytes), fetched once in whole lines; per
   // group the lanes then read LDS instead of one line per column
@@ -90,9 +92,11 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
   const uint32_t neg136 = 0xC308C308u;   // bf16(-136) pair
   const bf16x8 bneg = as_bf16x8(neg136, neg136, neg136, neg136);
 
-  f32x4 acc[NT];
+  f32x4 acc[MT][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // double-buffered loads: x (4 x 16 B), weights (NT x 16 B), scales (NT).
   // Two named buffer sets, so that no register array is indexed at run time.
@@ -115,36 +119,77 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
 #pragma unroll
     for (int j = 0; j < XR; ++j) {
       const int r = 4 * j + (lane >> 4), pc = lane & 15;
-      xw[16 * r + (pc ^ r)] = xb[j];
+      xw[16 * r + (pc ^ (r & 15))] = xb[j];
     }
-    bf16x8 a[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // row m = col, piece 4 kb + j: k = 128 g + 32 kb + 8 j + 0..7
-      const u32x4 v = xw[16 * col + ((4 * kb + j) ^ col)];
-      a[j] = as_bf16x8(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
-                       __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
-    }
-    // -136 * sum of this group's x for the lane's 4 output rows
-    f32x4 c0 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], bneg, c0, 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const u32x4 wv = wb[t];
-      const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
-      f32x4 tmp = c0;
+    if constexpr (MT == 1) {
+      bf16x8 a[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8 b = as_bf16x8(magic_pair_interleaved(wd[j], 0), magic_pair_interleaved(wd[j], 1),
-                                   magic_pair_interleaved(wd[j], 2), magic_pair_interleaved(wd[j], 3));
-        tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b, tmp, 0, 0, 0);
+        // row m = col, piece 4 kb + j: k = 128 g + 32 kb + 8 j + 0..7
+        const u32x4 v = xw[16 * col + ((4 * kb + j) ^ col)];
+        a[j] = as_bf16x8(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                         __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
       }
-      const float sc = bf16f(SLDS ? scl[sb[t]] : sb[t]);
-      acc[t].x = fmaf(sc, tmp.x, acc[t].x);
-      acc[t].y = fmaf(sc, tmp.y, acc[t].y);
-      acc[t].z = fmaf(sc, tmp.z, acc[t].z);
-      acc[t].w = fmaf(sc, tmp.w, acc[t].w);
+      // -136 * sum of this group's x for the lane's 4 output rows
+      f32x4 c0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], bneg, c0, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const u32x4 wv = wb[t];
+        const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+        f32x4 tmp = c0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 b = as_bf16x8(magic_pair_interleaved(wd[j], 0), magic_pair_interleaved(wd[j], 1),
+                                     magic_pair_interleaved(wd[j], 2), magic_pair_interleaved(wd[j], 3));
+          tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b, tmp, 0, 0, 0);
+        }
+        const float sc = bf16f(SLDS ? scl[sb[t]] : sb[t]);
+        acc[0][t].x = fmaf(sc, tmp.x, acc[0][t].x);
+        acc[0][t].y = fmaf(sc, tmp.y, acc[0][t].y);
+        acc[0][t].z = fmaf(sc, tmp.z, acc[0][t].z);
+        acc[0][t].w = fmaf(sc, tmp.w, acc[0][t].w);
+      }
+    } else {
+      // two row tiles: the weight operands are dequantised once for both
+      bf16x8 bw[NT][4];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const u32x4 wv = wb[t];
+        const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bw[t][j] = as_bf16x8(magic_pair_interleaved(wd[j], 0), magic_pair_interleaved(wd[j], 1),
+                               magic_pair_interleaved(wd[j], 2), magic_pair_interleaved(wd[j], 3));
+      }
+      float sc[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sc[t] = bf16f(SLDS ? scl[sb[t]] : sb[t]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        bf16x8 a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // row m = 16 mt + col, piece 4 kb + j
+          const u32x4 v = xw[16 * (16 * mt + col) + ((4 * kb + j) ^ col)];
+          a[j] = as_bf16x8(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                           __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+        }
+        f32x4 c0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], bneg, c0, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          f32x4 tmp = c0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], bw[t][j], tmp, 0, 0, 0);
+          acc[mt][t].x = fmaf(sc[t], tmp.x, acc[mt][t].x);
+          acc[mt][t].y = fmaf(sc[t], tmp.y, acc[mt][t].y);
+          acc[mt][t].z = fmaf(sc[t], tmp.z, acc[mt][t].z);
+          acc[mt][t].w = fmaf(sc[t], tmp.w, acc[mt][t].w);
+        }
+      }
     }
   };
 
@@ -210,37 +255,43 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
   if (WAVES > 1) {
     if (wave > 0) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) red[wave - 1][t][lane] = acc[t];
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) red[wave - 1][mt][t][lane] = acc[mt][t];
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int v = 0; v < WAVES - 1; ++v) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const f32x4 p = red[v][t][lane];
-        acc[t].x += p.x;
-        acc[t].y += p.y;
-        acc[t].z += p.z;
-        acc[t].w += p.w;
-      }
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const f32x4 p = red[v][mt][t][lane];
+          acc[mt][t].x += p.x;
+          acc[mt][t].y += p.y;
+          acc[mt][t].z += p.z;
+          acc[mt][t].w += p.w;
+        }
     }
   }
 
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int n = nb + 16 * t + col;
-    if (n >= N) continue;
-    const float vals[4] = {acc[t].x, acc[t].y, acc[t].z, acc[t].w};
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * kb + i;
-      if (m < M) {
-        if (ws == nullptr) y[(size_t)m * N + n] = to_bf16(vals[i]);
-        else ws[((size_t)slice * M + m) * N + n] = vals[i];
+    for (int t = 0; t < NT; ++t) {
+      const int n = nb + 16 * t + col;
+      if (n >= N) continue;
+      const float vals[4] = {acc[mt][t].x, acc[mt][t].y, acc[mt][t].z, acc[mt][t].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * kb + i;
+        if (m < M) {
+          if (ws == nullptr) y[(size_t)m * N + n] = to_bf16(vals[i]);
+          else ws[((size_t)slice * M + m) * N + n] = vals[i];
+        }
       }
     }
-  }
 }
 
 // ---------------------------------------------------------------- streaming layout
@@ -505,7 +556,7 @@ hipError_t launch_skinny_stream(const uint16_t* x, const uint8_t* w, const uint1
   return hipErrorInvalidValue;
 }
 
-template <int NT, int WV, int XR>
+template <int NT, int WV, int XR, int MT = 1>
 static hipError_t launch_skinny_t(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                                   int M, int N, int K, int gps, int sk, hipStream_t stream) {
   dim3 grid((N + 16 * NT - 1) / (16 * NT), sk);
@@ -513,28 +564,34 @@ static hipError_t launch_skinny_t(const uint16_t* x, const uint8_t* w, const uin
   if (gps <= kSkinnyMaxScaleGroups) {
     const size_t dyn = ((size_t)16 * NT * gps * 2 + 15) & ~(size_t)15;
     static std::atomic<uint64_t> lds_set{0};   // per instantiation and device
-    const hipError_t ea = ensure_dyn_lds(reinterpret_cast<const void*>(&skinny_kernel<NT, WV, true, XR>),
+    const hipError_t ea = ensure_dyn_lds(reinterpret_cast<const void*>(&skinny_kernel<NT, WV, true, XR, MT>),
                                          16 * NT * kSkinnyMaxScaleGroups * 2, lds_set);
     if (ea != hipSuccess) return ea;
-    hipLaunchKernelGGL((skinny_kernel<NT, WV, true, XR>), grid, dim3(64 * WV), dyn, stream, x, w, s, y, ws, M, N,
-                       K, gps);
+    hipLaunchKernelGGL((skinny_kernel<NT, WV, true, XR, MT>), grid, dim3(64 * WV), dyn, stream, x, w, s, y, ws, M,
+                       N, K, gps);
   } else {
-    hipLaunchKernelGGL((skinny_kernel<NT, WV, false, XR>), grid, dim3(64 * WV), 0, stream, x, w, s, y, ws, M, N, K,
-                       gps);
+    hipLaunchKernelGGL((skinny_kernel<NT, WV, false, XR, MT>), grid, dim3(64 * WV), 0, stream, x, w, s, y, ws, M, N,
+                       K, gps);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_skinny(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                          int M, int N, int K, int gps, int sk, int nt, int waves, hipStream_t stream) {
-  if (M < 1 || M > 16) return hipErrorInvalidValue;
-  // only the row quads of X that hold rows < M are loaded
-#define W4A16_SKINNY(NTT, WV)                                                                   \
-  if (nt == NTT && waves == WV) {                                                               \
-    if (M <= 4) return launch_skinny_t<NTT, WV, 1>(x, w, s, y, ws, M, N, K, gps, sk, stream);  \
-    if (M <= 8) return launch_skinny_t<NTT, WV, 2>(x, w, s, y, ws, M, N, K, gps, sk, stream);  \
-    if (M <= 12) return launch_skinny_t<NTT, WV, 3>(x, w, s, y, ws, M, N, K, gps, sk, stream); \
-    return launch_skinny_t<NTT, WV, 4>(x, w, s, y, ws, M, N, K, gps, sk, stream);              \
+  if (M < 1 || M > kSkinnyMaxRows) return hipErrorInvalidValue;
+  // only the row quads of X that hold rows < M are loaded; two row tiles of
+  // 16 past 16 rows (8 waves of 1 or 2 column tiles)
+#define W4A16_SKINNY(NTT, WV)                                                                           \
+  if (nt == NTT && waves == WV) {                                                                       \
+    if (M <= 4) return launch_skinny_t<NTT, WV, 1>(x, w, s, y, ws, M, N, K, gps, sk, stream);          \
+    if (M <= 8) return launch_skinny_t<NTT, WV, 2>(x, w, s, y, ws, M, N, K, gps, sk, stream);          \
+    if (M <= 12) return launch_skinny_t<NTT, WV, 3>(x, w, s, y, ws, M, N, K, gps, sk, stream);         \
+    if (M <= 16) return launch_skinny_t<NTT, WV, 4>(x, w, s, y, ws, M, N, K, gps, sk, stream);         \
+    if constexpr (WV == 8 && NTT <= 2) {                                                               \
+      if (M <= 24) return launch_skinny_t<NTT, WV, 6, 2>(x, w, s, y, ws, M, N, K, gps, sk, stream);    \
+      return launch_skinny_t<NTT, WV, 8, 2>(x, w, s, y, ws, M, N, K, gps, sk, stream);                 \
+    }                                                                                                   \
+    return hipErrorInvalidValue;                                                                        \
   }
   W4A16_SKINNY(1, 4)
   W4A16_SKINNY(2, 4)

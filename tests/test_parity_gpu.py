@@ -133,6 +133,14 @@ SKINNY_CASES = [
     (12, 300, 640, 1, 41),
     (13, 257, 384, 1, 84),
     (4, 100, 40960, 1, 82),       # a slice too long to stage its scales in LDS (320 groups)
+    # two row tiles of 16 (17 <= M <= 32; 6 or 8 row quads), 8 waves of 1 or 2 column tiles
+    (17, 300, 640, 1, 82),
+    (20, 257, 1024, 2, 81),
+    (24, 513, 2048, 4, 82),
+    (25, 100, 384, 16, 82),       # more slices than groups
+    (31, 1000, 1024, 1, 81),
+    (32, 8192, 1024, 0, 82),
+    (32, 300, 40960, 1, 82),      # a slice too long to stage its scales in LDS
     # streaming layout: 1000 + 100 * row tiles + 10 * units in flight + waves / 4
     (1, 256, 512, 1, 1131),
     (3, 17, 384, 1, 1121),        # fewer rows than one 16-row block
