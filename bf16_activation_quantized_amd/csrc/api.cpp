@@ -52,16 +52,21 @@ int skinny_default_variant(int64_t M) { return M <= 8 ? 81 : 82; }
 
 bool skinny_streaming(int variant) { return variant >= 1000; }
 
-Path auto_path(int64_t M, int64_t K, int32_t sk) {
+int device_cus();
+
+Path auto_path(int64_t M, int64_t N, int64_t K, int32_t sk) {
   const int64_t Gk = K / kGroup;
   if (M == 1) {
     // the GEMV keeps a lane's x in registers: at most 64 groups per slice
     const int64_t s = sk > 0 ? sk : 16;
     return ceil_div(Gk, s) <= 64 ? kPathGemv : kPathSkinny;
   }
-  // up to two row tiles of 16: at 17 <= M <= 32 the small-batch kernel ran
-  // 6-33 % faster than the tile kernel (17408 x 5120, 8192 x 8192, 2560 x 9728)
-  if (M <= w4a16::kSkinnyMaxRows) return kPathSkinny;
+  if (M <= 16) return kPathSkinny;
+  // two row tiles of 16 (one 8-wave workgroup per compute unit per round):
+  // at 17 <= M <= 32 the small-batch kernel ran 6-33 % faster than the tile
+  // kernel at 17408 x 5120, 8192 x 8192 and 2560 x 9728 (at most 2.1 rounds
+  // of workgroups), 4-12 % slower at 28672 x 8192 (3.5 rounds)
+  if (M <= w4a16::kSkinnyMaxRows && ceil_div(N, 32) <= 3 * (int64_t)device_cus()) return kPathSkinny;
   return kPathTile;
 }
 
@@ -149,14 +154,15 @@ int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg, int
         while (sk < 16 && blocks * sk < 1024 && sk * 2 <= Gk) sk <<= 1;
         break;
       }
-      // the most slices that still fit one round of one workgroup per compute
-      // unit (a second, partly filled round of slices costs more than it
-      // saves: 2560 x 9728 ran 20 % faster at SK 2 than at 4), every wave
-      // keeping at least one group
+      // split only while fewer than half of the compute units have a
+      // workgroup: the reduce kernel and the partials cost more than the
+      // shorter slices save once the grid is half full (4096 x 4096, 128
+      // workgroups: SK 1 8-16 % faster than 2; 2560 x 9728, 80 workgroups:
+      // SK 2 20 % faster than 4), every wave keeping at least one group
       const int v = variant > 0 ? variant : skinny_default_variant(M);
       const int nt = v % 10, waves = v / 10;
       const int64_t wgs = ceil_div(N, 16 * (int64_t)std::max(nt, 1));
-      while (sk < 16 && wgs * sk * 2 <= device_cus() && ceil_div(Gk, (int64_t)sk * 2) >= waves) sk <<= 1;
+      while (sk < 16 && wgs * sk < device_cus() / 2 && ceil_div(Gk, (int64_t)sk * 2) >= waves) sk <<= 1;
       break;
     }
     case kPathTile: {
@@ -273,7 +279,7 @@ w4a16_status make_batched_plan(int32_t B, int64_t M, int64_t N, int64_t K, int32
 w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg, int32_t gs,
                        Plan* p) {
   const int64_t Gk = K / kGroup;
-  Path path = gs == kGroup ? auto_path(M, K, split_k) : kPathTile;
+  Path path = gs == kGroup ? auto_path(M, N, K, split_k) : kPathTile;
   int variant = -1;
   if (cfg != nullptr) {
     if (cfg->path < 0 || cfg->path > 3) return W4A16_ERR_SHAPE;
