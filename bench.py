@@ -280,7 +280,7 @@ def bench_dispatch(N, K, Ms, steps=20):
         cands = [("auto", None, None, 0)]
         if M == 1:
             cands += [("gemv", w4.PATH_GEMV, None, sk) for sk in (1, 2, 4)]
-        if M <= 32:
+        if M <= 48:
             cands += [("small-batch", w4.PATH_SKINNY, None, sk) for sk in (1, 2, 4, 8)]
         if M > 1:
             for cfg in (2, 3, 4, 5, 6):

@@ -48,7 +48,7 @@ constexpr int kGemvDefaultVariant = 2110;
 // runs at the same rate): one column tile per wave up to 8 rows, two above
 // (at 17408 x 5120 and 8192 x 8192, rotated weights: M = 2-4 7-10 % faster
 // with one tile, M >= 9 4-12 % faster with two).
-int skinny_default_variant(int64_t M) { return M <= 8 ? 81 : 82; }
+int skinny_default_variant(int64_t M) { return M <= 8 || M > 32 ? 81 : 82; }
 
 bool skinny_streaming(int variant) { return variant >= 1000; }
 
@@ -66,7 +66,11 @@ Path auto_path(int64_t M, int64_t N, int64_t K, int32_t sk) {
   // at 17 <= M <= 32 the small-batch kernel ran 6-33 % faster than the tile
   // kernel at 17408 x 5120, 8192 x 8192 and 2560 x 9728 (at most 2.1 rounds
   // of workgroups), 4-12 % slower at 28672 x 8192 (3.5 rounds)
-  if (M <= w4a16::kSkinnyMaxRows && ceil_div(N, 32) <= 3 * (int64_t)device_cus()) return kPathSkinny;
+  if (M <= 32 && ceil_div(N, 32) <= 3 * (int64_t)device_cus()) return kPathSkinny;
+  // three row tiles (8 waves of one column tile): only while one round of
+  // workgroups covers N (4096 x 4096 and 2560 x 9728 at 33-48 rows: 8-35 %
+  // faster than the tile kernel; 8192 x 8192, two rounds: 15-30 % slower)
+  if (M <= w4a16::kSkinnyMaxRows && ceil_div(N, 16) <= (int64_t)device_cus()) return kPathSkinny;
   return kPathTile;
 }
 
@@ -291,8 +295,8 @@ w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w
   if (path != kPathTile && gs != kGroup) return W4A16_ERR_GROUP_SIZE;
   if (path == kPathSkinny && variant <= 0) variant = skinny_default_variant(M);
   // past 16 rows (two row tiles): the group-striped layout with 8 waves of
-  // 1 or 2 column tiles only
-  if (path == kPathSkinny && M > 16 && !(variant == 81 || variant == 82)) return W4A16_ERR_SHAPE;
+  // 1 or 2 column tiles only; past 32 rows (three row tiles) of 1
+  if (path == kPathSkinny && M > 16 && !(variant == 81 || (variant == 82 && M <= 32))) return W4A16_ERR_SHAPE;
   int tile_cfg = 0;
   if (path == kPathTile) {
     tile_cfg = variant >= 0 ? variant : default_tile_cfg(M, N, K, split_k, gs);

@@ -41,9 +41,9 @@ constexpr int kSkinnyStreamMaxGroups = 32;
 // slices of at most this many groups stage their scales in LDS (16 NT x gps x 2
 // bytes, at most 32 KiB)
 constexpr int kSkinnyMaxScaleGroups = 256;
-// rows of the small-batch kernel: 16 per row tile, two row tiles with 8
-// waves of 1 or 2 column tiles
-constexpr int kSkinnyMaxRows = 32;
+// rows of the small-batch kernel: 16 per row tile, two or three row tiles
+// with 8 waves of 1 or 2 column tiles
+constexpr int kSkinnyMaxRows = 48;
 hipError_t launch_skinny_stream(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                                 int M, int N, int K, int gps, int sk, int nt, int depth, int waves, int gb,
                                 hipStream_t stream);

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
                                                             uint16_t* __restrict__ y,
                                                             float* __restrict__ ws,
                                                             int M, int N, int K, int gps) {
-  static_assert(XR >= 1 && XR <= 4 * MT && (MT == 1 || MT == 2), "row quads within the row tiles");
+  static_assert(XR >= 1 && XR <= 4 * MT && MT >= 1 && MT <= 3, "row quads within the row tiles");
   __shared__ f32x4 red[WAVES > 1 ? (WAVES - 1) : 1][MT][NT][64];
   // per-wave staging of one group of X: [16 MT rows][16 slots of 16 bytes],
   // the piece p of row r in slot p ^ (r & 15) (conflict-free for both access
@@ -580,7 +580,8 @@ hipError_t launch_skinny(const uint16_t* x, const uint8_t* w, const uint16_t* s,
                          int M, int N, int K, int gps, int sk, int nt, int waves, hipStream_t stream) {
   if (M < 1 || M > kSkinnyMaxRows) return hipErrorInvalidValue;
   // only the row quads of X that hold rows < M are loaded; two row tiles of
-  // 16 past 16 rows (8 waves of 1 or 2 column tiles)
+  // 16 past 16 rows (8 waves of 1 or 2 column tiles), three past 32 rows (8
+  // waves of 1 column tile)
 #define W4A16_SKINNY(NTT, WV)                                                                           \
   if (nt == NTT && waves == WV) {                                                                       \
     if (M <= 4) return launch_skinny_t<NTT, WV, 1>(x, w, s, y, ws, M, N, K, gps, sk, stream);          \
@@ -589,7 +590,11 @@ hipError_t launch_skinny(const uint16_t* x, const uint8_t* w, const uint16_t* s,
     if (M <= 16) return launch_skinny_t<NTT, WV, 4>(x, w, s, y, ws, M, N, K, gps, sk, stream);         \
     if constexpr (WV == 8 && NTT <= 2) {                                                               \
       if (M <= 24) return launch_skinny_t<NTT, WV, 6, 2>(x, w, s, y, ws, M, N, K, gps, sk, stream);    \
-      return launch_skinny_t<NTT, WV, 8, 2>(x, w, s, y, ws, M, N, K, gps, sk, stream);                 \
+      if (M <= 32) return launch_skinny_t<NTT, WV, 8, 2>(x, w, s, y, ws, M, N, K, gps, sk, stream);    \
+      if constexpr (NTT == 1) { /* three row tiles: one column tile fits the registers */               \
+        if (M <= 40) return launch_skinny_t<NTT, WV, 10, 3>(x, w, s, y, ws, M, N, K, gps, sk, stream); \
+        return launch_skinny_t<NTT, WV, 12, 3>(x, w, s, y, ws, M, N, K, gps, sk, stream);              \
+      }                                                                                                 \
     }                                                                                                   \
     return hipErrorInvalidValue;                                                                        \
   }

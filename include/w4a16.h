@@ -82,8 +82,8 @@ w4a16_status w4a16_pack_int4(const uint8_t* q, uint8_t* w_packed,
 /*
  * The split-K factor the library uses for w4a16_gemm with group_size 128
  * when split_k == 0 (auto) at this shape: for the M = 1 GEMV only what its register budget for
- * x needs (at most 64 groups per slice), for the M <= 32 kernel the most
- * slices that still fit one round of one workgroup per compute unit, and
+ * x needs (at most 64 groups per slice), for the M <= 48 kernel slices
+ * only while fewer than half of the compute units have a workgroup, and
  * for the tile kernel the power of
  * two (at most 16) of least estimated time among those that keep tiles x SK
  * within one workgroup per compute unit, counting the fp32 partials and the
@@ -96,7 +96,8 @@ int32_t w4a16_gemm_auto_split_k(int64_t M, int64_t N, int64_t K);
 /*
  * Bytes of workspace w4a16_gemm needs at this shape and split_k (0 = auto)
  * with group_size 128: SK * M * N * 4 (rounded up to 256) when the effective
- * split factor SK > 1, plus, when M > 32 (the tile kernel), (K/128) *
+ * split factor SK > 1, plus, on the tile kernel (M > 16 where the small-
+ * batch kernel does not take the shape), (K/128) *
  * round_up(M, 4) * 4 for the per-row group sums of X. Returns 0 when none is
  * needed and for invalid arguments. w4a16_gemm_workspace_bytes_gs gives it
  * for either group size.
@@ -115,7 +116,7 @@ size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K,
  *   M >= 0 (M == 0: returns W4A16_OK, nothing enqueued), N >= 1, K >= 128.
  *   group_size: 128, or 32; K % 128 == 0 either way. Group size 32 always
  *               runs the tile kernel (path 3, configurations 2 to 5), at any
- *               M: the M = 1 and M <= 32 kernels take 128-groups only.
+ *               M: the M = 1 and M <= 48 kernels take 128-groups only.
  *   split_k   : 0 = auto, or 1, 2, 4, 8, 16. With SK > 1 the K range is cut
  *               into SK contiguous slices of ceil((K/128)/SK) blocks of 128 k
  *               (trailing slices may be empty); slice s writes its fp32 partial sums to
@@ -236,8 +237,10 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  * The result of a forced path still satisfies the same contract.
  *   path   : 0 = automatic, 1 = M == 1 GEMV (at most 64 groups per split-K
  *            slice),
- *            2 = M <= 32 MFMA 16x16x32 small-batch kernel (one row tile of
- *            16, two past 16 rows), 3 = MFMA tile kernel
+ *            2 = M <= 48 MFMA 16x16x32 small-batch kernel (one row tile of
+ *            16, two past 16 rows, three past 32; automatic for M <= 16,
+ *            for M <= 32 while ceil(N/32) <= 3 x compute units, for M <= 48
+ *            while ceil(N/16) <= compute units), 3 = MFMA tile kernel
  *            (LDS-staged; the only path of the grouped call)
  *   variant: -1 = default for the path; otherwise
  *            path 1: 1000 * layout + layout digits.
@@ -274,8 +277,9 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  *            workgroup per compute unit times rows per tile, weighted by
  *            each height's measured per-row rate (the grouped call
  *            estimates ceil(M_total/h) + G/2 row tiles per column).
- * An unavailable combination (e.g. path 1 with M != 1, path 2 with M > 32,
- * or with M > 16 and a variant other than 81 or 82)
+ * An unavailable combination (e.g. path 1 with M != 1, path 2 with M > 48,
+ * with M > 16 and a variant other than 81 or 82, or with M > 32 and a
+ * variant other than 81)
  * returns W4A16_ERR_SHAPE; path 1 or 2 with group_size 32 returns
  * W4A16_ERR_GROUP_SIZE.
  */

@@ -139,13 +139,16 @@ def test_explicit_path_errors():
     cfg = w4._Config(1, -1)   # GEMV path forced at M=2
     st = L().w4a16_gemm_ex(A, B, C, D, 2, 64, 128, 128, 0, None, 0, None, ctypes.byref(cfg))
     assert st == ERR_SHAPE
-    cfg = w4._Config(2, -1)   # small-batch path forced at M=33 (two row tiles of 16 at most)
-    st = L().w4a16_gemm_ex(A, B, C, D, 33, 64, 128, 128, 0, None, 0, None, ctypes.byref(cfg))
+    cfg = w4._Config(2, -1)   # small-batch path forced at M=49 (three row tiles of 16 at most)
+    st = L().w4a16_gemm_ex(A, B, C, D, 49, 64, 128, 128, 0, None, 0, None, ctypes.byref(cfg))
     assert st == ERR_SHAPE
     for v in (41, 42, 44, 84, 1121):   # past 16 rows only 8 waves of 1 or 2 column tiles
         cfg = w4._Config(2, v)
         st = L().w4a16_gemm_ex(A, B, C, D, 20, 64, 128, 128, 1, None, 0, None, ctypes.byref(cfg))
         assert st == ERR_SHAPE, v
+    cfg = w4._Config(2, 82)   # past 32 rows only 1 column tile per wave
+    st = L().w4a16_gemm_ex(A, B, C, D, 40, 64, 128, 128, 1, None, 0, None, ctypes.byref(cfg))
+    assert st == ERR_SHAPE
     cfg = w4._Config(7, -1)
     st = L().w4a16_gemm_ex(A, B, C, D, 2, 64, 128, 128, 0, None, 0, None, ctypes.byref(cfg))
     assert st == ERR_SHAPE

@@ -141,6 +141,13 @@ SKINNY_CASES = [
     (31, 1000, 1024, 1, 81),
     (32, 8192, 1024, 0, 82),
     (32, 300, 40960, 1, 82),      # a slice too long to stage its scales in LDS
+    # three row tiles (33 <= M <= 48; 10 or 12 row quads), 8 waves of 1 column tile
+    (33, 300, 640, 1, 81),
+    (40, 257, 1024, 2, 81),
+    (41, 513, 2048, 4, 81),
+    (48, 100, 384, 16, 81),       # more slices than groups
+    (48, 1000, 1024, 0, None),    # forced path, default variant and split
+    (47, 300, 40960, 1, 81),      # a slice too long to stage its scales in LDS
     # streaming layout: 1000 + 100 * row tiles + 10 * units in flight + waves / 4
     (1, 256, 512, 1, 1131),
     (3, 17, 384, 1, 1121),        # fewer rows than one 16-row block
