@@ -283,7 +283,7 @@ def bench_dispatch(N, K, Ms, steps=20):
         if M <= 48:
             cands += [("small-batch", w4.PATH_SKINNY, None, sk) for sk in (1, 2, 4, 8)]
         if M > 1:
-            for cfg in (2, 3, 4, 5, 6):
+            for cfg in (2, 3, 4, 5, 6, 7, 8):
                 for sk in ((1, 2, 4, 8) if M < 1024 else (1, 2)):
                     cands.append((f"tile{cfg}", w4.PATH_TILE, cfg, sk))
         res = []

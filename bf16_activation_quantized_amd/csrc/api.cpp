@@ -127,7 +127,10 @@ int32_t tile_split_rate(int64_t M, int64_t N, int64_t Gk, int64_t tiles, int bm,
 // at 1322 x 19456 x 2560 on one box: 4 rounds of 128 rows 166 us, 4 of 112
 // rows 161 us, 3 of 144 rows 146 us, 5 of 96 rows 176 us)
 struct TileCand { int cfg, bm; double rate; };
-constexpr TileCand kTileCands[] = {{2, 128, 1.0}, {6, 144, 0.96}, {4, 112, 0.91}, {3, 96, 0.907}, {5, 80, 0.85}};
+// (64 and 48 rows, measured at 40-64 rows of 17408 x 5120 and 8192 x 8192
+// against 80: 0.70 and 0.55)
+constexpr TileCand kTileCands[] = {{2, 128, 1.0},  {6, 144, 0.96}, {4, 112, 0.91}, {3, 96, 0.907},
+                                   {5, 80, 0.85},  {7, 64, 0.70},  {8, 48, 0.55}};
 
 double tile_rate(int cfg) {
   for (const TileCand& c : kTileCands)

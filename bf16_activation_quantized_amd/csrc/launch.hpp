@@ -60,7 +60,7 @@ hipError_t launch_rowsum_neg136(const uint16_t* x, float* out, int M, int K, int
 hipError_t launch_tile(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
                        float* ws, const int32_t* m_sizes, int m_uniform, int M_total, int N, int K, int G, int ld,
                        int gps, int sk, int cfg, int gsize, hipStream_t stream);
-// LDS-DMA tile kernel: (16 row_tiles) x 256 output tiles (row_tiles = 5 .. 9);
+// LDS-DMA tile kernel: (16 row_tiles) x 256 output tiles (row_tiles = 3 .. 9);
 // same contract as launch_tile.
 hipError_t launch_prefill(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
                           float* ws, const int32_t* m_sizes, int m_uniform, int M_total, int N, int K, int G,

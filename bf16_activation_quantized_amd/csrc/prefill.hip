@@ -10,7 +10,7 @@
 // accumulator. No weight is ever rounded.
 //
 // Structure (one 512-thread workgroup per (16 MS) x 256 output tile, 8 waves
-// of (16 MS) x 32, MS = 5 .. 9; one workgroup per compute unit):
+// of (16 MS) x 32, MS = 3 .. 9; one workgroup per compute unit):
 //  * one K-stage = one 128-group: X [16 MS rows, 128 k] bf16, the packed
 //    weights [256 rows, 64 B] (16 KiB, still 4-bit) and the 16 MS row sums;
 //    NSTAGE stages in LDS, filled by buffer loads that write LDS directly (no
@@ -469,6 +469,8 @@ hipError_t launch_prefill(const uint16_t* x, const uint8_t* w, const uint16_t* s
     case 7: return launch_prefill_t<3, 7>(a, sk, stream);     // 112 x 256 tiles, 3 x 44.4 KiB stages
     case 6: return launch_prefill_t<3, 6>(a, sk, stream);     // 96 x 256 tiles, 3 x 40.4 KiB stages
     case 5: return launch_prefill_t<3, 5>(a, sk, stream);     // 80 x 256 tiles, 3 x 36.3 KiB stages
+    case 4: return launch_prefill_t<3, 4>(a, sk, stream);     // 64 x 256 tiles, 3 x 32.3 KiB stages
+    case 3: return launch_prefill_t<3, 3>(a, sk, stream);     // 48 x 256 tiles, 3 x 28.2 KiB stages
     default: return hipErrorInvalidValue;
   }
 }

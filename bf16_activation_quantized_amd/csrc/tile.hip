@@ -336,20 +336,21 @@ static hipError_t launch_tile_t(const TileArgs& a0, int mtiles_bound, int sk, hi
 //   1: 128 x 128, 2 x 2 waves of 64 x 64, weights dequantised into LDS
 //   2: 128 x 256, 8 waves of 128 x 32, LDS-DMA staging, 3 stages (prefill.hip)
 struct TileCfg { int bm, bn; };
-static const TileCfg kTileCfgs[] = {{128, 256}, {128, 128}, {128, 256}, {96, 256}, {112, 256}, {80, 256}, {144, 256}};
+static const TileCfg kTileCfgs[] = {{128, 256}, {128, 128}, {128, 256}, {96, 256}, {112, 256},
+                                    {80, 256},  {144, 256}, {64, 256},  {48, 256}};
 int tile_num_cfgs() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0])); }
 int tile_bm(int cfg) { return kTileCfgs[cfg].bm; }
 int tile_bn(int cfg) { return kTileCfgs[cfg].bn; }
 bool tile_group_ok(int cfg, int gsize) {
   if (cfg < 0 || cfg >= tile_num_cfgs()) return false;
-  return gsize == 128 || (gsize == 32 && cfg >= 2 && kTileCfgs[cfg].bm <= 128);
+  return gsize == 128 || (gsize == 32 && cfg >= 2 && cfg <= 5);
 }
 
 hipError_t launch_tile(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
                        float* ws, const int32_t* m_sizes, int m_uniform, int M_total, int N, int K, int G, int ld,
                        int gps, int sk, int cfg, int gsize, hipStream_t stream) {
   if (cfg < 0 || cfg >= tile_num_cfgs()) return hipErrorInvalidValue;
-  if (cfg >= 2)   // LDS-DMA kernel: 8 (cfg 2), 6 (cfg 3), 7 (cfg 4), 5 (cfg 5) or 9 (cfg 6) row tiles of 16
+  if (cfg >= 2)   // LDS-DMA kernel: 8 (cfg 2), 6 (3), 7 (4), 5 (5), 9 (6), 4 (7) or 3 (8) row tiles of 16
     return launch_prefill(x, w, s, sxn, y, ws, m_sizes, m_uniform, M_total, N, K, G, ld, gps, sk,
                           kTileCfgs[cfg].bm / 16, gsize, stream);
   if (gsize != 128) return hipErrorInvalidValue;   // configs 0 and 1: 128-groups only

@@ -270,11 +270,12 @@ w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
  *            runs the default of the first form; path 3: tile
  *            configuration index (0: 128x256 and 1: 128x128 with weights
  *            dequantised into LDS; 2: 128x256 with LDS-DMA staging, 8
- *            waves, 3 LDS stages; 3, 4, 5, 6: the same with 96x256,
- *            112x256, 80x256 and 144x256 tiles; group_size 32 runs on 2 to
- *            5 only, W4A16_ERR_GROUP_SIZE otherwise). By default the call
- *            picks among 2 to 6 (2 to 5 for group_size 32) the tile height with the fewest rounds of one
- *            workgroup per compute unit times rows per tile, weighted by
+ *            waves, 3 LDS stages; 3, 4, 5, 6, 7, 8: the same with 96x256,
+ *            112x256, 80x256, 144x256, 64x256 and 48x256 tiles; group_size
+ *            32 runs on 2 to 5 only, W4A16_ERR_GROUP_SIZE otherwise). By
+ *            default the call picks among 2 to 8 (2 to 5 for group_size 32)
+ *            the tile height and split with the least estimated time: the
+ *            rounds of one workgroup per compute unit times rows per tile, weighted by
  *            each height's measured per-row rate (the grouped call
  *            estimates ceil(M_total/h) + G/2 row tiles per column).
  * An unavailable combination (e.g. path 1 with M != 1, path 2 with M > 48,

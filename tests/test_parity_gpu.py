@@ -221,6 +221,15 @@ TILE_CASES = [
     (257, 300, 256, 8, 6),
     (1322, 512, 2560, 1, 6),
     (143, 129, 512, 0, 6),
+    # 7 = 64 x 256 and 8 = 48 x 256 tiles (16 and 12 X DMA blocks over 8 waves)
+    (17, 100, 128, 1, 7),
+    (65, 256, 256, 1, 7),     # one row past a 64-row tile
+    (300, 1000, 640, 2, 7),
+    (1322, 512, 2560, 1, 7),
+    (17, 100, 128, 1, 8),
+    (49, 256, 256, 1, 8),     # one row past a 48-row tile
+    (300, 1000, 640, 8, 8),
+    (47, 129, 512, 0, 8),
     # 5 = 80 x 256 tiles (20 X DMA blocks over 8 waves)
     (17, 100, 128, 1, 5),
     (81, 256, 256, 1, 5),
@@ -265,6 +274,8 @@ GROUPED_CASES = [
     ([80, 81, 79, 0, 1], 256, 640, 5),
     ([0, 0, 0, 0, 0, 0, 0, 700], 512, 256, 5),      # all rows in the last group
     ([144, 145, 143, 0, 1], 256, 640, 6),           # 144-row tiles
+    ([64, 65, 63, 0, 1], 256, 640, 7),              # 64-row tiles
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 8),   # 48-row tiles
 ]
 
 
