@@ -37,6 +37,10 @@ METRIC = "effective weight GB/s at M=1 decode; TFLOP/s at M=1322 prefill (1x MI3
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROTATE_BYTES = 512 << 20
+# GPU work run back to back before the timed replay (clock settling)
+SETTLE_S = 0.05
+# spin before the timed replay (GPU clock cycles, about a millisecond)
+PREROLL_CYCLES = 2_000_000
 # the decode GEMV at M=1, N=17408, K=5120, split_k 1 (40 groups per slice ->
 # 2-row blocks, 5 instructions per block; one block in flight; one 8-wave
 # workgroup per compute unit, x in registers)
@@ -79,14 +83,15 @@ class Dev:
         torch.cuda.synchronize()
 
 
-def time_steps(step, steps, warmup, settle_s=0.03):
+def time_steps(step, steps, warmup, settle_s=SETTLE_S):
     """W untimed eager warmup steps; then the K steps are captured once in a
     HIP graph on a side stream (the library enqueues only kernels, so the
-    capture is exact) and replayed untimed (graph upload, then until about
-    `settle_s` of GPU work has run, so that the clocks have left their idle
-    state; at most 20 replays), and the timed region is one replay of exactly
-    K steps bracketed by synchronisations and HIP events on that stream.
-    Returns (total seconds, seconds per step)."""
+    capture is exact) and replayed untimed until at least `settle_s` seconds
+    of GPU work have run back to back (however many replays that takes), so
+    that the clocks have left their idle state; the timed region is then one
+    replay of exactly K steps bracketed by synchronisations and HIP events on
+    that stream. The shader and memory clocks are sampled while the settling
+    replays run. Returns (total seconds, seconds per step, clock record)."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -101,19 +106,91 @@ def time_steps(step, steps, warmup, settle_s=0.03):
         g.replay()
         torch.cuda.synchronize()
         w0 = time.perf_counter()
-        for _ in range(20):
-            if time.perf_counter() - w0 >= settle_s:
-                break
+        g.replay()
+        torch.cuda.synchronize()
+        one = max(time.perf_counter() - w0, 1e-6)
+        n = max(2, int(math.ceil(settle_s / one)))
+        t_settle = time.perf_counter()
+        for _ in range(n):
             g.replay()
-            torch.cuda.synchronize()
+        done = torch.cuda.Event()
+        done.record(s)
+        clocks = CLOCKS.sample_while(done)          # while the replays run
+        torch.cuda.synchronize()
+        settled_s = time.perf_counter() - t_settle
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
+        # a spin kernel of about a millisecond ahead of the first event keeps
+        # the host's submission of the graph out of the timed region: t0 .. t1
+        # then spans the K steps' GPU execution only
+        torch.cuda._sleep(PREROLL_CYCLES)
         t0.record(s)
         g.replay()
         t1.record(s)
         torch.cuda.synchronize()
     total = t0.elapsed_time(t1) / 1e3
-    return total, total / steps
+    clocks = dict(clocks or {}, settle_replays=n, settle_ms=round(settled_s * 1e3, 2))
+    return total, total / steps, clocks
+
+
+class _Clocks:
+    """Shader / memory clock of the visible GPU from sysfs (the current DPM
+    level, marked '*'), found through the device's PCI address; None where
+    the files are not readable."""
+
+    def __init__(self):
+        self.dev_dir = None
+
+    def _find(self):
+        if self.dev_dir is not None:
+            return self.dev_dir
+        self.dev_dir = ""
+        try:
+            import torch
+            p = torch.cuda.get_device_properties(0)
+            bus = "%04x:%02x:%02x.0" % (getattr(p, "pci_domain_id", 0), p.pci_bus_id, p.pci_device_id)
+            d = os.path.join("/sys/bus/pci/devices", bus)
+            if os.path.exists(os.path.join(d, "pp_dpm_sclk")):
+                self.dev_dir = d
+        except Exception:
+            pass
+        return self.dev_dir
+
+    @staticmethod
+    def _current(path):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return line.split(":", 1)[1].strip(" *\n")
+        except OSError:
+            return None
+        return None
+
+    def sample(self):
+        d = self._find()
+        if not d:
+            return None
+        return dict(sclk=self._current(os.path.join(d, "pp_dpm_sclk")),
+                    mclk=self._current(os.path.join(d, "pp_dpm_mclk")))
+
+    def sample_while(self, event, every_s=0.004, most=12):
+        """Samples every few milliseconds until `event` has completed (the
+        GPU work queued before it is done); the samples' sclk values and the
+        last mclk."""
+        if not self._find():
+            return None
+        sclk, last = [], None
+        while len(sclk) < most:
+            last = self.sample()
+            sclk.append(last["sclk"])
+            if event.query():
+                break
+            time.sleep(every_s)
+        return dict(sclk_samples=sclk, mclk=last["mclk"])
+
+
+CLOCKS = _Clocks()
 
 
 def bench_decode(name, steps, warmup, split_k=0, path=None, variant=None):
@@ -135,9 +212,9 @@ def bench_decode(name, steps, warmup, split_k=0, path=None, variant=None):
         j = i % copies
         w4.w4a16_gemm(d.x, d.w[j], d.s[j], y=y, split_k=split_k, workspace=ws, path=path, variant=variant)
 
-    total, t = time_steps(step, steps, warmup)
+    total, t, clk = time_steps(step, steps, warmup)
     return dict(M=M, N=N, K=K, split_k=sk, weight_copies=copies, eff_weight_bytes=wb,
-                us_per_step=t * 1e6, gbs=wb / t / 1e9, frac_hbm=wb / t / 1e9 / HBM_PEAK_GBS), d, y
+                us_per_step=t * 1e6, gbs=wb / t / 1e9, frac_hbm=wb / t / 1e9 / HBM_PEAK_GBS, clocks=clk), d, y
 
 
 def bench_prefill(name, steps, warmup, variant=None):
@@ -156,10 +233,10 @@ def bench_prefill(name, steps, warmup, variant=None):
     def step(i):
         w4.w4a16_gemm(d.x, d.w[0], d.s[0], y=y, workspace=ws, path=path, variant=variant)
 
-    total, t = time_steps(step, steps, warmup)
+    total, t, clk = time_steps(step, steps, warmup)
     flops = 2.0 * M * N * K
     return dict(M=M, N=N, K=K, us_per_step=t * 1e6,
-                tflops=flops / t / 1e12, frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS), d, y
+                tflops=flops / t / 1e12, frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS, clocks=clk), d, y
 
 
 def bench_grouped(name, steps, warmup, variant=None):
@@ -171,15 +248,14 @@ def bench_grouped(name, steps, warmup, variant=None):
     c = make_config(name)
     d = Dev(c, 1)
     y = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(w4.w4a16_gemm_grouped_workspace_bytes(G, Mt, N, K) // 4 + 4, dtype=torch.float32, device="cuda")
 
     def step(i):
-        w4.w4a16_gemm_grouped(d.x, d.w[0], d.s[0], d.m_sizes, y=y, workspace=ws, variant=variant)
+        w4.w4a16_gemm_grouped(d.x, d.w[0], d.s[0], d.m_sizes, y=y, variant=variant)
 
-    total, t = time_steps(step, steps, warmup)
+    total, t, clk = time_steps(step, steps, warmup)
     flops = 2.0 * Mt * N * K
     return dict(G=G, M_total=Mt, N=N, K=K, m_sizes=[int(v) for v in c.m_sizes], us_per_step=t * 1e6,
-                tflops=flops / t / 1e12, frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS), d, y
+                tflops=flops / t / 1e12, frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS, clocks=clk), d, y
 
 
 def bench_batched(name, steps, warmup, variant=None, split_k=0):
@@ -198,10 +274,10 @@ def bench_batched(name, steps, warmup, variant=None, split_k=0):
     def step(i):
         w4.w4a16_gemm_batched(x, d.w[0], d.s[0], y=y, split_k=split_k, workspace=ws, variant=variant)
 
-    total, t = time_steps(step, steps, warmup)
+    total, t, clk = time_steps(step, steps, warmup)
     flops = 2.0 * B * M * N * K
     return dict(B=B, M=M, N=N, K=K, us_per_step=t * 1e6,
-                tflops=flops / t / 1e12, frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS), d, y
+                tflops=flops / t / 1e12, frac_bf16=flops / t / 1e12 / BF16_PEAK_TFLOPS, clocks=clk), d, y
 
 
 # the four decoder GEMMs of one layer at M = 1322 (N, K), after the per-GEMM
@@ -230,7 +306,7 @@ def bench_layers(steps, warmup, group):
         def step(i, d=d, y=y, ws=ws):
             w4.w4a16_gemm(d.x, d.w[0], d.s[0], y=y, workspace=ws, group_size=group)
 
-        _, t = time_steps(step, steps, warmup)
+        _, t, _ = time_steps(step, steps, warmup)
         flops = 2.0 * M * N * K
         out[name] = dict(N=N, K=K, us_per_step=round(t * 1e6, 2), tflops=round(flops / t / 1e12, 1))
         tot_flops += flops
@@ -252,7 +328,7 @@ def bench_pack(steps, warmup):
     def step(i):
         w4.w4a16_pack_int4(q, out=out)
 
-    total, t = time_steps(step, steps, warmup)
+    total, t, _ = time_steps(step, steps, warmup)
     return dict(rows=N, K=K, us_per_step=t * 1e6, gbs=(N * K * 1.5) / t / 1e9)
 
 
@@ -283,9 +359,9 @@ def bench_dispatch(N, K, Ms, steps=20):
         if M <= 48:
             cands += [("small-batch", w4.PATH_SKINNY, None, sk) for sk in (1, 2, 4, 8)]
         if M > 1:
-            for cfg in (2, 3, 4, 5, 6, 7, 8):
+            for rows in (48, 64, 80, 96, 112, 128, 144):
                 for sk in ((1, 2, 4, 8) if M < 1024 else (1, 2)):
-                    cands.append((f"tile{cfg}", w4.PATH_TILE, cfg, sk))
+                    cands.append((f"tile{rows}", w4.PATH_TILE, rows, sk))
         res = []
         for name, path, var, sk in cands:
             need = w4.w4a16_gemm_workspace_bytes(M, N, K, sk, path=path, variant=var)
@@ -295,7 +371,7 @@ def bench_dispatch(N, K, Ms, steps=20):
                 w4.w4a16_gemm(x, ws_[i % copies], ss_[i % copies], y=y, split_k=sk, workspace=wsp,
                               path=path, variant=var)
             try:
-                _, t = time_steps(step, steps, 3)
+                _, t, _ = time_steps(step, steps, 3)
                 res.append((t * 1e6, name, sk))
             except RuntimeError as e:   # a combination the library refuses
                 log(f"dispatch M={M} {name} sk={sk}: {e}")
@@ -306,7 +382,7 @@ def bench_dispatch(N, K, Ms, steps=20):
             w4.w4a16_gemm(x, ws_[i % copies], ss_[i % copies], y=y, split_k=0, workspace=wsp_auto)
         wsp_auto = torch.empty(max(w4.w4a16_gemm_workspace_bytes(M, N, K, 0) // 4, 1) + 4, dtype=torch.float32,
                                device="cuda")
-        _, t = time_steps(step_auto, steps, 3)
+        _, t, _ = time_steps(step_auto, steps, 3)
         auto = min(res[0], (t * 1e6, "auto", 0))
         best = min(res[1:] or res)
         r = dict(N=N, K=K, M=M, auto_us=round(auto[0], 2), best=[best[1], best[2], round(best[0], 2)],
@@ -318,32 +394,62 @@ def bench_dispatch(N, K, Ms, steps=20):
     return out
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def oracle_time(name, budget_s=6.0, max_runs=3):
+    """The CPU oracle (unpack + dequant + fp64 GEMM, numpy with a threaded
+    BLAS) on the whole of workload `name`, timed on the host cores: the median
+    of up to `max_runs` runs, fewer once `budget_s` has passed (at least one).
+    Returns seconds per run and the number of runs."""
+    import oracle
+    from synth import make_config
+    c = make_config(name)
+    p = oracle.pack_int4(c.q)
+    if name == "grouped":
+        run = lambda: oracle.gemm_grouped(c.x, p, c.s, c.m_sizes)
+    elif name == "batched":
+        B = c.G
+        xb = c.x.reshape(B, c.M // B, c.K)
+        run = lambda: oracle.gemm_batched(xb, p, c.s)
+    else:
+        run = lambda: oracle.gemm(c.x, p, c.s)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_runs:
+        t0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s:
+            break
+    return float(np.median(times)), len(times)
+
+
+def cpu_oracle_record(name, work, unit, budget_s=6.0):
+    """Per-workload oracle timing: `work` is the workload's effective weight
+    bytes (unit GB/s) or flops (unit TFLOP/s)."""
+    t, n = oracle_time(name, budget_s)
+    val = work / t / (1e9 if unit == "GB/s" else 1e12)
+    return dict(ms=round(t * 1e3, 2), value=val, unit=unit, runs=n, cores=int(_blas_threads()), kind="oracle",
+                sample=f"whole workload, unpack + dequant + fp64 GEMM, median of {n}")
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle (unpack + dequant + fp64 GEMV) on the decode workload, timed
     on the host cores."""
-    import oracle
-    from synth import make_config, CONFIGS
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    from synth import CONFIGS
+    blas_threads = _blas_threads()
     cfg = CONFIGS["decode_gemv"]
-    c = make_config("decode_gemv")
-    p = oracle.pack_int4(c.q)
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        oracle.gemm(c.x, p, c.s)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 20:
-            break
-    t = float(np.median(times))
+    t, n = oracle_time("decode_gemv", budget_s, max_runs=20)
     wb = eff_weight_bytes(cfg["N"], cfg["K"])
     return dict(value=wb / t / 1e9, unit="GB/s", cores=int(blas_threads), kind="oracle",
                 sample=f"full decode workload M=1 N={cfg['N']} K={cfg['K']} (unpack + dequant + fp64 GEMV), "
-                       f"{len(times)} runs, median {t * 1e3:.1f} ms; numpy element-wise steps single-threaded, "
+                       f"{n} runs, median {t * 1e3:.1f} ms; numpy element-wise steps single-threaded, "
                        f"BLAS with {blas_threads} threads",
                 host_cpus=os.cpu_count(), affinity_cpus=len(os.sched_getaffinity(0)),
                 cpu_model=_cpu_model())
@@ -414,6 +520,7 @@ def main():
 
     log("bench: decode_gemv (headline)")
     head, _, _ = bench_decode("decode_gemv", args.steps, args.warmup)
+    log(f"bench: decode_gemv: {head['us_per_step']:.3f} us per step, clocks {head.get('clocks')}")
     wb = head["eff_weight_bytes"]
     ms_per_step = head["us_per_step"] / 1e3
     # dominant kernel of the step: the decode GEMV, one launch per step at
@@ -450,11 +557,34 @@ def main():
         log("bench: pack")
         workloads["pack_int4"] = bench_pack(steps2, args.warmup)
         torch.cuda.empty_cache()
+        for k, r in workloads.items():
+            if "us_per_step" in r:
+                log(f"bench: {k}: {r['us_per_step']:.2f} us per step")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         cpu = cpu_baseline()
+        # the oracle beside every workload, same process (the whole workload
+        # each time, median of up to 3 runs)
+        for key, name in (("tiny", "tiny"), ("decode_splitk_skauto", "decode_splitk"), ("prefill", "prefill"),
+                          ("grouped", "grouped"), ("batched", "batched")):
+            r = workloads.get(key)
+            if r is None:
+                continue
+            log(f"bench: cpu oracle {name}")
+            if "gbs" in r:
+                rec = cpu_oracle_record(name, r["eff_weight_bytes"], "GB/s")
+                rec["gpu_over_cpu"] = round(r["gbs"] / rec["value"], 1)
+            else:
+                rows = r["M_total"] if "M_total" in r else r["M"] * r.get("B", 1)
+                flops = 2.0 * rows * r["N"] * r["K"]
+                rec = cpu_oracle_record(name, flops, "TFLOP/s")
+                rec["gpu_over_cpu"] = round(r["tflops"] / rec["value"], 1)
+            r["cpu_oracle"] = rec
+        head["cpu_oracle"] = dict(ms=round(head["eff_weight_bytes"] / cpu["value"] / 1e6, 2), value=cpu["value"],
+                                  unit="GB/s", cores=cpu["cores"], kind="oracle",
+                                  gpu_over_cpu=round(head["gbs"] / cpu["value"], 1))
 
     out = {
         "metric": METRIC,
@@ -474,7 +604,8 @@ def main():
                    "weight_copies_rotated": head["weight_copies"], "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "workloads": workloads,
+        "clocks": head.get("clocks"),
+        "workloads": dict(decode_gemv=head, **workloads),
     }
     print(json.dumps(out), flush=True)
 

@@ -1,4 +1,6 @@
-"""Python binding of the W4A16 GEMM library (libw4a16.so, C ABI in include/w4a16.h).
+"""Python binding of the W4A16 GEMM library (libw4a16.so, C ABI in include/w4a16.h;
+the kernel-forcing entry points used by tests and benchmarks are declared in
+csrc/w4a16_internal.h).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of the library. PyTorch provides device memory and the current
@@ -20,6 +22,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a16.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "w4a16.h")
+INTERNAL_HEADER = os.path.join(_HERE, "csrc", "w4a16_internal.h")
 
 GROUP_SIZE = 128
 PATH_AUTO, PATH_GEMV, PATH_SKINNY, PATH_TILE = 0, 1, 2, 3
@@ -54,21 +57,19 @@ def _lib():
     sig = {
         "w4a16_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "w4a16_pack_int4": (ctypes.c_int, [P, P, I64, I64, P]),
-        "w4a16_gemm_auto_split_k": (I32, [I64, I64, I64]),
+        "w4a16_gemm_auto_split_k": (I32, [I64, I64, I64, I32]),
         "w4a16_gemm_workspace_bytes": (SZ, [I64, I64, I64, I32]),
-        "w4a16_gemm_workspace_bytes_ex": (SZ, [I64, I64, I64, I32, P]),
+        "w4a16_gemm_workspace_bytes_gs": (SZ, [I64, I64, I64, I32, I32]),
         "w4a16_gemm": (ctypes.c_int, [P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P]),
-        "w4a16_gemm_ex": (ctypes.c_int, [P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P, P]),
-        "w4a16_gemm_grouped_workspace_bytes": (SZ, [I32, I64, I64, I64]),
-        "w4a16_gemm_grouped": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I64, I32, P, SZ, P]),
-        "w4a16_gemm_grouped_ex": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I64, I32, P, SZ, P, P]),
-        "w4a16_splitk_reduce": (ctypes.c_int, [P, P, I32, I64, I64, P]),
-        "w4a16_gemm_batched_workspace_bytes": (SZ, [I32, I64, I64, I64, I32]),
-        "w4a16_gemm_batched_workspace_bytes_ex": (SZ, [I32, I64, I64, I64, I32, P]),
-        "w4a16_gemm_workspace_bytes_gs": (SZ, [I64, I64, I64, I32, I32, P]),
-        "w4a16_gemm_grouped_workspace_bytes_gs": (SZ, [I32, I64, I64, I64, I32]),
-        "w4a16_gemm_batched_workspace_bytes_gs": (SZ, [I32, I64, I64, I64, I32, I32, P]),
+        "w4a16_gemm_grouped": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I64, I32, P]),
+        "w4a16_gemm_batched_workspace_bytes": (SZ, [I32, I64, I64, I64, I32, I32]),
         "w4a16_gemm_batched": (ctypes.c_int, [P, P, P, P, I32, I64, I64, I64, I32, I32, P, SZ, P]),
+        "w4a16_splitk_reduce": (ctypes.c_int, [P, P, I32, I64, I64, P]),
+        # internal entry points that force a kernel (tests, benchmarks)
+        "w4a16_gemm_workspace_bytes_ex": (SZ, [I64, I64, I64, I32, I32, P]),
+        "w4a16_gemm_ex": (ctypes.c_int, [P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P, P]),
+        "w4a16_gemm_grouped_ex": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I64, I32, P, P]),
+        "w4a16_gemm_batched_workspace_bytes_ex": (SZ, [I32, I64, I64, I64, I32, I32, P]),
         "w4a16_gemm_batched_ex": (ctypes.c_int, [P, P, P, P, I32, I64, I64, I64, I32, I32, P, SZ, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -79,9 +80,9 @@ def _lib():
     return L
 
 
-def header_functions() -> list:
-    """Names of the functions include/w4a16.h declares."""
-    with open(HEADER) as f:
+def header_functions(path: str = HEADER) -> list:
+    """Names of the functions a header (default include/w4a16.h) declares."""
+    with open(path) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
@@ -144,26 +145,36 @@ def w4a16_pack_int4(q: torch.Tensor, out: Optional[torch.Tensor] = None, stream=
     return out
 
 
-def w4a16_gemm_auto_split_k(M: int, N: int, K: int) -> int:
-    return int(_lib().w4a16_gemm_auto_split_k(M, N, K))
+def w4a16_gemm_auto_split_k(M: int, N: int, K: int, group_size: int = GROUP_SIZE) -> int:
+    return int(_lib().w4a16_gemm_auto_split_k(M, N, K, group_size))
 
 
 def w4a16_gemm_workspace_bytes(M: int, N: int, K: int, split_k: int = 0,
                                path: Optional[int] = None, variant: Optional[int] = None,
                                group_size: int = GROUP_SIZE) -> int:
+    """Workspace bytes of w4a16_gemm (0 when the effective split is 1)."""
     cfg = _cfg(path, variant)
+    if cfg is not None:
+        return int(_lib().w4a16_gemm_workspace_bytes_ex(M, N, K, group_size, split_k, cfg))
     if group_size != GROUP_SIZE:
-        return int(_lib().w4a16_gemm_workspace_bytes_gs(M, N, K, group_size, split_k, cfg))
-    if cfg is None:
-        return int(_lib().w4a16_gemm_workspace_bytes(M, N, K, split_k))
-    return int(_lib().w4a16_gemm_workspace_bytes_ex(M, N, K, split_k, cfg))
+        return int(_lib().w4a16_gemm_workspace_bytes_gs(M, N, K, group_size, split_k))
+    return int(_lib().w4a16_gemm_workspace_bytes(M, N, K, split_k))
+
+
+def _workspace(need: int, workspace: Optional[torch.Tensor], device) -> Optional[torch.Tensor]:
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4 + 1, dtype=torch.float32, device=device)
+    if workspace is not None:
+        _check(workspace, "workspace", torch.float32)
+    return workspace
 
 
 def w4a16_gemm(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
                y: Optional[torch.Tensor] = None, split_k: int = 0,
                workspace: Optional[torch.Tensor] = None, path: Optional[int] = None,
                variant: Optional[int] = None, stream=None, group_size: int = GROUP_SIZE) -> torch.Tensor:
-    """Y[M, N] = X[M, K] . dequant(W)[N, K]^T (bf16 out, fp32 accumulation)."""
+    """Y[M, N] = X[M, K] . dequant(W)[N, K]^T (bf16 out, fp32 accumulation).
+    `path` / `variant` force a kernel (internal entry point w4a16_gemm_ex)."""
     _check(x, "x", torch.bfloat16)
     M, K = x.shape
     N = w_packed.shape[0]
@@ -172,11 +183,8 @@ def w4a16_gemm(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _check(y, "y", torch.bfloat16, (M, N))
-    need = w4a16_gemm_workspace_bytes(M, N, K, split_k, path, variant, group_size)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need // 4 + 1, dtype=torch.float32, device=x.device)
-    if workspace is not None:
-        _check(workspace, "workspace", torch.float32)
+    workspace = _workspace(w4a16_gemm_workspace_bytes(M, N, K, split_k, path, variant, group_size), workspace,
+                           x.device)
     wbytes = 0 if workspace is None else workspace.numel() * 4
     cfg = _cfg(path, variant)
     L = _lib()
@@ -190,18 +198,11 @@ def w4a16_gemm(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
     return y
 
 
-def w4a16_gemm_grouped_workspace_bytes(G: int, M_total: int, N: int, K: int,
-                                       group_size: int = GROUP_SIZE) -> int:
-    if group_size != GROUP_SIZE:
-        return int(_lib().w4a16_gemm_grouped_workspace_bytes_gs(G, M_total, N, K, group_size))
-    return int(_lib().w4a16_gemm_grouped_workspace_bytes(G, M_total, N, K))
-
-
 def w4a16_gemm_grouped(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
                        m_sizes: torch.Tensor, y: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None, variant: Optional[int] = None,
-                       stream=None, group_size: int = GROUP_SIZE) -> torch.Tensor:
-    """Grouped GEMM in one launch; m_sizes stays on the device."""
+                       variant: Optional[int] = None, stream=None, group_size: int = GROUP_SIZE) -> torch.Tensor:
+    """Grouped GEMM in one launch; m_sizes stays on the device. `variant`
+    forces the tile height in rows (internal entry point)."""
     _check(x, "x", torch.bfloat16)
     M_total, K = x.shape
     G, N = w_packed.shape[0], w_packed.shape[1]
@@ -211,20 +212,13 @@ def w4a16_gemm_grouped(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Te
     if y is None:
         y = torch.empty((M_total, N), dtype=torch.bfloat16, device=x.device)
     _check(y, "y", torch.bfloat16, (M_total, N))
-    need = w4a16_gemm_grouped_workspace_bytes(G, M_total, N, K, group_size)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need // 4 + 1, dtype=torch.float32, device=x.device)
-    if workspace is not None:
-        _check(workspace, "workspace", torch.float32)
-    wbytes = 0 if workspace is None else workspace.numel() * 4
     L = _lib()
-    cfg = _cfg(PATH_TILE, variant) if variant is not None else None
-    if cfg is None:
+    if variant is None:
         st = L.w4a16_gemm_grouped(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(m_sizes), _ptr(y), G, M_total, N, K,
-                                  group_size, _ptr(workspace), wbytes, _stream(stream))
+                                  group_size, _stream(stream))
     else:
         st = L.w4a16_gemm_grouped_ex(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(m_sizes), _ptr(y), G, M_total, N,
-                                     K, group_size, _ptr(workspace), wbytes, _stream(stream), cfg)
+                                     K, group_size, _stream(stream), _cfg(PATH_TILE, variant))
     _raise(st, "w4a16_gemm_grouped")
     return y
 
@@ -232,12 +226,9 @@ def w4a16_gemm_grouped(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Te
 def w4a16_gemm_batched_workspace_bytes(B: int, M: int, N: int, K: int, split_k: int = 0,
                                        variant: Optional[int] = None, group_size: int = GROUP_SIZE) -> int:
     L = _lib()
-    if group_size != GROUP_SIZE:
-        cfg = None if variant is None else _cfg(PATH_TILE, variant)
-        return int(L.w4a16_gemm_batched_workspace_bytes_gs(B, M, N, K, group_size, split_k, cfg))
     if variant is None:
-        return int(L.w4a16_gemm_batched_workspace_bytes(B, M, N, K, split_k))
-    return int(L.w4a16_gemm_batched_workspace_bytes_ex(B, M, N, K, split_k, _cfg(PATH_TILE, variant)))
+        return int(L.w4a16_gemm_batched_workspace_bytes(B, M, N, K, group_size, split_k))
+    return int(L.w4a16_gemm_batched_workspace_bytes_ex(B, M, N, K, group_size, split_k, _cfg(PATH_TILE, variant)))
 
 
 def w4a16_gemm_batched(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
@@ -253,11 +244,8 @@ def w4a16_gemm_batched(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Te
     if y is None:
         y = torch.empty((B, M, N), dtype=torch.bfloat16, device=x.device)
     _check(y, "y", torch.bfloat16, (B, M, N))
-    need = w4a16_gemm_batched_workspace_bytes(B, M, N, K, split_k, variant, group_size)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need // 4 + 1, dtype=torch.float32, device=x.device)
-    if workspace is not None:
-        _check(workspace, "workspace", torch.float32)
+    workspace = _workspace(w4a16_gemm_batched_workspace_bytes(B, M, N, K, split_k, variant, group_size), workspace,
+                           x.device)
     wbytes = 0 if workspace is None else workspace.numel() * 4
     L = _lib()
     if variant is None:

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
 
-SOURCES = ["api.cpp", "pack_reduce.hip", "gemv.hip", "skinny.hip", "tile.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "pack_reduce.hip", "gemv.hip", "skinny.hip", "prefill.hip"]
 # MFMA accumulators that the VALU reads (diagonal extraction, per-group
 # rescale) stay in VGPRs (the default heuristic moved them through AGPRs with
 # extra copies)

@@ -10,10 +10,11 @@
 
 #include "../../include/w4a16.h"
 #include "launch.hpp"
+#include "w4a16_internal.h"
 
 namespace {
 
-constexpr int64_t kGroup = 128;   // k per pipeline stage (and the default scale group)
+constexpr int64_t kGroup = 128;       // k per pipeline stage (and the default scale group)
 constexpr int32_t kGroupSmall = 32;   // the other scale group size (tile path only)
 constexpr int64_t kMaxDim = 0x7FFFFFFFLL;
 constexpr uint64_t kMaxBytes = 0xFFFFFFFFULL;   // one buffer resource extent
@@ -34,25 +35,26 @@ int32_t pow2_at_least(int64_t v) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// GEMV default variant: layout 2 (MFMA diagonal contraction), one 8-wave
-// workgroup per compute unit, x held in registers, one weight block in
-// flight per wave (encoding in the dispatcher of gemv.hip).
-constexpr int kGemvDefaultVariant = 2110;
-// Small batch (M <= 32, two row tiles of 16 past 16 rows): variants below
-// 1000 are the group-striped layout
-// (10 * waves + column tiles per wave); 1000 * u + 100 * row tiles + 10 *
-// units in flight + waves / 4 is the streaming layout with units of 4 << (u - 1)
-// groups (one workgroup per compute unit, X of the slice in LDS, at most
-// kSkinnyStreamMaxGroups groups per slice). The default is the group-striped
-// layout with 8 waves (at the small-batch decode workload the streaming one
-// runs at the same rate): one column tile per wave up to 8 rows, two above
-// (at 17408 x 5120 and 8192 x 8192, rotated weights: M = 2-4 7-10 % faster
-// with one tile, M >= 9 4-12 % faster with two).
-int skinny_default_variant(int64_t M) { return M <= 8 || M > 32 ? 81 : 82; }
+// Compute units of the current device (cached per device; safe to call from
+// several host threads).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 
-bool skinny_streaming(int variant) { return variant >= 1000; }
-
-int device_cus();
+// Small batch: one column tile of 16 per wave up to 8 rows and past 32, two
+// between (8 waves per workgroup; at 17408 x 5120 and 8192 x 8192, rotated
+// weights: M = 2-4 7-10 % faster with one tile, M >= 9 4-12 % faster with
+// two; past 32 rows the three row tiles leave registers for one only).
+int skinny_default_tiles(int64_t M) { return M <= 8 || M > 32 ? 1 : 2; }
+constexpr int kSkinnyWaves = 8;
 
 Path auto_path(int64_t M, int64_t N, int64_t K, int32_t sk) {
   const int64_t Gk = K / kGroup;
@@ -72,20 +74,6 @@ Path auto_path(int64_t M, int64_t N, int64_t K, int32_t sk) {
   // faster than the tile kernel; 8192 x 8192, two rounds: 15-30 % slower)
   if (M <= w4a16::kSkinnyMaxRows && ceil_div(N, 16) <= (int64_t)device_cus()) return kPathSkinny;
   return kPathTile;
-}
-
-// Compute units of the current device (cached per device; safe to call from
-// several host threads).
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cache[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
 }
 
 // Cost model of the tile path, in units of one row x one 128-group of work on
@@ -122,109 +110,53 @@ int32_t tile_split_rate(int64_t M, int64_t N, int64_t Gk, int64_t tiles, int bm,
   return best;
 }
 
-// per-row rates of the tile heights, relative to the 128-row tile (shorter
+// Per-row rates of the tile heights, relative to the 128-row tile (shorter
 // tiles amortise the per-group dequantisation and barrier over fewer rows;
 // at 1322 x 19456 x 2560 on one box: 4 rounds of 128 rows 166 us, 4 of 112
-// rows 161 us, 3 of 144 rows 146 us, 5 of 96 rows 176 us)
-struct TileCand { int cfg, bm; double rate; };
-// (64 and 48 rows, measured at 40-64 rows of 17408 x 5120 and 8192 x 8192
-// against 80: 0.70 and 0.55)
-constexpr TileCand kTileCands[] = {{2, 128, 1.0},  {6, 144, 0.96}, {4, 112, 0.91}, {3, 96, 0.907},
-                                   {5, 80, 0.85},  {7, 64, 0.70},  {8, 48, 0.55}};
+// rows 161 us, 3 of 144 rows 146 us, 5 of 96 rows 176 us; 64 and 48 rows
+// measured at 40-64 rows of 17408 x 5120 and 8192 x 8192 against 80).
+struct TileCand { int bm; double rate; };
+constexpr TileCand kTileCands[] = {{128, 1.0}, {144, 0.96}, {112, 0.91}, {96, 0.907},
+                                   {80, 0.85}, {64, 0.70},  {48, 0.55}};
 
-double tile_rate(int cfg) {
+double tile_rate(int bm) {
   for (const TileCand& c : kTileCands)
-    if (c.cfg == cfg) return c.rate;
-  return 0.9;   // tile configurations 0 and 1
+    if (c.bm == bm) return c.rate;
+  return 0.9;
 }
 
-int32_t tile_split(int64_t M, int64_t N, int64_t Gk, int64_t tiles, int cfg) {
-  return tile_split_rate(M, N, Gk, tiles, w4a16::tile_bm(cfg), tile_rate(cfg));
+int32_t tile_split(int64_t M, int64_t N, int64_t Gk, int64_t tiles, int bm) {
+  return tile_split_rate(M, N, Gk, tiles, bm, tile_rate(bm));
 }
 
-int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int tile_cfg, int variant) {
-  const int64_t Gk = K / kGroup;
-  int32_t sk = 1;
-  switch (path) {
-    case kPathGemv: {
-      // only what the register budget for x needs (at most 64 groups per
-      // slice): a split adds the reduce kernel, and over N x K from 1024 x
-      // 8192 to 28672 x 8192 one slice was fastest wherever it fits
-      sk = pow2_at_least(ceil_div(Gk, 64));
-      break;
-    }
-    case kPathSkinny: {
-      if (skinny_streaming(variant)) {
-        // a slice's X must fit LDS; then enough row blocks x slices for the GPU
-        sk = pow2_at_least(ceil_div(Gk, w4a16::kSkinnyStreamMaxGroups));
-        const int64_t blocks = ceil_div(N, 16);
-        while (sk < 16 && blocks * sk < 1024 && sk * 2 <= Gk) sk <<= 1;
-        break;
-      }
-      // split only while fewer than half of the compute units have a
-      // workgroup: the reduce kernel and the partials cost more than the
-      // shorter slices save once the grid is half full (4096 x 4096, 128
-      // workgroups: SK 1 8-16 % faster than 2; 2560 x 9728, 80 workgroups:
-      // SK 2 20 % faster than 4), every wave keeping at least one group
-      const int v = variant > 0 ? variant : skinny_default_variant(M);
-      const int nt = v % 10, waves = v / 10;
-      const int64_t wgs = ceil_div(N, 16 * (int64_t)std::max(nt, 1));
-      while (sk < 16 && wgs * sk < device_cus() / 2 && ceil_div(Gk, (int64_t)sk * 2) >= waves) sk <<= 1;
-      break;
-    }
-    case kPathTile: {
-      const int64_t tiles = ceil_div(M, w4a16::tile_bm(tile_cfg)) * ceil_div(N, w4a16::tile_bn(tile_cfg));
-      sk = tile_split(M, N, Gk, tiles, tile_cfg);
-      break;
-    }
-    default:
-      break;
-  }
-  return sk;
-}
-
-struct Plan {
-  Path path;
-  int32_t sk;        // effective split-K
-  int32_t gps;       // groups per slice
-  int variant;       // kernel variant of the path
-  uint64_t ws_split; // bytes of the [SK, M, N] fp32 partials
-  uint64_t ws_sx;    // bytes of the [K/128, ld] fp32 row sums (tile path)
-  int64_t ld;        // row stride of the row sums
-};
-
-// Tile configuration 2 (LDS-DMA staging, 8 waves of 128 x 32, tile.hip).
-
-// Grouped launches: the grid holds ceil(M_total / BM) + G row tiles per column
-// tile (group boundaries split tiles). Shorter tiles (96 rows, configuration
-// 3) when that whole grid still fits one wave of workgroups over the compute
-// units: each tile then finishes sooner and no tile waits for a second round.
-// Tile height of the LDS-DMA kernel: the candidate of least cost (above),
-// with its own best split when split_k is automatic (`split` < 0) or the
-// given one. `tiles(bm)` counts the output tiles of a height.
-// Only heights that run the scale group size gs are candidates.
+// Tile height of the least estimated cost, with its own best split when
+// split_k is automatic (`split` < 0) or the given one. `tiles(bm)` counts the
+// output tiles of a height. Only heights built for the scale group size gs
+// are candidates.
 template <class T>
-int pick_tile_cfg(int64_t M, int64_t N, int64_t Gk, T tiles, int64_t split, int32_t gs) {
+int pick_tile_rows(int64_t M, int64_t N, int64_t Gk, T tiles, int64_t split, int32_t gs) {
   const int64_t cus = device_cus();
-  int best = 2;
+  int best = 128;
   double best_cost = 0.0;
   for (const TileCand& c : kTileCands) {
-    if (!w4a16::tile_group_ok(c.cfg, gs)) continue;
+    if (!w4a16::tile_rows_ok(c.bm, gs)) continue;
     const int64_t t = tiles(c.bm);
     const int64_t sk = split > 0 ? split : tile_split_rate(M, N, Gk, t, c.bm, c.rate);
     const double cost = tile_cost(M, N, Gk, t, c.bm, c.rate, sk, cus);
     if (best_cost == 0.0 || cost < best_cost * (1.0 - 1e-9)) {
-      best = c.cfg;
+      best = c.bm;
       best_cost = cost;
     }
   }
   return best;
 }
 
+int64_t tile_cols(int64_t N) { return ceil_div(N, w4a16::kTileCols); }
+
 // split_k = 0: automatic, chosen with the height; otherwise fixed
-int default_tile_cfg(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t gs) {
-  const int64_t nt = ceil_div(N, 256), Gk = K / kGroup;
-  return pick_tile_cfg(
+int default_tile_rows(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t gs) {
+  const int64_t nt = tile_cols(N), Gk = K / kGroup;
+  return pick_tile_rows(
       M, N, Gk, [&](int bm) { return ceil_div(std::max<int64_t>(M, 1), bm) * nt; }, split_k > 0 ? split_k : -1,
       gs);
 }
@@ -232,57 +164,69 @@ int default_tile_cfg(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t g
 // grouped (no split-K): M_sizes stays on the device, so the tile count is
 // estimated as ceil(M_total / bm) + G / 2 per column (each group's partial
 // last tile adds half a tile on average; the kernel maps only the real tiles)
-int default_grouped_tile_cfg(int64_t G, int64_t M_total, int64_t N, int64_t K, int32_t gs) {
-  const int64_t nt = ceil_div(N, 256);
-  return pick_tile_cfg(
-      M_total, N, K / kGroup, [&](int bm) { return (ceil_div(std::max<int64_t>(M_total, 1), bm) + G / 2) * nt; }, 1,
-      gs);
+int default_grouped_tile_rows(int64_t G, int64_t M_total, int64_t N, int64_t K, int32_t gs) {
+  const int64_t nt = tile_cols(N);
+  return pick_tile_rows(
+      M_total, N, K / kGroup,
+      [&](int bm) { return (ceil_div(std::max<int64_t>(M_total, 1), bm) + G / 2) * nt; }, 1, gs);
 }
 
-// bytes of the [K / gs, ld] fp32 row sums of the tile path
+int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int bm, int nt) {
+  const int64_t Gk = K / kGroup;
+  int32_t sk = 1;
+  switch (path) {
+    case kPathGemv:
+      // only what the register budget for x needs (at most 64 groups per
+      // slice): a split adds the reduce kernel, and over N x K from 1024 x
+      // 8192 to 28672 x 8192 one slice was fastest wherever it fits
+      sk = pow2_at_least(ceil_div(Gk, 64));
+      break;
+    case kPathSkinny: {
+      // split only while fewer than half of the compute units have a
+      // workgroup: the reduce kernel and the partials cost more than the
+      // shorter slices save once the grid is half full (4096 x 4096, 128
+      // workgroups: SK 1 8-16 % faster than 2; 2560 x 9728, 80 workgroups:
+      // SK 2 20 % faster than 4), every wave keeping at least one group
+      const int64_t wgs = ceil_div(N, 16 * (int64_t)nt);
+      while (sk < 16 && wgs * sk < device_cus() / 2 && ceil_div(Gk, (int64_t)sk * 2) >= kSkinnyWaves) sk <<= 1;
+      break;
+    }
+    case kPathTile:
+      sk = tile_split(M, N, Gk, ceil_div(M, bm) * tile_cols(N), bm);
+      break;
+    default:
+      break;
+  }
+  return sk;
+}
+
+// Row sums of X on the tile path: the tile kernel forms -136 * sum_k x per
+// (row, scale group) itself, on the matrix core, in every column tile; a
+// separate pre-pass forms them once, into the workspace. The kernel's own
+// sums cost more once many column tiles repeat them (1322 x 19456 x 2560,
+// 76 column tiles: 157 against 150.5 us with the pre-pass; N = 2048 and
+// 4096 at 1322 rows, 8 and 16 tiles: 1-3 us faster than the pre-pass; at
+// group 32 the in-kernel sums take four MFMAs per stage instead of one chain
+// and the crossover is lower), so the pre-pass is used from 32 column tiles
+// at group 128 and 8 at group 32, when the caller gives the workspace room.
+bool tile_prepass(int64_t N, int32_t gs) { return tile_cols(N) * (kGroup / gs) >= 32; }
+
+// bytes of the [K / gs, ld] fp32 row sums of the pre-pass
 uint64_t rowsum_bytes(int64_t M, int64_t K, int32_t gs) {
   return (uint64_t)(K / gs) * round_up((uint64_t)M, 4) * 4u;
 }
 
-// Batched: B problems of M rows on the tile kernel (weight group b = problem
-// b, its M rows at b * M), tile height and split-K as for one problem of B x
-// ceil(M / h) row tiles per column.
-struct BatchedPlan {
-  int cfg;
-  int32_t sk, gps;
-  uint64_t ws_split, ws_sx;
-  int64_t ld;
+struct Plan {
+  Path path;
+  int32_t sk;         // effective split-K
+  int32_t gps;        // 128-groups per slice
+  int variant;        // GEMV: 1 = half-wave layout; small batch: column tiles per wave; tile: rows per tile
+  uint64_t ws_split;  // bytes of the [SK, M, N] fp32 partials
+  uint64_t ws_sx;     // bytes of the pre-pass row sums (tile path with a wide N), else 0
 };
 
-w4a16_status make_batched_plan(int32_t B, int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg,
-                               int32_t gs, BatchedPlan* p) {
-  const int64_t Gk = K / kGroup, nt = ceil_div(N, 256), Mt = (int64_t)B * M;
-  int tile_cfg = -1;
-  if (cfg != nullptr) {
-    if (cfg->path != 0 && cfg->path != kPathTile) return W4A16_ERR_SHAPE;
-    tile_cfg = cfg->variant;
-  }
-  if (tile_cfg < 0)
-    tile_cfg = pick_tile_cfg(
-        Mt, N, Gk, [&](int bm) { return (int64_t)B * ceil_div(M, bm) * nt; }, split_k > 0 ? split_k : -1, gs);
-  if (tile_cfg >= w4a16::tile_num_cfgs()) return W4A16_ERR_SHAPE;
-  if (!w4a16::tile_group_ok(tile_cfg, gs)) return W4A16_ERR_GROUP_SIZE;
-  const int64_t tiles =
-      (int64_t)B * ceil_div(M, w4a16::tile_bm(tile_cfg)) * ceil_div(N, w4a16::tile_bn(tile_cfg));
-  int32_t sk = split_k > 0 ? split_k : tile_split(Mt, N, Gk, tiles, tile_cfg);
-  if (sk > Gk && split_k == 0) sk = 1;
-  p->cfg = tile_cfg;
-  p->sk = sk;
-  p->gps = (int32_t)ceil_div(Gk, sk);
-  p->ws_split = sk > 1 ? (uint64_t)sk * (uint64_t)Mt * (uint64_t)N * 4u : 0u;
-  p->ld = (int64_t)round_up((uint64_t)Mt, 4);
-  p->ws_sx = rowsum_bytes(Mt, K, gs);
-  return W4A16_OK;
-}
-
-
-// Group size 32 runs on the tile path only (the GEMV and skinny kernels take
-// one scale per 128 k), whatever M is.
+// Group size 32 runs on the tile path only (the GEMV and small-batch kernels
+// take one scale per 128 k), whatever M is.
 w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg, int32_t gs,
                        Plan* p) {
   const int64_t Gk = K / kGroup;
@@ -296,17 +240,25 @@ w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w
   if (path == kPathGemv && M != 1) return W4A16_ERR_SHAPE;
   if (path == kPathSkinny && M > w4a16::kSkinnyMaxRows) return W4A16_ERR_SHAPE;
   if (path != kPathTile && gs != kGroup) return W4A16_ERR_GROUP_SIZE;
-  if (path == kPathSkinny && variant <= 0) variant = skinny_default_variant(M);
-  // past 16 rows (two row tiles): the group-striped layout with 8 waves of
-  // 1 or 2 column tiles only; past 32 rows (three row tiles) of 1
-  if (path == kPathSkinny && M > 16 && !(variant == 81 || (variant == 82 && M <= 32))) return W4A16_ERR_SHAPE;
-  int tile_cfg = 0;
-  if (path == kPathTile) {
-    tile_cfg = variant >= 0 ? variant : default_tile_cfg(M, N, K, split_k, gs);
-    if (tile_cfg >= w4a16::tile_num_cfgs()) return W4A16_ERR_SHAPE;
-    if (!w4a16::tile_group_ok(tile_cfg, gs)) return W4A16_ERR_GROUP_SIZE;
+  switch (path) {
+    case kPathGemv:
+      if (variant > 1) return W4A16_ERR_SHAPE;
+      break;
+    case kPathSkinny:
+      if (variant <= 0) variant = skinny_default_tiles(M);
+      // past 32 rows (three row tiles) one column tile per wave only
+      if (variant > 2 || (M > 32 && variant != 1)) return W4A16_ERR_SHAPE;
+      break;
+    case kPathTile:
+      if (variant <= 0) variant = default_tile_rows(M, N, K, split_k, gs);
+      if (!w4a16::tile_rows_ok(variant, kGroup) && !w4a16::tile_rows_ok(variant, kGroupSmall))
+        return W4A16_ERR_SHAPE;
+      if (!w4a16::tile_rows_ok(variant, gs)) return W4A16_ERR_GROUP_SIZE;
+      break;
+    default:
+      return W4A16_ERR_SHAPE;
   }
-  int32_t sk = split_k > 0 ? split_k : auto_split(path, M, N, K, tile_cfg, variant);
+  int32_t sk = split_k > 0 ? split_k : auto_split(path, M, N, K, variant, variant);
   if (sk > Gk && split_k == 0) sk = 1;
   if (path == kPathGemv && ceil_div(Gk, sk) > 64) {
     if (split_k != 0) return W4A16_ERR_SPLIT_K;   // explicit split too small for the GEMV path
@@ -315,10 +267,9 @@ w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w
   p->path = path;
   p->sk = sk;
   p->gps = (int32_t)ceil_div(Gk, sk);
-  p->variant = path == kPathTile ? tile_cfg : variant;
+  p->variant = variant;
   p->ws_split = sk > 1 ? (uint64_t)sk * (uint64_t)M * (uint64_t)N * 4u : 0u;
-  p->ld = (int64_t)round_up((uint64_t)M, 4);
-  p->ws_sx = path == kPathTile ? rowsum_bytes(M, K, gs) : 0u;
+  p->ws_sx = path == kPathTile && tile_prepass(N, gs) ? rowsum_bytes(M, K, gs) : 0u;
   return W4A16_OK;
 }
 
@@ -346,55 +297,49 @@ w4a16_status check_batched(int32_t B, int64_t M, int64_t N, int64_t K, int32_t g
 
 w4a16_status launched(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
 
-w4a16_status run_gemm(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, int64_t M, int64_t N,
-                      int64_t K, int32_t group_size, int32_t split_k, float* workspace, size_t workspace_bytes,
-                      void* stream, const w4a16_config* cfg) {
+// Validated plan of a plain GEMM: status, or W4A16_OK with *p filled and
+// *empty set when M == 0 (nothing to enqueue).
+w4a16_status plan_gemm(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, int64_t M, int64_t N,
+                       int64_t K, int32_t group_size, int32_t split_k, const w4a16_config* cfg, Plan* p,
+                       bool* empty) {
+  *empty = false;
   if (!valid_split(split_k)) return W4A16_ERR_SPLIT_K;
   w4a16_status st = check_dims(M, N, K, group_size);
   if (st != W4A16_OK) return st;
-  if (M == 0) return W4A16_OK;   // empty problem: nothing to read or write
+  if (M == 0) {   // empty problem: nothing to read or write
+    *empty = true;
+    return W4A16_OK;
+  }
   if (x == nullptr || w == nullptr || s == nullptr || y == nullptr) return W4A16_ERR_NULL;
   if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(y)) return W4A16_ERR_ALIGN;
-  Plan p;
-  st = make_plan(M, N, K, split_k, cfg, group_size, &p);
+  st = make_plan(M, N, K, split_k, cfg, group_size, p);
   if (st != W4A16_OK) return st;
-  if (p.ws_split > kMaxBytes) return W4A16_ERR_SHAPE;
-  const uint64_t need = plan_bytes(p);
-  if (need > 0) {
-    if (workspace == nullptr) return W4A16_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
-    if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
-  }
-  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  float* ws_split = p.sk > 1 ? workspace : nullptr;
-  float* ws_sx = p.ws_sx ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + round_up(p.ws_split, 256))
-                         : nullptr;
+  if (p->ws_split > kMaxBytes) return W4A16_ERR_SHAPE;
+  return W4A16_OK;
+}
+
+// Enqueues a planned GEMM; `partials` holds the [SK, M, N] fp32 slices when
+// p.sk > 1 (unused otherwise); `rowsums` (tile path, may be nullptr) the
+// pre-pass row sums.
+w4a16_status launch_plan(const Plan& p, const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y,
+                         int64_t M, int64_t N, int64_t K, int32_t group_size, float* partials, float* rowsums,
+                         hipStream_t strm) {
+  float* ws_split = p.sk > 1 ? partials : nullptr;
   const int iM = (int)M, iN = (int)N, iK = (int)K;
   hipError_t e = hipSuccess;
   switch (p.path) {
-    case kPathGemv: {
-      const int v = p.variant > 0 ? p.variant : kGemvDefaultVariant;
-      e = w4a16::launch_gemv_m1(x, w, s, y, ws_split, iN, iK, p.gps, p.sk, v, strm);
+    case kPathGemv:
+      e = w4a16::launch_gemv_m1(x, w, s, y, ws_split, iN, iK, p.gps, p.sk, p.variant == 1, strm);
       break;
-    }
-    case kPathSkinny: {
-      const int v = p.variant > 0 ? p.variant : skinny_default_variant(M);
-      if (v >= 1000 && p.gps <= w4a16::kSkinnyStreamMaxGroups) {
-        e = w4a16::launch_skinny_stream(x, w, s, y, ws_split, iM, iN, iK, p.gps, p.sk, (v / 100) % 10,
-                                        (v / 10) % 10, 4 * (v % 10), 4 << ((v / 1000) - 1), strm);
-        break;
-      }
-      // group-striped layout (also for slices too long for the streaming one)
-      const int vs = v < 1000 ? v : skinny_default_variant(M);
-      const int nt = vs % 10, waves = vs / 10;
-      e = w4a16::launch_skinny(x, w, s, y, ws_split, iM, iN, iK, p.gps, p.sk, nt, waves, strm);
+    case kPathSkinny:
+      e = w4a16::launch_skinny(x, w, s, y, ws_split, iM, iN, iK, p.gps, p.sk, p.variant, kSkinnyWaves, strm);
       break;
-    }
     case kPathTile: {
-      e = w4a16::launch_rowsum_neg136(x, ws_sx, iM, iK, (int)p.ld, group_size, strm);
+      const int ld = (int)round_up((uint64_t)M, 4);
+      if (rowsums != nullptr) e = w4a16::launch_rowsum_neg136(x, rowsums, iM, iK, ld, group_size, strm);
       if (e == hipSuccess)
-        e = w4a16::launch_tile(x, w, s, ws_sx, y, ws_split, nullptr, 0, iM, iN, iK, 1, (int)p.ld, p.gps, p.sk,
-                               p.variant, group_size, strm);
+        e = w4a16::launch_tile(x, w, s, rowsums, ld, y, ws_split, nullptr, 0, iM, iN, iK, 1, p.gps, p.sk, p.variant,
+                               group_size, strm);
       break;
     }
     default:
@@ -403,6 +348,76 @@ w4a16_status run_gemm(const uint16_t* x, const uint8_t* w, const uint16_t* s, ui
   if (e != hipSuccess) return W4A16_ERR_LAUNCH;
   if (p.sk > 1) return launched(w4a16::launch_splitk_reduce(ws_split, y, (uint64_t)M * (uint64_t)N, p.sk, strm));
   return W4A16_OK;
+}
+
+w4a16_status run_gemm(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, int64_t M, int64_t N,
+                      int64_t K, int32_t group_size, int32_t split_k, float* workspace, size_t workspace_bytes,
+                      void* stream, const w4a16_config* cfg) {
+  Plan p;
+  bool empty = false;
+  w4a16_status st = plan_gemm(x, w, s, y, M, N, K, group_size, split_k, cfg, &p, &empty);
+  if (st != W4A16_OK || empty) return st;
+  if (p.ws_split > 0) {
+    if (workspace == nullptr) return W4A16_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
+    if (workspace_bytes < round_up(p.ws_split, 256)) return W4A16_ERR_WORKSPACE;
+  }
+  // the pre-pass row sums only where the workspace has room for them too
+  float* rowsums = nullptr;
+  if (p.ws_sx > 0 && workspace != nullptr && aligned16(workspace) && workspace_bytes >= plan_bytes(p))
+    rowsums = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + round_up(p.ws_split, 256));
+  return launch_plan(p, x, w, s, y, M, N, K, group_size, workspace, rowsums, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t split_k,
+                            const w4a16_config* cfg) {
+  if (!valid_split(split_k) || check_dims(M, N, K, group_size) != W4A16_OK || M == 0) return 0;
+  Plan p;
+  if (make_plan(M, N, K, split_k, cfg, group_size, &p) != W4A16_OK) return 0;
+  return (size_t)plan_bytes(p);
+}
+
+// Batched: B problems of M rows on the tile kernel (weight group b = problem
+// b, its M rows at b * M), tile height and split-K as for one problem of B x
+// ceil(M / h) row tiles per column. (M <= 16 problems run the tile kernel too:
+// the per-problem scale tensors are not 16-byte aligned in general, which the
+// decode kernels require.)
+struct BatchedPlan {
+  int bm;
+  int32_t sk, gps;
+  uint64_t ws_split, ws_sx;
+};
+
+w4a16_status make_batched_plan(int32_t B, int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg,
+                               int32_t gs, BatchedPlan* p) {
+  const int64_t Gk = K / kGroup, nt = tile_cols(N), Mt = (int64_t)B * M;
+  int bm = -1;
+  if (cfg != nullptr) {
+    if (cfg->path != 0 && cfg->path != kPathTile) return W4A16_ERR_SHAPE;
+    bm = cfg->variant;
+  }
+  if (bm <= 0)
+    bm = pick_tile_rows(
+        Mt, N, Gk, [&](int h) { return (int64_t)B * ceil_div(M, h) * nt; }, split_k > 0 ? split_k : -1, gs);
+  if (!w4a16::tile_rows_ok(bm, kGroup) && !w4a16::tile_rows_ok(bm, kGroupSmall)) return W4A16_ERR_SHAPE;
+  if (!w4a16::tile_rows_ok(bm, gs)) return W4A16_ERR_GROUP_SIZE;
+  const int64_t tiles = (int64_t)B * ceil_div(M, bm) * nt;
+  int32_t sk = split_k > 0 ? split_k : tile_split(Mt, N, Gk, tiles, bm);
+  if (sk > Gk && split_k == 0) sk = 1;
+  p->bm = bm;
+  p->sk = sk;
+  p->gps = (int32_t)ceil_div(Gk, sk);
+  p->ws_split = sk > 1 ? (uint64_t)sk * (uint64_t)Mt * (uint64_t)N * 4u : 0u;
+  p->ws_sx = tile_prepass(N, gs) ? rowsum_bytes(Mt, K, gs) : 0u;
+  return W4A16_OK;
+}
+
+size_t batched_workspace_bytes(int32_t B, int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t split_k,
+                               const w4a16_config* cfg) {
+  if (!valid_split(split_k) || check_batched(B, M, N, K, group_size) != W4A16_OK || M == 0) return 0;
+  BatchedPlan p;
+  if (make_batched_plan(B, M, N, K, split_k, cfg, group_size, &p) != W4A16_OK) return 0;
+  return (size_t)(round_up(p.ws_split, 256) + p.ws_sx);
 }
 
 }  // namespace
@@ -430,30 +445,28 @@ w4a16_status w4a16_pack_int4(const uint8_t* q, uint8_t* w_packed, int64_t rows, 
   if (!aligned16(q) || !aligned16(w_packed)) return W4A16_ERR_ALIGN;
   if (rows == 0) return W4A16_OK;
   if ((uint64_t)rows > (uint64_t)INT64_MAX / (uint64_t)K) return W4A16_ERR_SHAPE;
-  return launched(w4a16::launch_pack_int4(q, w_packed, (uint64_t)rows * (uint64_t)K, reinterpret_cast<hipStream_t>(stream)));
+  return launched(
+      w4a16::launch_pack_int4(q, w_packed, (uint64_t)rows * (uint64_t)K, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int32_t w4a16_gemm_auto_split_k(int64_t M, int64_t N, int64_t K) {
-  if (check_dims(M, N, K, 128) != W4A16_OK || M == 0) return 0;
+int32_t w4a16_gemm_auto_split_k(int64_t M, int64_t N, int64_t K, int32_t group_size) {
+  if (check_dims(M, N, K, group_size) != W4A16_OK || M == 0) return 0;
   Plan p;
-  if (make_plan(M, N, K, 0, nullptr, kGroup, &p) != W4A16_OK) return 0;
+  if (make_plan(M, N, K, 0, nullptr, group_size, &p) != W4A16_OK) return 0;
   return p.sk;
 }
 
 size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t split_k) {
-  return w4a16_gemm_workspace_bytes_gs(M, N, K, kGroup, split_k, nullptr);
+  return gemm_workspace_bytes(M, N, K, kGroup, split_k, nullptr);
 }
 
-size_t w4a16_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int32_t split_k, const w4a16_config* cfg) {
-  return w4a16_gemm_workspace_bytes_gs(M, N, K, kGroup, split_k, cfg);
+size_t w4a16_gemm_workspace_bytes_gs(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t split_k) {
+  return gemm_workspace_bytes(M, N, K, group_size, split_k, nullptr);
 }
 
-size_t w4a16_gemm_workspace_bytes_gs(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t split_k,
+size_t w4a16_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t split_k,
                                      const w4a16_config* cfg) {
-  if (!valid_split(split_k) || check_dims(M, N, K, group_size) != W4A16_OK || M == 0) return 0;
-  Plan p;
-  if (make_plan(M, N, K, split_k, cfg, group_size, &p) != W4A16_OK) return 0;
-  return (size_t)plan_bytes(p);
+  return gemm_workspace_bytes(M, N, K, group_size, split_k, cfg);
 }
 
 w4a16_status w4a16_gemm(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales, uint16_t* y, int64_t M,
@@ -468,26 +481,15 @@ w4a16_status w4a16_gemm_ex(const uint16_t* x, const uint8_t* w_packed, const uin
   return run_gemm(x, w_packed, scales, y, M, N, K, group_size, split_k, workspace, workspace_bytes, stream, cfg);
 }
 
-size_t w4a16_gemm_grouped_workspace_bytes(int32_t G, int64_t M_total, int64_t N, int64_t K) {
-  return w4a16_gemm_grouped_workspace_bytes_gs(G, M_total, N, K, kGroup);
-}
-
-size_t w4a16_gemm_grouped_workspace_bytes_gs(int32_t G, int64_t M_total, int64_t N, int64_t K, int32_t group_size) {
-  if (G < 1 || M_total <= 0 || check_dims(M_total, N, K, group_size) != W4A16_OK) return 0;
-  return (size_t)rowsum_bytes(M_total, K, group_size);
-}
-
 w4a16_status w4a16_gemm_grouped(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales,
                                 const int32_t* m_sizes, uint16_t* y, int32_t G, int64_t M_total, int64_t N, int64_t K,
-                                int32_t group_size, float* workspace, size_t workspace_bytes, void* stream) {
-  return w4a16_gemm_grouped_ex(x, w_packed, scales, m_sizes, y, G, M_total, N, K, group_size, workspace,
-                               workspace_bytes, stream, nullptr);
+                                int32_t group_size, void* stream) {
+  return w4a16_gemm_grouped_ex(x, w_packed, scales, m_sizes, y, G, M_total, N, K, group_size, stream, nullptr);
 }
 
 w4a16_status w4a16_gemm_grouped_ex(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales,
                                    const int32_t* m_sizes, uint16_t* y, int32_t G, int64_t M_total, int64_t N,
-                                   int64_t K, int32_t group_size, float* workspace, size_t workspace_bytes,
-                                   void* stream, const w4a16_config* cfg) {
+                                   int64_t K, int32_t group_size, void* stream, const w4a16_config* cfg) {
   if (G < 1 || M_total < 0) return W4A16_ERR_SHAPE;
   w4a16_status st = check_dims(M_total, N, K, group_size);
   if (st != W4A16_OK) return st;
@@ -499,41 +501,28 @@ w4a16_status w4a16_gemm_grouped_ex(const uint16_t* x, const uint8_t* w_packed, c
     return W4A16_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_packed) || !aligned16(scales) || !aligned16(y)) return W4A16_ERR_ALIGN;
   if (((uintptr_t)m_sizes & 3u) != 0) return W4A16_ERR_ALIGN;
-  int tile_cfg = default_grouped_tile_cfg(G, M_total, N, K, group_size);
+  int bm = -1;
   if (cfg != nullptr) {
     if (cfg->path != 0 && cfg->path != kPathTile) return W4A16_ERR_SHAPE;
-    if (cfg->variant >= 0) tile_cfg = cfg->variant;
-    if (tile_cfg >= w4a16::tile_num_cfgs()) return W4A16_ERR_SHAPE;
+    bm = cfg->variant;
   }
-  if (!w4a16::tile_group_ok(tile_cfg, group_size)) return W4A16_ERR_GROUP_SIZE;
-  const uint64_t need = rowsum_bytes(M_total, K, group_size);
-  if (workspace == nullptr) return W4A16_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
-  if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
-  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  const int ld = (int)round_up((uint64_t)M_total, 4);
+  if (bm <= 0) bm = default_grouped_tile_rows(G, M_total, N, K, group_size);
+  if (!w4a16::tile_rows_ok(bm, kGroup) && !w4a16::tile_rows_ok(bm, kGroupSmall)) return W4A16_ERR_SHAPE;
+  if (!w4a16::tile_rows_ok(bm, group_size)) return W4A16_ERR_GROUP_SIZE;
   const int Gk = (int)(K / kGroup);
-  hipError_t e = w4a16::launch_rowsum_neg136(x, workspace, (int)M_total, (int)K, ld, group_size, strm);
-  if (e != hipSuccess) return W4A16_ERR_LAUNCH;
-  return launched(w4a16::launch_tile(x, w_packed, scales, workspace, y, nullptr, m_sizes, 0, (int)M_total, (int)N,
-                                     (int)K, G, ld, Gk, 1, tile_cfg, group_size, strm));
+  // row sums formed in the kernel: the call takes no workspace
+  return launched(w4a16::launch_tile(x, w_packed, scales, nullptr, 0, y, nullptr, m_sizes, 0, (int)M_total, (int)N,
+                                     (int)K, G, Gk, 1, bm, group_size, reinterpret_cast<hipStream_t>(stream)));
 }
 
-size_t w4a16_gemm_batched_workspace_bytes_gs(int32_t B, int64_t M, int64_t N, int64_t K, int32_t group_size,
+size_t w4a16_gemm_batched_workspace_bytes(int32_t B, int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                          int32_t split_k) {
+  return batched_workspace_bytes(B, M, N, K, group_size, split_k, nullptr);
+}
+
+size_t w4a16_gemm_batched_workspace_bytes_ex(int32_t B, int64_t M, int64_t N, int64_t K, int32_t group_size,
                                              int32_t split_k, const w4a16_config* cfg) {
-  if (!valid_split(split_k) || check_batched(B, M, N, K, group_size) != W4A16_OK || M == 0) return 0;
-  BatchedPlan p;
-  if (make_batched_plan(B, M, N, K, split_k, cfg, group_size, &p) != W4A16_OK) return 0;
-  return (size_t)(round_up(p.ws_split, 256) + p.ws_sx);
-}
-
-size_t w4a16_gemm_batched_workspace_bytes_ex(int32_t B, int64_t M, int64_t N, int64_t K, int32_t split_k,
-                                             const w4a16_config* cfg) {
-  return w4a16_gemm_batched_workspace_bytes_gs(B, M, N, K, kGroup, split_k, cfg);
-}
-
-size_t w4a16_gemm_batched_workspace_bytes(int32_t B, int64_t M, int64_t N, int64_t K, int32_t split_k) {
-  return w4a16_gemm_batched_workspace_bytes_ex(B, M, N, K, split_k, nullptr);
+  return batched_workspace_bytes(B, M, N, K, group_size, split_k, cfg);
 }
 
 w4a16_status w4a16_gemm_batched_ex(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales, uint16_t* y,
@@ -549,18 +538,24 @@ w4a16_status w4a16_gemm_batched_ex(const uint16_t* x, const uint8_t* w_packed, c
   st = make_batched_plan(B, M, N, K, split_k, cfg, group_size, &p);
   if (st != W4A16_OK) return st;
   if (p.ws_split > kMaxBytes) return W4A16_ERR_SHAPE;
-  const uint64_t need = round_up(p.ws_split, 256) + p.ws_sx;
-  if (workspace == nullptr) return W4A16_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
-  if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+  if (p.ws_split > 0) {
+    if (workspace == nullptr) return W4A16_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return W4A16_ERR_ALIGN;
+    if (workspace_bytes < round_up(p.ws_split, 256)) return W4A16_ERR_WORKSPACE;
+  }
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
   float* ws_split = p.sk > 1 ? workspace : nullptr;
-  float* ws_sx = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + round_up(p.ws_split, 256));
   const int Mt = (int)((int64_t)B * M);
-  hipError_t e = w4a16::launch_rowsum_neg136(x, ws_sx, Mt, (int)K, (int)p.ld, group_size, strm);
-  if (e != hipSuccess) return W4A16_ERR_LAUNCH;
-  e = w4a16::launch_tile(x, w_packed, scales, ws_sx, y, ws_split, nullptr, (int)M, Mt, (int)N, (int)K, B, (int)p.ld,
-                         p.gps, p.sk, p.cfg, group_size, strm);
+  const int ld = (int)round_up((uint64_t)Mt, 4);
+  float* rowsums = nullptr;
+  if (p.ws_sx > 0 && workspace != nullptr && aligned16(workspace) &&
+      workspace_bytes >= round_up(p.ws_split, 256) + p.ws_sx)
+    rowsums = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + round_up(p.ws_split, 256));
+  hipError_t e = hipSuccess;
+  if (rowsums != nullptr) e = w4a16::launch_rowsum_neg136(x, rowsums, Mt, (int)K, ld, group_size, strm);
+  if (e == hipSuccess)
+    e = w4a16::launch_tile(x, w_packed, scales, rowsums, ld, y, ws_split, nullptr, (int)M, Mt, (int)N, (int)K, B,
+                           p.gps, p.sk, p.bm, group_size, strm);
   if (e != hipSuccess) return W4A16_ERR_LAUNCH;
   if (p.sk > 1) return launched(w4a16::launch_splitk_reduce(ws_split, y, (uint64_t)Mt * (uint64_t)N, p.sk, strm));
   return W4A16_OK;

@@ -26,6 +26,7 @@
 #include "launch.hpp"
 
 #include <algorithm>
+#include <atomic>
 
 namespace w4a16 {
 
@@ -138,191 +139,20 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t* __restrict
   }
 }
 
-// ---------------------------------------------------------------- flat layout
-// Same arithmetic, but the lanes of a wave are laid over a block of R weight
-// rows (of this K-slice) so that every wave instruction reads one contiguous
-// 1 KiB run: in instruction i lane l takes 16-byte chunk c = 64 i + l of the
-// block, i.e. row c / cps, chunk c % cps (cps = chunks per row-slice).
-// R = 64 / gcd(cps, 64) rows make the block a whole number I of 1 KiB runs.
-// A lane keeps R row partials; each row is summed over the wave with DPP and
-// written by lane 63.
+// Sum of each of R row partials over the 64 lanes of a wave (DPP, no LDS
+// trips), valid in lane 63.
 template <int R>
 __device__ __forceinline__ void wave_reduce_rows(float (&acc)[R]) {
-  // every row's sum over the 64 lanes, valid in lane 63 (DPP, no LDS trips)
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) acc[rr] = wave64_sum(acc[rr]);
 }
 
 constexpr int kMaxChunks = 256;   // 32-k chunks per row-slice (64 groups)
 
-template <int R, int I, int D, int AUX>
-__global__ __launch_bounds__(256) void gemv_flat_kernel(const uint16_t* __restrict__ x,
-                                                        const uint8_t* __restrict__ w,
-                                                        const uint16_t* __restrict__ s,
-                                                        uint16_t* __restrict__ y,
-                                                        float* __restrict__ ws,
-                                                        int N, int K, int gps) {
-  const int lane = threadIdx.x & 63;
-  const int wv = (int)(blockIdx.x * 4 + (threadIdx.x >> 6));   // global wave id
-  const int W = (int)(gridDim.x * 4);
-  const int G = K / kGroup;
-  const int slice = blockIdx.y;
-  const int g0 = slice * gps;
-  const int g1 = min(G, g0 + gps);
-  const int cps = g1 > g0 ? (g1 - g0) * 4 : 0;   // chunks per row in this slice
-  const int nblk = (N + R - 1) / R;
-  // row blocks b = wv + j * W: neighbouring waves stream neighbouring blocks
-  const int nb = wv < nblk ? (nblk - 1 - wv) / W + 1 : 0;
-
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)K * 2u);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint32_t)((uint64_t)N * (uint32_t)K / 2u));
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, (uint32_t)N * (uint32_t)G * 2u);
-  const uint32_t rowb = (uint32_t)(K / 2);
-
-  // ---- x of the slice, prepared once per workgroup in LDS: each 32-k chunk
-  // as 16 dwords in the magic-constant pair order plus -136 * its sum
-  __shared__ u32x4 xprep[kMaxChunks * 4];
-  __shared__ float cinl[kMaxChunks];
-  const int tid = threadIdx.x;
-  constexpr int kPrepPer = (kMaxChunks * 4 + 255) / 256;
-  u32x4 xv[kPrepPer];
-#pragma unroll
-  for (int k = 0; k < kPrepPer; ++k) {
-    const int p = tid + 256 * k;   // 16-byte piece p = 4 * chunk + d
-    xv[k] = p < cps * 4 ? ld128(rx, (uint32_t)(g0 * kGroup) * 2u + 16u * (uint32_t)p) : u32x4{0u, 0u, 0u, 0u};
-  }
-
-  // static per-lane mapping, identical for every block
-  uint32_t woff[I], soff[I];
-  int rib[I], chi[I];
-  bool valid[I];
-#pragma unroll
-  for (int i = 0; i < I; ++i) {
-    const int c = 64 * i + lane;
-    valid[i] = cps > 0 && c < R * cps;
-    const int r = valid[i] ? c / cps : 0;
-    const int ch = valid[i] ? c - r * cps : 0;
-    rib[i] = r;
-    chi[i] = ch;
-    woff[i] = (uint32_t)r * rowb + (uint32_t)g0 * 64u + (uint32_t)ch * 16u;
-    soff[i] = ((uint32_t)r * (uint32_t)G + (uint32_t)g0 + (uint32_t)(ch >> 2)) * 2u;
-  }
-
-  u32x4 wbuf[D][I];
-  uint16_t sbuf[D][I];
-  auto issue = [&](u32x4 (&wb)[I], uint16_t (&sb)[I], int j) {
-    const int b = wv + j * W;
-    const bool live = j < nb;
-    const uint32_t wbase = (uint32_t)b * (uint32_t)R * rowb;
-    const uint32_t sbase = (uint32_t)b * (uint32_t)R * (uint32_t)G * 2u;
-#pragma unroll
-    for (int i = 0; i < I; ++i) {
-      if (live && valid[i]) {
-        wb[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, wbase + woff[i], 0, AUX);
-        sb[i] = ld16(rs, sbase + soff[i]);
-      } else {
-        wb[i] = u32x4{0u, 0u, 0u, 0u};
-        sb[i] = 0;
-      }
-    }
-  };
-#pragma unroll
-  for (int j = 0; j < D; ++j) issue(wbuf[j], sbuf[j], j);
-
-  const uint32_t ones = 0x3F803F80u;   // bf16 (1, 1)
-#pragma unroll
-  for (int k = 0; k < kPrepPer; ++k) {
-    const int p = tid + 256 * k;
-    if (p < cps * 4) {   // whole quads of a chunk are active together (cps * 4 % 4 == 0)
-      const u32x4 v = xv[k];
-      u32x4 o;
-      o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);   // (x0, x4)
-      o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);   // (x1, x5)
-      o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);   // (x2, x6)
-      o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);   // (x3, x7)
-      xprep[p] = o;
-      float sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(ones), 0.0f, false);
-      sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(ones), sx, false);
-      sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), as_bf16x2(ones), sx, false);
-      sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), as_bf16x2(ones), sx, false);
-      sx += dpp_f<0xB1>(sx);   // quad_perm [1,0,3,2]
-      sx += dpp_f<0x4E>(sx);   // quad_perm [2,3,0,1]
-      if ((p & 3) == 0) cinl[p >> 2] = -136.0f * sx;
-    }
-  }
-  __syncthreads();
-
-  const uint32_t magic = vgpr_const(kMagicPair);
-  const uint32_t mask = __builtin_amdgcn_readfirstlane(kNibblePairMask);
-  uint32_t xp[I][16];
-  float cinit[I];
-  float rmask[I][R];
-#pragma unroll
-  for (int i = 0; i < I; ++i) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const u32x4 o = valid[i] ? xprep[4 * chi[i] + d] : u32x4{0u, 0u, 0u, 0u};
-      xp[i][4 * d + 0] = o.x;
-      xp[i][4 * d + 1] = o.y;
-      xp[i][4 * d + 2] = o.z;
-      xp[i][4 * d + 3] = o.w;
-    }
-    cinit[i] = valid[i] ? cinl[chi[i]] : 0.0f;
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) rmask[i][rr] = (valid[i] && rib[i] == rr) ? 1.0f : 0.0f;
-  }
-
-  auto consume = [&](const u32x4 (&wb)[I], const uint16_t (&sb)[I], int j) {
-    float acc[R];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) acc[rr] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < I; ++i) {
-      float t = cinit[i];
-      const uint32_t wd[4] = {wb[i].x, wb[i].y, wb[i].z, wb[i].w};
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t w0 = wd[d], w1 = wd[d] >> 4, w2 = wd[d] >> 8, w3 = wd[d] >> 12;
-        t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or_sv(w0, mask, magic)),
-                                           as_bf16x2(xp[i][4 * d + 0]), t, false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or_sv(w1, mask, magic)),
-                                           as_bf16x2(xp[i][4 * d + 1]), t, false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or_sv(w2, mask, magic)),
-                                           as_bf16x2(xp[i][4 * d + 2]), t, false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or_sv(w3, mask, magic)),
-                                           as_bf16x2(xp[i][4 * d + 3]), t, false);
-      }
-      const float v = bf16f(sb[i]) * t;
-#pragma unroll
-      for (int rr = 0; rr < R; ++rr) acc[rr] = fmaf(rmask[i][rr], v, acc[rr]);
-    }
-    wave_reduce_rows<R>(acc);
-    if (lane == 63 && j < nb) {
-#pragma unroll
-      for (int rr = 0; rr < R; ++rr) {
-        const int n = (wv + j * W) * R + rr;
-        if (n < N) {
-          if (ws == nullptr) y[n] = to_bf16(acc[rr]);
-          else ws[(size_t)slice * N + n] = acc[rr];
-        }
-      }
-    }
-  };
-
-  for (int j0 = 0; j0 < nb; j0 += D) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      if (j0 + j < nb) {
-        consume(wbuf[j], sbuf[j], j0 + j);
-        if (j0 + j + D < nb) issue(wbuf[j], sbuf[j], j0 + j + D);
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- MFMA layout
-// Same stream as the flat layout (every wave instruction one contiguous 1 KiB
-// run over a block of R rows), but the multiply-add runs on the matrix cores.
+// The default for M = 1. The lanes of a wave are laid over a block of R weight
+// rows (of this K-slice) so that every wave instruction reads one contiguous
+// 1 KiB run, and the multiply-add runs on the matrix cores.
 // In instruction i lane L = m + 16 kb reads the 16 bytes of sub-chunk kb of
 // block-group 16 i + m (a block-group is one 128-k group of one row). For the
 // 4 dwords j of those bytes a 16x16x32 MFMA takes A[m][.] = the lane's 8
@@ -597,184 +427,64 @@ static bool mfma_geometry(int gs, int* R, int* I) {
 
 // Compute units of the current device (cached per device).
 static int cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int v = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cache[dev] = v;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
 }
 
-// Instances that fit the register budget of their occupancy without spills
-// (a 12-wave workgroup leaves 170 VGPRs per wave, a 16-wave one 128).
-template <int R, int I, int D, int WV, bool XL>
-constexpr bool mfma_fits() {
-  if (WV == 16) return XL && D == 1 && R * I <= 10;
-  if (WV == 12) return XL ? !(D == 2 && I == 7) : (D == 1 && I <= 3);
-  if (WV == 8) return XL || !(D == 2 && I == 7);
-  return true;
-}
-
+// One 8-wave workgroup per compute unit, x held in registers, one weight
+// block in flight per wave.
 template <int R, int I>
 static hipError_t launch_mfma_ri(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
-                                 int N, int K, int gps, int sk, int depth, int waves, int bpw, bool xlds,
-                                 hipStream_t stream) {
+                                 int N, int K, int gps, int sk, hipStream_t stream) {
+  constexpr int kWaves = 8;
   const int nblk = (N + R - 1) / R;
-  // bpw 0: one workgroup per compute unit; otherwise bpw row blocks per wave
-  const int per_wg = waves * (bpw > 0 ? bpw : 1);
-  int gx = (nblk + per_wg - 1) / per_wg;
-  if (bpw == 0) gx = std::min(cu_count(), (nblk + waves - 1) / waves);
-  if (gx < 1) gx = 1;
-#define W4A16_MF(DD, WV, XL)                                                                          \
-  if constexpr (mfma_fits<R, I, DD, WV, XL>()) {                                                           \
-    if (depth == DD && waves == WV && xlds == XL) {                                                   \
-      hipLaunchKernelGGL((gemv_mfma_kernel<R, I, DD, WV, XL>), dim3(gx, sk), dim3(64 * WV), 0, stream, x, w, \
-                         s, y, ws, N, K, gps);                                                        \
-      return hipGetLastError();                                                                       \
-    }                                                                                                 \
-  }
-  W4A16_MF(1, 4, false) W4A16_MF(2, 4, false) W4A16_MF(1, 8, false) W4A16_MF(2, 8, false) W4A16_MF(1, 12, false)
-  W4A16_MF(1, 4, true) W4A16_MF(2, 4, true) W4A16_MF(3, 4, true) W4A16_MF(1, 8, true) W4A16_MF(2, 8, true)
-  W4A16_MF(1, 12, true) W4A16_MF(2, 12, true) W4A16_MF(1, 16, true)
-#undef W4A16_MF
-  return hipErrorInvalidValue;
+  const int gx = std::max(1, std::min(cu_count(), (nblk + kWaves - 1) / kWaves));
+  hipLaunchKernelGGL((gemv_mfma_kernel<R, I, 1, kWaves, false>), dim3(gx, sk), dim3(64 * kWaves), 0, stream, x, w,
+                     s, y, ws, N, K, gps);
+  return hipGetLastError();
 }
 
-static hipError_t launch_mfma(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
-                              int N, int K, int gps, int sk, int R, int I, int depth, int waves, int bpw,
-                              bool xlds, hipStream_t stream) {
-#define W4A16_RI(RR, II) \
-  if (R == RR && I == II)  \
-    return launch_mfma_ri<RR, II>(x, w, s, y, ws, N, K, gps, sk, depth, waves, bpw, xlds, stream);
-  W4A16_RI(1, 1) W4A16_RI(1, 2) W4A16_RI(1, 3) W4A16_RI(1, 4)
-  W4A16_RI(2, 1) W4A16_RI(2, 3) W4A16_RI(2, 5) W4A16_RI(2, 7)
-  W4A16_RI(4, 1) W4A16_RI(4, 3) W4A16_RI(4, 5) W4A16_RI(4, 7)
-#undef W4A16_RI
-  return hipErrorInvalidValue;
-}
-
-// flat-layout geometry for a slice of `cps` chunks per row; false if it does
-// not fit the instantiated shapes (R <= 4 rows, I <= 8 runs of 1 KiB)
-static bool flat_geometry(int cps, int* R, int* I) {
-  int g = 64, a = cps;
-  while (a % 2 == 0 && g > 1) { a /= 2; g /= 2; }   // g = 64 / gcd(cps, 64)
-  *R = g;
-  *I = g * cps / 64;
-  return *R <= 4 && *I >= 1 && *I <= 8;
-}
-
-template <int R, int I>
-static hipError_t launch_flat_ri(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
-                                 int N, int K, int gps, int sk, int depth, int nt, int blocks_per_wave,
-                                 hipStream_t stream) {
-  const int nblk = (N + R - 1) / R;
-  const int waves = (nblk + blocks_per_wave - 1) / blocks_per_wave;
-  dim3 grid((waves + 3) / 4, sk);
-#define W4A16_FLAT(DD, AA)                                                                           \
-  if (depth == DD && nt == AA) {                                                                     \
-    hipLaunchKernelGGL((gemv_flat_kernel<R, I, DD, AA * 2>), grid, dim3(256), 0, stream, x, w, s, y, ws, \
-                       N, K, gps);                                                                   \
-    return hipGetLastError();                                                                        \
-  }
-  W4A16_FLAT(1, 0)
-  W4A16_FLAT(2, 0)
-  W4A16_FLAT(3, 0)
-  W4A16_FLAT(1, 1)
-  W4A16_FLAT(2, 1)
-  W4A16_FLAT(3, 1)
-#undef W4A16_FLAT
-  return hipErrorInvalidValue;
-}
-
-static hipError_t launch_flat(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
-                              int N, int K, int gps, int sk, int R, int I, int depth, int nt, int bpw,
-                              hipStream_t stream) {
-#define W4A16_RI(RR, II) \
-  if (R == RR && I == II) return launch_flat_ri<RR, II>(x, w, s, y, ws, N, K, gps, sk, depth, nt, bpw, stream);
-  W4A16_RI(1, 1) W4A16_RI(1, 2) W4A16_RI(1, 3) W4A16_RI(1, 4) W4A16_RI(1, 5) W4A16_RI(1, 6) W4A16_RI(1, 7)
-  W4A16_RI(1, 8)
-  W4A16_RI(2, 1) W4A16_RI(2, 3) W4A16_RI(2, 5) W4A16_RI(2, 7)
-  W4A16_RI(4, 1) W4A16_RI(4, 3) W4A16_RI(4, 5) W4A16_RI(4, 7)
-#undef W4A16_RI
-  return hipErrorInvalidValue;
-}
-
+// Half-wave layout (slices with no MFMA geometry): two rows in flight per
+// half-wave, about four rows per half-wave, non-temporal weight loads.
 template <int CPL>
-static hipError_t launch_gemv_cpl(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y,
-                                  float* ws, int N, int K, int gps, int sk, int variant, hipStream_t stream) {
-  // variant: 10 * prefetch depth + rows per half-wave target (1..9); 100 adds
-  // the non-temporal cache policy on the weight stream
-  const int nt = (variant / 100) % 10;
-  const int depth = (variant / 10) % 10;
-  const int rows_target = variant % 10 > 0 ? variant % 10 : 1;
-  const int halfwaves = (N + rows_target - 1) / rows_target;
+static hipError_t launch_halfwave(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
+                                  int N, int K, int gps, int sk, hipStream_t stream) {
+  constexpr int kRowsPerHalfwave = 4;
+  const int halfwaves = (N + kRowsPerHalfwave - 1) / kRowsPerHalfwave;
   const int blocks = (halfwaves + 7) / 8;
-  dim3 grid(blocks > 0 ? blocks : 1, sk);
-#define W4A16_GEMV(DD, AA)                                                                          \
-  if (depth == DD && nt == AA) {                                                                    \
-    hipLaunchKernelGGL((gemv_m1_kernel<CPL, DD, AA * 2>), grid, dim3(256), 0, stream, x, w, s, y, ws, \
-                       N, K, gps);                                                                  \
-    return hipGetLastError();                                                                       \
-  }
-  W4A16_GEMV(1, 0)
-  W4A16_GEMV(2, 0)
-  W4A16_GEMV(3, 0)
-  W4A16_GEMV(4, 0)
-  W4A16_GEMV(1, 1)
-  W4A16_GEMV(2, 1)
-  W4A16_GEMV(3, 1)
-  W4A16_GEMV(4, 1)
-#undef W4A16_GEMV
-  return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemv_m1_kernel<CPL, 2, 2>), dim3(blocks > 0 ? blocks : 1, sk), dim3(256), 0, stream, x, w, s,
+                     y, ws, N, K, gps);
+  return hipGetLastError();
 }
 
-constexpr int kHalfwaveFallback = 124;
-
-bool gemv_flat_fits(int gps) {
-  int R, I;
-  return flat_geometry(gps * 4, &R, &I);
-}
-
-hipError_t launch_gemv_m1(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y,
-                          float* ws, int N, int K, int gps, int sk, int variant,
-                          hipStream_t stream) {
-  // variant: 1000 * layout (0 flat, 1 half-wave, 2 MFMA) + layout digits;
-  // flat and half-wave: 100 * non-temporal + 10 * prefetch depth + blocks
-  // (flat) / rows (half-wave) per wave
-  const int layout = (variant / 1000) % 10;
+hipError_t launch_gemv_m1(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws, int N,
+                          int K, int gps, int sk, bool force_halfwave, hipStream_t stream) {
   int R = 0, I = 0;
-  if (layout == 2 && mfma_geometry(gps, &R, &I)) {
-    // 2000 + 100 * (4 * x-in-LDS + waves / 4 - 1) + 10 * prefetch depth
-    //      + row blocks per wave (0: one workgroup per compute unit)
-    const int h = (variant / 100) % 10;
-    const int waves = 4 * ((h & 3) + 1);
-    const bool xlds = (h & 4) != 0;
-    const int depth = (variant / 10) % 10 > 0 ? (variant / 10) % 10 : 1;
-    const int bpw = variant % 10;
-    return launch_mfma(x, w, s, y, ws, N, K, gps, sk, R, I, depth, waves, bpw, xlds, stream);
+  if (!force_halfwave && mfma_geometry(gps, &R, &I)) {
+#define W4A16_RI(RR, II) \
+  if (R == RR && I == II) return launch_mfma_ri<RR, II>(x, w, s, y, ws, N, K, gps, sk, stream);
+    W4A16_RI(1, 1) W4A16_RI(1, 2) W4A16_RI(1, 3) W4A16_RI(1, 4)
+    W4A16_RI(2, 1) W4A16_RI(2, 3) W4A16_RI(2, 5) W4A16_RI(2, 7)
+    W4A16_RI(4, 1) W4A16_RI(4, 3) W4A16_RI(4, 5) W4A16_RI(4, 7)
+#undef W4A16_RI
   }
-  if (layout == 0 && flat_geometry(gps * 4, &R, &I)) {
-    const int nt = (variant / 100) % 10;
-    const int depth = (variant / 10) % 10 > 0 ? (variant / 10) % 10 : 2;
-    const int bpw = variant % 10 > 0 ? variant % 10 : 4;
-    return launch_flat(x, w, s, y, ws, N, K, gps, sk, R, I, depth, nt, bpw, stream);
-  }
-  // the half-wave kernel takes every slice of at most 64 groups; an MFMA
-  // variant whose slice length has no MFMA geometry runs its default
-  const int v = layout == 2 ? kHalfwaveFallback : variant % 1000;
-  const int cpl = (gps * 4 + 31) / 32;   // chunks per lane in a slice
-  switch (cpl) {
-    case 1: return launch_gemv_cpl<1>(x, w, s, y, ws, N, K, gps, sk, v, stream);
-    case 2: return launch_gemv_cpl<2>(x, w, s, y, ws, N, K, gps, sk, v, stream);
-    case 3: return launch_gemv_cpl<3>(x, w, s, y, ws, N, K, gps, sk, v, stream);
-    case 4: return launch_gemv_cpl<4>(x, w, s, y, ws, N, K, gps, sk, v, stream);
-    case 5: return launch_gemv_cpl<5>(x, w, s, y, ws, N, K, gps, sk, v, stream);
-    case 6: return launch_gemv_cpl<6>(x, w, s, y, ws, N, K, gps, sk, v, stream);
-    case 7: return launch_gemv_cpl<7>(x, w, s, y, ws, N, K, gps, sk, v, stream);
-    case 8: return launch_gemv_cpl<8>(x, w, s, y, ws, N, K, gps, sk, v, stream);
+  // the half-wave kernel takes every slice of at most 64 groups
+  switch ((gps * 4 + 31) / 32) {   // 32-k chunks per lane in a slice
+    case 1: return launch_halfwave<1>(x, w, s, y, ws, N, K, gps, sk, stream);
+    case 2: return launch_halfwave<2>(x, w, s, y, ws, N, K, gps, sk, stream);
+    case 3: return launch_halfwave<3>(x, w, s, y, ws, N, K, gps, sk, stream);
+    case 4: return launch_halfwave<4>(x, w, s, y, ws, N, K, gps, sk, stream);
+    case 5: return launch_halfwave<5>(x, w, s, y, ws, N, K, gps, sk, stream);
+    case 6: return launch_halfwave<6>(x, w, s, y, ws, N, K, gps, sk, stream);
+    case 7: return launch_halfwave<7>(x, w, s, y, ws, N, K, gps, sk, stream);
+    case 8: return launch_halfwave<8>(x, w, s, y, ws, N, K, gps, sk, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,20 +1,24 @@
 // Prefill / grouped W4A16 GEMM for gfx950 with LDS-DMA staging and in-register
 // dequantisation.
 //
-// Numerics are those of the tile kernel: the weight operand is bf16(128 + q),
-// exact, from the magic-constant OR ("[ROCm][Kernel] W4A16 skinny GEMM:
-// hand-asm kernel for gfx1151", section 1); each 128-group's MFMA chain of a
-// 16x16 output tile starts from -136 * sum_{k in g} x[m, k] (row sums from the
-// pre-pass), so after the group's 4 MFMA steps it holds sum_k x * (q - 8) in
-// fp32, which is scaled by the column's bf16 scale and added to the fp32
-// accumulator. No weight is ever rounded.
+// Numerics: the weight operand is bf16(128 + q), exact, from the
+// magic-constant OR ("[ROCm][Kernel] W4A16 skinny GEMM: hand-asm kernel for
+// gfx1151", section 1); each 128-group's MFMA chain of a 16x16 output tile
+// starts from -136 * sum_{k in g} x[m, k], so after the group's 4 MFMA steps it
+// holds sum_k x * (q - 8) in fp32, which is scaled by the column's bf16 scale
+// and added to the fp32 accumulator. No weight is ever rounded. The row sums
+// are formed in the kernel, on the matrix core: an MFMA of the X fragments
+// against a constant bf16(-136) operand gives -136 * sum_k x[m, k] in every
+// output column; the MS row tiles of a stage are spread over the 8 waves and
+// done one group ahead, into the stage's row-sum slots.
 //
 // Structure (one 512-thread workgroup per (16 MS) x 256 output tile, 8 waves
 // of (16 MS) x 32, MS = 3 .. 9; one workgroup per compute unit):
-//  * one K-stage = one 128-group: X [16 MS rows, 128 k] bf16, the packed
-//    weights [256 rows, 64 B] (16 KiB, still 4-bit) and the 16 MS row sums;
-//    NSTAGE stages in LDS, filled by buffer loads that write LDS directly (no
-//    registers, no VALU), issued NSTAGE - 1 groups ahead;
+//  * one K-stage = one 128-group: X [16 MS rows, 128 k] bf16 and the packed
+//    weights [256 rows, 64 B] (16 KiB, still 4-bit), filled by buffer loads
+//    that write LDS directly (no registers, no VALU), issued two groups
+//    ahead, and the 16 MS row sums (-136 * sum x) written by the waves one
+//    group ahead; three stages in LDS;
 //  * each wave reads its 32 columns of packed weights once per group and
 //    dequantises them in registers (32 VGPRs of bf16 B operands), then sweeps
 //    the MS row tiles of 16: 4 MFMA 16x16x32 steps per (row tile, column
@@ -60,7 +64,7 @@ struct PrefillArgs {
   const uint16_t* x;       // [M_total, K]
   const uint8_t* w;        // [G, N, K/2]
   const uint16_t* s;       // [G, N, K/GS]
-  const float* sxn;        // [K/GS, ld]
+  const float* sxn;        // [K/GS, ld] -136 * row sums from the pre-pass (RSK false), else unused
   uint16_t* y;             // [M_total, N]
   float* ws;               // [SK, M_total, N] fp32 split-K partials, or nullptr
   const int32_t* m_sizes;  // [G] on device, or nullptr
@@ -85,9 +89,9 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst
 
 }  // namespace
 
-template <int NSTAGE, int MS, int GS>
+template <int NSTAGE, int MS, int GS, bool RSK>
 __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs args) {
-  static_assert(NSTAGE == 2 || NSTAGE == 3, "stages");
+  static_assert(NSTAGE == 3, "stages: the row sums of group j + 1 are formed while group j + 2 is in flight");
   static_assert(MS >= 2 && MS <= 16, "row tiles");
   static_assert(GS == 128 || GS == 32, "scale group");
   constexpr int NSG = 128 / GS;         // scale groups per 128-k stage
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   constexpr int NQX = 4 * MS;           // X DMA instructions per group (4 rows of 256 B each)
   constexpr int QX = (NQX + kNW - 1) / kNW;   // per wave (block q = wave + 8 i)
   constexpr int QW = 16 / kNW;          // W DMA instructions per wave and group
-  constexpr int RL = 4 * MS;            // row-sum DMA lanes of wave 0 (16 B = 4 rows each)
+  constexpr int RL = 4 * MS;            // row-sum DMA lanes (16 B = 4 rows each), RSK false
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -130,8 +134,9 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   // past N read other scales or zeros and are never stored
   const __amdgpu_buffer_rsrc_t rs =
       make_scale_rsrc(args.s, (uint32_t)((size_t)args.G * args.N * Gs));
+  // row sums of the pre-pass (RSK false): [K/GS, ld] fp32, from this tile's first row
   const __amdgpu_buffer_rsrc_t rsx =
-      make_rsrc(args.sxn + row0, (uint32_t)(((size_t)Gs * args.ld - row0) * 4u));
+      make_rsrc(RSK ? nullptr : args.sxn + row0, RSK ? 0u : (uint32_t)(((size_t)Gs * args.ld - row0) * 4u));
   const int slice = blockIdx.y;
   const int gb = slice * args.gps;
   const int ge = min(Gk, gb + args.gps);
@@ -154,8 +159,6 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     const int wr = lane >> 2, wp = lane & 3;
     return (uint32_t)(16 * QW * wv + wr) * K2 + 16u * (uint32_t)(wp ^ ((wr >> 1) & 3));
   };
-  // row sums: lanes 0..RL-1 of wave 0 fetch 4 rows each
-  auto rvo = [&]() { return (uint32_t)(4 * lane) * 4u; };
 
   // Row offsets always go into the vector offset, which the hardware range
   // checks against the buffer extent (rows past the tile read zeros); the
@@ -176,10 +179,11 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     const uint32_t wo = wvo();
 #pragma unroll
     for (int i = 0; i < QW; ++i) dma16(rw, base + ST::kX + 1024 * (QW * wv + i), wo + (uint32_t)i * 16u * K2, gw);
-    // wave sg < NSG fetches the row sums of scale group sg of the stage
-    if (wv < NSG && lane < RL)
+    // RSK false: wave sg < NSG fetches the row sums of scale group sg of the
+    // stage, lanes 0 .. RL - 1 four rows each
+    if (!RSK && wv < NSG && lane < RL)
       dma16(rsx, base + ST::kX + ST::kW + ST::kRows * 4 * wv,
-            rvo() + (uint32_t)(NSG * g + wv) * (uint32_t)args.ld * 4u, 0u);
+            (uint32_t)(4 * lane) * 4u + (uint32_t)(NSG * g + wv) * (uint32_t)args.ld * 4u, 0u);
   };
 
   // ---- scales: GS = 128: the aligned word holding s[n][g] for this lane's
@@ -228,17 +232,71 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
 
   SW sc_cur[SN], sc_nxt[SN];
 
+  // GS = 32 operand offsets (natural k order, see below)
+  const uint32_t aoffN = (uint32_t)m16 * 256u + 16u * (uint32_t)(kb ^ (m16 & 7));
+  const uint32_t boffN = ST::kX + (uint32_t)(TN * wv + m16) * 64u + 4u * (uint32_t)kb + 16u * (uint32_t)((m16 >> 1) & 3);
+  // ---- -136 * row sums of a landed stage, on the matrix core: MFMA steps of
+  // the X fragments against a constant bf16(-136) operand give D[m][n] =
+  // -136 * sum_k x[m, k] in every column n, so the lanes of column 0 (lane
+  // (0, kb) holds rows 4 kb + 0..3) store the tile's 16 sums. GS = 128: the
+  // group's four steps chained (any k order sums the whole group); GS = 32:
+  // step st alone is 32-group st (natural k order). Row tile ms of the stage
+  // is taken by wave (ms + j) mod 8, so that the extra tile of MS > 8 moves
+  // from wave to wave with the group j. Products x * 136 are exact in fp32.
+  // The MFMAs are issued at the start of a group's compute and their results
+  // stored after its dequantisation, so no wave waits on them.
+  constexpr int RSM = (MS + kNW - 1) / kNW;   // row tiles of sums per wave, at most
+  const uint32_t neg136 = vgpr_const(0xC308C308u);   // bf16(-136) pair
+  const bf16x8 bneg = __builtin_bit_cast(bf16x8, u32x4{neg136, neg136, neg136, neg136});
+  auto rs_tile = [&](int j, int i) { return ((wv - j) & (kNW - 1)) + kNW * i; };   // wave-uniform
+  auto rs_issue = [&](int stage, int j, f32x4 (&d)[RSM][NSG]) {
+    const uint8_t* sb = lds + stage * ST::kBytes;
+#pragma unroll
+    for (int i = 0; i < RSM; ++i) {
+      const int ms = rs_tile(j, i);
+      if (ms < MS) {
+        if constexpr (GS == 128) {
+          d[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const bf16x8 a =
+                *reinterpret_cast<const bf16x8*>(sb + (aoff0 ^ (16u * (uint32_t)st)) + 4096u * (uint32_t)ms);
+            d[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bneg, d[i][0], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const bf16x8 a =
+                *reinterpret_cast<const bf16x8*>(sb + (aoffN ^ (64u * (uint32_t)st)) + 4096u * (uint32_t)ms);
+            d[i][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bneg, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+  auto rs_store = [&](int stage, int j, const f32x4 (&d)[RSM][NSG]) {
+    uint8_t* sb = lds + stage * ST::kBytes;
+#pragma unroll
+    for (int i = 0; i < RSM; ++i) {
+      const int ms = rs_tile(j, i);
+      if (ms < MS && m16 == 0) {
+#pragma unroll
+        for (int st = 0; st < NSG; ++st)
+          *reinterpret_cast<f32x4*>(sb + roff + (uint32_t)(ST::kRows * 4 * st) + 64u * (uint32_t)ms) = d[i][st];
+      }
+    }
+  };
+
   // GS = 32: MFMA step st covers scale group st of the stage (natural k
   // order: lane (r, kb) of step st holds k = 32 st + 8 kb + 0..7 for both
   // operands), each step starts from its group's row sums and is rescaled on
   // its own. A: chunk 4 st + kb of the row, slot (4 st + kb) ^ (row & 7) =
   // ((kb ^ (row & 7)) ^ 4 st); B: dword kb of chunk st of the packed row, slot
   // st ^ ((row >> 1) & 3).
-  const uint32_t aoffN = (uint32_t)m16 * 256u + 16u * (uint32_t)(kb ^ (m16 & 7));
-  const uint32_t boffN = ST::kX + (uint32_t)(TN * wv + m16) * 64u + 4u * (uint32_t)kb + 16u * (uint32_t)((m16 >> 1) & 3);
-  auto compute32 = [&](int stage) {
+  auto compute32 = [&](int stage, int rstage, int j) {
     if constexpr (GS == 32) {
     const uint8_t* sb = lds + stage * ST::kBytes;
+    f32x4 rsd[RSM][NSG];
     // row tile ms's operands: the 4 steps' initial C (row sums of the
     // stage's four 32-groups) and A fragments; the next row tile's reads go
     // out before this tile's MFMAs (two register sets)
@@ -253,6 +311,7 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
         a[st] = *reinterpret_cast<const bf16x8*>(sb + (aoffN ^ (64u * (uint32_t)st)) + 4096u * (uint32_t)ms);
     };
     read_rows(0, cq[0], aq[0]);
+    if (rstage >= 0) rs_issue(rstage, j, rsd);
     bf16x8 bd[SN][4];
 #pragma unroll
     for (int ns = 0; ns < SN; ++ns)
@@ -272,6 +331,7 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     for (int ns = 0; ns < SN; ++ns)
 #pragma unroll
       for (int st = 0; st < 4; ++st) scv[ns][st] = scale32(sc_cur[ns], st);
+    if (rstage >= 0) rs_store(rstage, j, rsd);
     // step st's products are rescaled after the next step's MFMAs are issued
     // (the last step's after the next row tile's first step), so no MFMA
     // result is read right behind its issue; the empty asm pins each rescale
@@ -305,9 +365,10 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     }
   };
 
-  auto compute = [&](int stage, int g) {
+  auto compute = [&](int stage, int g, int rstage, int j) {
     if constexpr (GS == 128) {
     const uint8_t* sb = lds + stage * ST::kBytes;
+    f32x4 rsd[RSM][NSG];
     // row tile ms's operands: initial C and the 4 steps' A fragments; the next
     // row tile's reads go out before this tile's MFMAs (two register sets)
     f32x4 cq[2];
@@ -319,6 +380,7 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
         a[st] = *reinterpret_cast<const bf16x8*>(sb + (aoff0 ^ (16u * (uint32_t)st)) + 4096u * (uint32_t)ms);
     };
     read_rows(0, cq[0], aq[0]);
+    if (rstage >= 0) rs_issue(rstage, j, rsd);
     // dequantise this wave's TN columns x 128 k: bd[ns][st] = 8 bf16 (128 + q)
     bf16x8 bd[SN][4];
 #pragma unroll
@@ -339,6 +401,7 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     float scv[SN];
 #pragma unroll
     for (int ns = 0; ns < SN; ++ns) scv[ns] = scale_of(sc_cur[ns], ns, g);
+    if (rstage >= 0) rs_store(rstage, j, rsd);
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
       const int cur = ms & 1;
@@ -364,26 +427,37 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
       }
   };
 
-  // ---- pipeline: group j + NSTAGE - 1 is loaded while group j is computed.
-  // The barrier that ends group j waits for all of this wave's vector-memory
-  // operations (vmcnt(0)): that includes the DMA of group j + 1, and also the
-  // DMA of group j + 2 issued at the start of group j, which has had a whole
-  // group of compute to land. A precise count would let group j + 2 stay in
-  // flight, but it is only correct while the compiler emits no other vector
-  // memory operations (spills count too), so the simple wait is used.
+  // ---- pipeline: group j + 2 is loaded while group j is computed, and (RSK)
+  // the row sums of group j + 1 (landed) are formed during group j's compute
+  // (otherwise they arrive with the stage's DMA from the pre-pass). The
+  // barrier that ends group j waits for all of this wave's vector-memory
+  // operations (vmcnt(0)) and LDS writes: that includes the DMA of group
+  // j + 1 and the DMA of group j + 2 issued at the start of group j, which
+  // has had a whole group of compute to land, and publishes group j + 1's row
+  // sums. A precise count would let group j + 2 stay in flight, but it is only
+  // correct while the compiler emits no other vector memory operations
+  // (spills count too), so the simple wait is used.
   if (ng > 0) {
     issue(gb, 0);
-    if (NSTAGE == 3 && ng > 1) issue(gb + 1, 1);
+    if (ng > 1) issue(gb + 1, 1);
     load_scales(sc_cur, gb);
     wait_vm_barrier<0>();
+    if constexpr (RSK) {
+      f32x4 rsd[RSM][NSG];
+      rs_issue(0, 0, rsd);
+      rs_store(0, 0, rsd);
+      wait_vm_barrier<0>();
+    }
   }
   for (int j = 0; j < ng; ++j) {
     const int g = gb + j;
     const bool ahead = j + NSTAGE - 1 < ng;
     if (ahead) issue(g + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE);
     if (j + 1 < ng) load_scales(sc_nxt, g + 1);
-    if constexpr (GS == 128) compute(j % NSTAGE, g);
-    else compute32(j % NSTAGE);
+    // RSK: the row sums of group j + 1 (landed) are formed during group j
+    const int rstage = RSK && j + 1 < ng ? (j + 1) % NSTAGE : -1;
+    if constexpr (GS == 128) compute(j % NSTAGE, g, rstage, j + 1);
+    else compute32(j % NSTAGE, rstage, j + 1);
     if (j + 1 < ng) {
       wait_vm_barrier<0>();
 #pragma unroll
@@ -426,13 +500,61 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   }
 }
 
-template <int NSTAGE, int MS, int GS = 128>
-static hipError_t launch_prefill_t(PrefillArgs a, int sk, hipStream_t stream) {
+// ---------------------------------------------------------------- row-sum pre-pass
+// out[g * ld + m] = -136 * sum_{k in group g} x[m, k], fp32, for groups of GS
+// = 128 or 32 k: the initial accumulators of the tile kernel's group chains
+// when they come from a separate pass (the tile kernel forms them itself
+// otherwise). One wave per row; a wave instruction covers 512 consecutive k
+// and up to 8 of them are in flight before any is reduced; a group's lanes
+// (16 for 128 k, 4 for 32 k) are summed with DPP. Loads past the row read
+// zeros (exact buffer extent).
+template <int GS>
+__global__ __launch_bounds__(256) void rowsum_neg136_kernel(const uint16_t* __restrict__ x,
+                                                           float* __restrict__ out, int M, int K, int ld) {
+  constexpr int U = 8;
+  constexpr int LPG = GS / 8;   // lanes per group
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)m * K, (uint32_t)K * 2u);
+  for (int base = 0; base < K; base += 512 * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld128(rx, (uint32_t)(base + 512 * u + 8 * lane) * 2u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = base + 512 * u + 8 * lane;
+      float p = (bf16lo(v[u].x) + bf16hi(v[u].x)) + (bf16lo(v[u].y) + bf16hi(v[u].y)) +
+                (bf16lo(v[u].z) + bf16hi(v[u].z)) + (bf16lo(v[u].w) + bf16hi(v[u].w));
+      if constexpr (LPG == 16) {
+        p = row16_sum(p);
+      } else {
+        p += dpp_f<0xB1>(p);   // quad_perm [1,0,3,2]
+        p += dpp_f<0x4E>(p);   // quad_perm [2,3,0,1]
+      }
+      if ((lane & (LPG - 1)) == 0 && k < K) out[(size_t)(k / GS) * ld + m] = -136.0f * p;
+    }
+  }
+}
+
+hipError_t launch_rowsum_neg136(const uint16_t* x, float* out, int M, int K, int ld, int gsize, hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  if (gsize == 128)
+    hipLaunchKernelGGL(rowsum_neg136_kernel<128>, dim3((M + 3) / 4), dim3(256), 0, stream, x, out, M, K, ld);
+  else if (gsize == 32)
+    hipLaunchKernelGGL(rowsum_neg136_kernel<32>, dim3((M + 3) / 4), dim3(256), 0, stream, x, out, M, K, ld);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <int NSTAGE, int MS, int GS, bool RSK>
+static hipError_t launch_prefill_rsk(PrefillArgs a, int sk, hipStream_t stream) {
   constexpr int BM = Stage<MS, GS>::kRows;
   const int lds_bytes = NSTAGE * Stage<MS, GS>::kBytes;
   static std::atomic<uint64_t> lds_set{0};   // per instantiation and device
   const hipError_t ea =
-      ensure_dyn_lds(reinterpret_cast<const void*>(&prefill_kernel<NSTAGE, MS, GS>), lds_bytes, lds_set);
+      ensure_dyn_lds(reinterpret_cast<const void*>(&prefill_kernel<NSTAGE, MS, GS, RSK>), lds_bytes, lds_set);
   if (ea != hipSuccess) return ea;
   a.mtiles = a.m_uniform > 0 ? a.G * ((a.m_uniform + BM - 1) / BM)
                              : (a.M_total + BM - 1) / BM + (a.m_sizes != nullptr ? a.G : 0);
@@ -440,30 +562,47 @@ static hipError_t launch_prefill_t(PrefillArgs a, int sk, hipStream_t stream) {
   const long long blocks = (long long)a.mtiles * a.ntiles;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<NSTAGE, MS, GS>), dim3((unsigned)blocks, sk), dim3(64 * kNW), lds_bytes, stream,
-                     a);
+  hipLaunchKernelGGL((prefill_kernel<NSTAGE, MS, GS, RSK>), dim3((unsigned)blocks, sk), dim3(64 * kNW), lds_bytes,
+                     stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, uint16_t* y,
-                          float* ws, const int32_t* m_sizes, int m_uniform, int M_total, int N, int K, int G,
-                          int ld, int gps, int sk, int row_tiles, int gsize, hipStream_t stream) {
+// row sums formed in the kernel (sxn == nullptr) or taken from the pre-pass
+template <int NSTAGE, int MS, int GS = 128>
+static hipError_t launch_prefill_t(PrefillArgs a, int sk, hipStream_t stream) {
+  if (a.sxn == nullptr) return launch_prefill_rsk<NSTAGE, MS, GS, true>(a, sk, stream);
+  return launch_prefill_rsk<NSTAGE, MS, GS, false>(a, sk, stream);
+}
+
+// Tile heights: 16 MS rows, MS = 3 .. 9 (48 .. 144 rows) at group 128; at
+// group 32 the four row-sum sets per stage leave room for MS = 5 .. 8 only
+// (a 144-row tile would not fit three stages in LDS).
+bool tile_rows_ok(int bm, int gsize) {
+  if (bm % 16 != 0) return false;
+  const int ms = bm / 16;
+  if (gsize == 128) return ms >= 3 && ms <= 9;
+  if (gsize == 32) return ms >= 5 && ms <= 8;
+  return false;
+}
+
+hipError_t launch_tile(const uint16_t* x, const uint8_t* w, const uint16_t* s, const float* sxn, int ld, uint16_t* y,
+                       float* ws, const int32_t* m_sizes, int m_uniform, int M_total, int N, int K, int G, int gps,
+                       int sk, int bm, int gsize, hipStream_t stream) {
+  if (!tile_rows_ok(bm, gsize)) return hipErrorInvalidValue;
   PrefillArgs a;
   a.x = x; a.w = w; a.s = s; a.sxn = sxn; a.y = y; a.ws = ws; a.m_sizes = m_sizes; a.m_uniform = m_uniform;
   a.M_total = M_total; a.N = N; a.K = K; a.G = G; a.ld = ld; a.gps = gps;
   a.mtiles = 0; a.ntiles = 0;
   if (gsize == 32) {
-    // four row-sum sets per stage: 144-row tiles would not fit 3 stages in LDS
-    switch (row_tiles) {
-      case 8: return launch_prefill_t<3, 8, 32>(a, sk, stream);   // 3 x 50 KiB stages
+    switch (bm / 16) {
+      case 8: return launch_prefill_t<3, 8, 32>(a, sk, stream);   // 3 x 50.5 KiB stages
       case 7: return launch_prefill_t<3, 7, 32>(a, sk, stream);
       case 6: return launch_prefill_t<3, 6, 32>(a, sk, stream);
       case 5: return launch_prefill_t<3, 5, 32>(a, sk, stream);
       default: return hipErrorInvalidValue;
     }
   }
-  if (gsize != 128) return hipErrorInvalidValue;
-  switch (row_tiles) {
+  switch (bm / 16) {
     case 9: return launch_prefill_t<3, 9>(a, sk, stream);     // 144 x 256 tiles, 3 x 52.6 KiB stages
     case 8: return launch_prefill_t<3, 8>(a, sk, stream);     // 128 x 256 tiles, 3 x 48.5 KiB stages
     case 7: return launch_prefill_t<3, 7>(a, sk, stream);     // 112 x 256 tiles, 3 x 44.4 KiB stages

@@ -1,4 +1,4 @@
-// Small-batch decode, 1 <= M <= 16: Y[M, N] with bf16 MFMA 16x16x32.
+// Small-batch decode, 1 <= M <= 48: Y[M, N] with bf16 MFMA 16x16x32.
 //
 // X (at most 16 rows) is the 16-row A operand (rows >= M read as zero through
 // the exact buffer extent); a column block of 16 * NT output columns is
@@ -294,268 +294,6 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
     }
 }
 
-// ---------------------------------------------------------------- streaming layout
-// Same contraction as above (A = X, at most 16 rows; B = dequantised weight
-// columns; C starts from -136 * sum(x) of the group), organised like the
-// decode GEMV: one workgroup per compute unit, each wave streaming row blocks
-// of 16 NT weight rows through a ring of D units in flight, so that the
-// whole GPU keeps megabytes of weight requests outstanding.
-//  * The workgroup stages its K-slice of X once in LDS: 16-byte pieces
-//    (group g, step st, lane l = m + 16 kb) holding x[m][128 g + 32 kb + 8 st
-//    + (0,4,1,5,2,6,3,7)], the pair order of the magic unpack, so that each
-//    MFMA A operand is one conflict-free ds_read_b128; with it, -136 * the
-//    group sums of each row (C init, lane (n, kb) holds rows 4 kb + 0..3).
-//  * A unit is one row block x GB = 4 groups: per lane NT x 4 x 16 bytes of
-//    weights (16 rows x 64 bytes per wave instruction, four instructions
-//    covering 256 consecutive bytes of each row) and their scale words.
-//    Units past the wave's last one, and groups past the slice, read a dead
-//    offset (zeros, no traffic): their scale is 0, so they add nothing.
-//  * Unpack: (w >> 4 j) & 0x000F000F | 0x43004300 with one 64-bit shift per
-//    two dwords.
-template <int NT, int D, int WAVES, int GB>
-__global__ __launch_bounds__(64 * WAVES) void skinny_stream_kernel(const uint16_t* __restrict__ x,
-                                                                   const uint8_t* __restrict__ w,
-                                                                   const uint16_t* __restrict__ s,
-                                                                   uint16_t* __restrict__ y,
-                                                                   float* __restrict__ ws,
-                                                                   int M, int N, int K, int gps) {
-  constexpr int NTHR = 64 * WAVES;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n16 = lane & 15, kb = lane >> 4;
-  const int G = K / kGroup;
-  const int slice = blockIdx.y;
-  const int g0 = slice * gps;
-  const int Gs = min(G, g0 + gps) > g0 ? min(G, g0 + gps) - g0 : 0;
-  const int C = (Gs + GB - 1) / GB;     // units per row block
-  // row blocks of the workgroup: a contiguous balanced range, striped over waves
-  const int RB = 16 * NT;
-  const int nblk = (N + RB - 1) / RB;
-  const int bper = nblk / (int)gridDim.x, brem = nblk - bper * (int)gridDim.x;
-  const int b_lo = (int)blockIdx.x * bper + min((int)blockIdx.x, brem);
-  const int nbw = bper + ((int)blockIdx.x < brem ? 1 : 0);
-  const int nb = wq < nbw ? (nbw - 1 - wq) / WAVES + 1 : 0;   // row blocks of this wave
-  const int U = nb * C;                                          // units of this wave
-
-  if (Gs == 0) {
-    // a slice past the last group: its partials are zeros
-    for (int bi = 0; bi < nb; ++bi) {
-      const int r0 = (b_lo + wq + bi * WAVES) * RB;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int n = r0 + 16 * t + n16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 4 * kb + i;
-          if (n < N && m < M) {
-            if (ws == nullptr) y[(size_t)m * N + n] = 0;
-            else ws[((size_t)slice * M + m) * N + n] = 0.0f;
-          }
-        }
-      }
-    }
-    return;
-  }
-
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint32_t)((uint64_t)N * (uint32_t)K / 2u));
-  const __amdgpu_buffer_rsrc_t rs = make_scale_rsrc(s, (uint32_t)N * (uint32_t)G);
-  const uint32_t rowb = (uint32_t)(K / 2);
-
-  // ---- X of the slice, pair order, and -136 * group sums, staged in LDS.
-  // Piece p = (m Gs + g) 16 + q holds x[m][128 (g0 + g) + 16 q .. + 8); the
-  // first kXB pieces of each thread are loaded before the weight ring is
-  // issued (they are needed first), all of a batch before any is processed.
-  uint8_t* xs = lds;                                     // [Gs][4][64] x 16 B
-  float* rsum = reinterpret_cast<float*>(lds + (size_t)Gs * 4096);   // [Gs][16]
-  const int npieces = 16 * Gs * 16;
-  constexpr int kXB = 16;                               // pieces per thread and batch
-  u32x4 xv[kXB];
-  auto load_x = [&](int base) {
-#pragma unroll
-    for (int i = 0; i < kXB; ++i) {
-      const int p = base + tid + NTHR * i;
-      const int m = p / (Gs * 16), rem = p - m * (Gs * 16);
-      xv[i] = ld128(rx, p < npieces && m < M
-                            ? (uint32_t)m * (uint32_t)K * 2u + (uint32_t)(g0 + (rem >> 4)) * 256u + 16u * (uint32_t)(rem & 15)
-                            : 0xFFFFFFF0u);
-    }
-  };
-  const uint32_t ones = vgpr_const(0x3F803F80u);
-  auto store_x = [&](int base) {
-#pragma unroll
-    for (int i = 0; i < kXB; ++i) {
-      const int p = base + tid + NTHR * i;
-      if (p >= npieces) break;     // uniform per wave (npieces % 64 == 0)
-      const int m = p / (Gs * 16), rem = p - m * (Gs * 16);
-      const int g = rem >> 4, q = rem & 15;          // piece q = 4 kb' + st of group g
-      const u32x4 v = xv[i];
-      u32x4 o;
-      o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-      o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-      o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-      o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-      *reinterpret_cast<u32x4*>(xs + (size_t)((g * 4 + (q & 3)) * 64 + m + 16 * (q >> 2)) * 16) = o;
-      float sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(ones), 0.0f, false);
-      sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(ones), sx, false);
-      sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), as_bf16x2(ones), sx, false);
-      sx = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), as_bf16x2(ones), sx, false);
-      // the 16 pieces of (m, g) are 16 consecutive p, one DPP row (NTHR % 16 == 0)
-      sx = row16_sum(sx);
-      if (q == 0) rsum[g * 16 + m] = -136.0f * sx;
-    }
-  };
-  load_x(0);
-
-  // ---- weight ring
-  u32x4 wbuf[D][NT][GB];
-  uint32_t sbuf[D][NT][GB];
-  auto issue = [&](u32x4 (&wb)[NT][GB], uint32_t (&sb)[NT][GB], int u) {
-    const bool live = u < U;
-    const int bi = live ? u / C : 0, c = live ? u - bi * C : 0;
-    const uint32_t r0 = (uint32_t)((b_lo + wq + bi * WAVES) * RB);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint32_t r = r0 + (uint32_t)(16 * t + n16);
-#pragma unroll
-      for (int j = 0; j < GB; ++j) {
-        const int g = c * GB + j;
-        const bool ok = live && g < Gs;
-        const uint32_t wo = ok ? r * rowb + (uint32_t)(g0 + g) * 64u + (uint32_t)kb * 16u : 0xFFFFFFF0u;
-        const uint32_t so = ok ? (r * (uint32_t)G + (uint32_t)(g0 + g)) * 2u : 0xFFFFFFF0u;
-        sb[t][j] = ld32(rs, so & ~3u);   // the aligned word holding the scale
-        wb[t][j] = __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 2);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-#pragma unroll
-  for (int u = 0; u < D; ++u) issue(wbuf[u], sbuf[u], u);
-
-
-  store_x(0);
-  for (int base = NTHR * kXB; base < npieces; base += NTHR * kXB) {
-    load_x(base);
-    store_x(base);
-  }
-  __syncthreads();
-
-  const uint32_t magic = vgpr_const(kMagicPair);
-  const uint32_t mask = __builtin_amdgcn_readfirstlane(vgpr_const(kNibblePairMask));
-  f32x4 acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto consume = [&](const u32x4 (&wb)[NT][GB], const uint32_t (&sb)[NT][GB], int u) {
-    const int bi = u / C, c = u - bi * C;
-    // the scale of row r, group g0 + 4 c + j sits in the high half of its word
-    // when r G + g0 + j is odd (the same for the NT tiles: they are 16 rows apart)
-    const uint32_t par = (uint32_t)(((b_lo + wq + bi * WAVES) * RB + n16) * G + g0) & 1u;
-#pragma unroll
-    for (int j = 0; j < GB; ++j) {
-      // groups past the slice: zero scale (their LDS reads are clamped in range)
-      const int g = min(c * GB + j, Gs - 1);
-      const f32x4 c0 = *reinterpret_cast<const f32x4*>(rsum + g * 16 + 4 * kb);
-      bf16x8 a[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        a[st] = *reinterpret_cast<const bf16x8*>(xs + (size_t)((g * 4 + st) * 64 + lane) * 16);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint32_t wd[4] = {wb[t][j].x, wb[t][j].y, wb[t][j].z, wb[t][j].w};
-        uint32_t w4[4], w8[4], w12[4];
-        shr64_pair<4>(wd[0], wd[1], w4[0], w4[1]);
-        shr64_pair<4>(wd[2], wd[3], w4[2], w4[3]);
-        shr64_pair<8>(wd[0], wd[1], w8[0], w8[1]);
-        shr64_pair<8>(wd[2], wd[3], w8[2], w8[3]);
-        shr64_pair<12>(wd[0], wd[1], w12[0], w12[1]);
-        shr64_pair<12>(wd[2], wd[3], w12[2], w12[3]);
-        f32x4 tt = c0;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{(wd[st] & mask) | magic, (w4[st] & mask) | magic,
-                                                            (w8[st] & mask) | magic, (w12[st] & mask) | magic});
-          tt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[st], b, tt, 0, 0, 0);
-        }
-        const float sc = __uint_as_float(((par ^ (uint32_t)(j & 1)) ? sb[t][j] : (sb[t][j] << 16)) & 0xFFFF0000u);
-        acc[t].x = fmaf(sc, tt.x, acc[t].x);
-        acc[t].y = fmaf(sc, tt.y, acc[t].y);
-        acc[t].z = fmaf(sc, tt.z, acc[t].z);
-        acc[t].w = fmaf(sc, tt.w, acc[t].w);
-      }
-    }
-    if (c == C - 1) {
-      // end of the row block: lane (n, kb) holds rows 4 kb + i of column n
-      const int r0 = (b_lo + wq + bi * WAVES) * RB;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int n = r0 + 16 * t + n16;
-        const float vals[4] = {acc[t].x, acc[t].y, acc[t].z, acc[t].w};
-        if (n < N) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = 4 * kb + i;
-            if (m < M) {
-              if (ws == nullptr) y[(size_t)m * N + n] = to_bf16(vals[i]);
-              else ws[((size_t)slice * M + m) * N + n] = vals[i];
-            }
-          }
-        }
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  };
-
-  for (int u0 = 0; u0 < U; u0 += D) {
-#pragma unroll
-    for (int k = 0; k < D; ++k) {
-      if (u0 + k < U) consume(wbuf[k], sbuf[k], u0 + k);
-      issue(wbuf[k], sbuf[k], u0 + k + D);
-    }
-  }
-}
-
-// LDS bytes of the streaming layout for a slice of gps groups
-static size_t skinny_stream_lds(int gps) { return (size_t)gps * 4096 + (size_t)gps * 64; }
-
-template <int NT, int D, int WAVES, int GB>
-static hipError_t launch_stream_t(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
-                                  int M, int N, int K, int gps, int sk, hipStream_t stream) {
-  const size_t lds = skinny_stream_lds(gps);
-  static std::atomic<uint64_t> lds_set{0};   // per instantiation and device
-  const hipError_t ea = ensure_dyn_lds(reinterpret_cast<const void*>(&skinny_stream_kernel<NT, D, WAVES, GB>),
-                                       (int)skinny_stream_lds(kSkinnyStreamMaxGroups), lds_set);
-  if (ea != hipSuccess) return ea;
-  // one workgroup per compute unit over the slices (at least one per slice)
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-  }
-  const int nblk = (N + 16 * NT - 1) / (16 * NT);
-  const int gx = std::max(1, std::min(nblk, cus / std::max(1, sk)));
-  hipLaunchKernelGGL((skinny_stream_kernel<NT, D, WAVES, GB>), dim3(gx, sk), dim3(64 * WAVES), lds, stream, x, w, s, y,
-                     ws, M, N, K, gps);
-  return hipGetLastError();
-}
-
-hipError_t launch_skinny_stream(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
-                                int M, int N, int K, int gps, int sk, int nt, int depth, int waves, int gb,
-                                hipStream_t stream) {
-  if (gps < 1 || gps > kSkinnyStreamMaxGroups) return hipErrorInvalidValue;
-#define W4A16_SKS(NTT, DD, WV, GBB)                                                              \
-  if (nt == NTT && depth == DD && waves == WV && gb == GBB)                                      \
-    return launch_stream_t<NTT, DD, WV, GBB>(x, w, s, y, ws, M, N, K, gps, sk, stream);
-  // (the instances that fit their register budget without spills)
-  W4A16_SKS(1, 2, 4, 4) W4A16_SKS(1, 3, 4, 4) W4A16_SKS(1, 2, 8, 4) W4A16_SKS(2, 2, 8, 4)
-  W4A16_SKS(1, 2, 4, 8) W4A16_SKS(1, 2, 8, 8) W4A16_SKS(1, 2, 4, 16) W4A16_SKS(1, 1, 8, 16)
-  W4A16_SKS(1, 3, 4, 16)
-#undef W4A16_SKS
-  return hipErrorInvalidValue;
-}
-
 template <int NT, int WV, int XR, int MT = 1>
 static hipError_t launch_skinny_t(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                                   int M, int N, int K, int gps, int sk, hipStream_t stream) {
@@ -598,12 +336,8 @@ hipError_t launch_skinny(const uint16_t* x, const uint8_t* w, const uint16_t* s,
     }                                                                                                   \
     return hipErrorInvalidValue;                                                                        \
   }
-  W4A16_SKINNY(1, 4)
-  W4A16_SKINNY(2, 4)
-  W4A16_SKINNY(4, 4)
   W4A16_SKINNY(1, 8)
   W4A16_SKINNY(2, 8)
-  W4A16_SKINNY(4, 8)
 #undef W4A16_SKINNY
   return hipErrorInvalidValue;
 }

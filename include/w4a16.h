@@ -80,30 +80,36 @@ w4a16_status w4a16_pack_int4(const uint8_t* q, uint8_t* w_packed,
                              int64_t rows, int64_t K, void* stream);
 
 /*
- * The split-K factor the library uses for w4a16_gemm with group_size 128
- * when split_k == 0 (auto) at this shape: for the M = 1 GEMV only what its register budget for
- * x needs (at most 64 groups per slice), for the M <= 48 kernel slices
- * only while fewer than half of the compute units have a workgroup, and
- * for the tile kernel the power of
- * two (at most 16) of least estimated time among those that keep tiles x SK
- * within one workgroup per compute unit, counting the fp32 partials and the
- * reduce, chosen together with the tile height (so, unlike the MI350X Triton
- * page's prune of split-K at M >= 512, a tall-K shape with few tiles splits
- * at any M). Returns 0 on invalid dimensions.
+ * The split-K factor w4a16_gemm uses at this shape and group size when
+ * split_k == 0 (auto): for the M = 1 GEMV only what its register budget for x
+ * needs (at most 64 groups per slice), for the M <= 48 kernel slices only
+ * while fewer than half of the compute units have a workgroup, and for the
+ * tile kernel the power of two (at most 16) of least estimated time among
+ * those that keep tiles x SK within one workgroup per compute unit, counting
+ * the fp32 partials and the reduce, chosen together with the tile height
+ * (so, unlike the MI350X Triton page's prune of split-K at M >= 512, a
+ * tall-K shape with few tiles splits at any M). Returns 0 on invalid
+ * arguments.
  */
-int32_t w4a16_gemm_auto_split_k(int64_t M, int64_t N, int64_t K);
+int32_t w4a16_gemm_auto_split_k(int64_t M, int64_t N, int64_t K, int32_t group_size);
 
 /*
- * Bytes of workspace w4a16_gemm needs at this shape and split_k (0 = auto)
- * with group_size 128: SK * M * N * 4 (rounded up to 256) when the effective
- * split factor SK > 1, plus, on the tile kernel (M > 16 where the small-
- * batch kernel does not take the shape), (K/128) *
- * round_up(M, 4) * 4 for the per-row group sums of X. Returns 0 when none is
- * needed and for invalid arguments. w4a16_gemm_workspace_bytes_gs gives it
- * for either group size.
+ * Bytes of workspace w4a16_gemm uses at this shape and split_k (0 = auto)
+ * with group_size 128 (w4a16_gemm_workspace_bytes_gs: either group size):
+ *  - SK * M * N * 4, rounded up to 256, for the split-K partials when the
+ *    effective split factor SK is above 1 (required);
+ *  - plus, on the tile kernel (M > 48, or group size 32 at any M) with a wide
+ *    N (at least 32 column tiles of 256 at group 128, 8 at group 32),
+ *    (K/group_size) * round_up(M, 4) * 4 for the -136 * row sums of X from a
+ *    pre-pass kernel (optional: with less room, or a NULL workspace at SK 1,
+ *    the tile kernel forms the row sums itself, which costs more time once
+ *    many column tiles repeat them).
+ * Returns 0 when no workspace is used and for invalid arguments.
  */
 size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K,
                                   int32_t split_k);
+size_t w4a16_gemm_workspace_bytes_gs(int64_t M, int64_t N, int64_t K,
+                                     int32_t group_size, int32_t split_k);
 
 /*
  * Y = X . dequant(W)^T.
@@ -115,19 +121,26 @@ size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K,
  *               the fp32 accumulator)
  *   M >= 0 (M == 0: returns W4A16_OK, nothing enqueued), N >= 1, K >= 128.
  *   group_size: 128, or 32; K % 128 == 0 either way. Group size 32 always
- *               runs the tile kernel (path 3, configurations 2 to 5), at any
- *               M: the M = 1 and M <= 48 kernels take 128-groups only.
+ *               runs the tile kernel, at any M: the M = 1 and M <= 48 kernels
+ *               take 128-groups only.
  *   split_k   : 0 = auto, or 1, 2, 4, 8, 16. With SK > 1 the K range is cut
  *               into SK contiguous slices of ceil((K/128)/SK) blocks of 128 k
- *               (trailing slices may be empty); slice s writes its fp32 partial sums to
- *               workspace[s, :, :] with plain stores (an empty slice writes
- *               zeros) and a second kernel sums the slices in order
- *               s = 0..SK-1 in fp32 and rounds once to bf16.
- *   workspace : fp32 device scratch, overwritten; may be NULL when
- *               w4a16_gemm_workspace_bytes_gs is 0. With SK > 1 its first
- *               SK * M * N floats hold the [SK, M, N] partials after the call.
- *   workspace_bytes: its size in bytes (>= w4a16_gemm_workspace_bytes_gs for
- *               this group_size).
+ *               (trailing slices may be empty); slice s writes its fp32
+ *               partial sums to workspace[s, :, :] with plain stores (an
+ *               empty slice writes zeros) and a second kernel sums the slices
+ *               in order s = 0..SK-1 in fp32 and rounds once to bf16
+ *               ("Add Triton BF16xINT4 rowwise GEMM for ROCm gfx942/gfx950",
+ *               Implementation "Split-K without atomics").
+ *   workspace : fp32 device scratch, overwritten, or NULL. Required when the
+ *               effective SK is above 1: its first SK * M * N floats then hold
+ *               the [SK, M, N] partials after the call. Where
+ *               w4a16_gemm_workspace_bytes_gs also counts row sums and the
+ *               workspace has that room, a pre-pass kernel writes the
+ *               -136 * row sums of X after the partials (256-byte aligned)
+ *               and the tile kernel reads them; otherwise the tile kernel
+ *               forms them itself (same results).
+ *   workspace_bytes: its size in bytes (with SK > 1 at least the rounded
+ *               partials, else W4A16_ERR_WORKSPACE).
  * Rows of Y are written exactly once; no atomics are used, so the result is
  * bitwise reproducible for a given shape and split_k.
  */
@@ -138,15 +151,9 @@ w4a16_status w4a16_gemm(const uint16_t* x, const uint8_t* w_packed,
                         size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of workspace w4a16_gemm_grouped needs with group_size 128: (K/128) *
- * round_up(M_total, 4) * 4 (one fp32 row sum per row and 128-group). Returns
- * 0 for invalid arguments or M_total == 0. w4a16_gemm_grouped_workspace_bytes_gs
- * gives it for either group size.
- */
-size_t w4a16_gemm_grouped_workspace_bytes(int32_t G, int64_t M_total, int64_t N, int64_t K);
-
-/*
- * Grouped GEMM in one launch: for each group g with
+ * Grouped GEMM in one launch ("Add Triton BF16xINT4 rowwise GEMM for ROCm
+ * gfx942/gfx950", Implementation "Native fused grouped kernel"): for each
+ * group g with
  *   start_g = sum_{h<g} m_sizes[h]   (computed on the device),
  * rows [start_g, start_g + m_sizes[g]) of Y are those rows of X times
  * dequant(W_g)^T.
@@ -162,31 +169,29 @@ size_t w4a16_gemm_grouped_workspace_bytes(int32_t G, int64_t M_total, int64_t N,
  *               m_sizes[g] == 0 contributes nothing.
  *   y         : [M_total, N] bf16, device, written
  *   G >= 1, M_total >= 0 (0: W4A16_OK, nothing enqueued), N >= 1, K >= 128,
- *   group_size 128 or 32 (tile configurations 2 to 5), K % 128 == 0; the
- *   scales of all groups together must be smaller than 2^32 bytes.
- *   workspace : fp32 device scratch of workspace_bytes >= the value of
- *               w4a16_gemm_grouped_workspace_bytes_gs; overwritten.
- * Two kernels are enqueued: a pass over X computing per-row group sums, and
- * the grouped tile kernel. The tile grid is sized from the host value
- * M_total: (ceil(M_total/BM) + G) * ceil(N/BN) workgroups; workgroups past
- * the last tile of the last group exit at once.
+ *   group_size 128 or 32, K % 128 == 0; the scales of all groups together
+ *   must be smaller than 2^32 bytes.
+ * One kernel is enqueued; it needs no workspace. Its grid is sized from the
+ * host value M_total: (ceil(M_total/BM) + G) * ceil(N/256) workgroups for a
+ * tile height BM chosen on the host; each workgroup counts the real tiles
+ * from m_sizes on the device, and those past the last one exit at once.
  */
 w4a16_status w4a16_gemm_grouped(const uint16_t* x, const uint8_t* w_packed,
                                 const uint16_t* scales, const int32_t* m_sizes,
                                 uint16_t* y, int32_t G, int64_t M_total,
                                 int64_t N, int64_t K, int32_t group_size,
-                                float* workspace, size_t workspace_bytes,
                                 void* stream);
 
 /*
- * Bytes of workspace w4a16_gemm_batched needs at this shape and split_k (0 =
- * auto) with group_size 128: SK * B * M * N * 4 (rounded up to 256) when the
- * effective split factor SK > 1, plus (K/128) * round_up(B * M, 4) * 4 for
- * the per-row group sums of X. Returns 0 for invalid arguments or M == 0.
- * w4a16_gemm_batched_workspace_bytes_gs gives it for either group size.
+ * Bytes of workspace w4a16_gemm_batched uses at this shape, group size and
+ * split_k (0 = auto): SK * B * M * N * 4, rounded up to 256, when the
+ * effective split factor SK is above 1 (required), plus the optional
+ * pre-pass row sums (K/group_size) * round_up(B * M, 4) * 4 for a wide N, as
+ * for w4a16_gemm. Returns 0 when none is used, for invalid arguments or
+ * M == 0.
  */
 size_t w4a16_gemm_batched_workspace_bytes(int32_t B, int64_t M, int64_t N, int64_t K,
-                                          int32_t split_k);
+                                          int32_t group_size, int32_t split_k);
 
 /*
  * Batched GEMM ("Add Triton BF16xINT4 rowwise GEMM for ROCm gfx942/gfx950",
@@ -198,18 +203,17 @@ size_t w4a16_gemm_batched_workspace_bytes(int32_t B, int64_t M, int64_t N, int64
  *   scales    : [B, N, K/group_size] bf16, device
  *   y         : [B, M, N] bf16, device, written
  *   B >= 1, M >= 0 (0: W4A16_OK, nothing enqueued), B * M < 2^31, N >= 1,
- *   K >= 128, group_size 128 or 32 (tile configurations 2 to 5), K % 128 ==
- *   0; the scales of all B problems together must be smaller than 2^32
- *   bytes.
+ *   K >= 128, group_size 128 or 32, K % 128 == 0; the scales of all B
+ *   problems together must be smaller than 2^32 bytes.
  *   split_k   : 0 (auto: the tile height and split chosen together, as for
  *               w4a16_gemm with B x ceil(M/h) row tiles per column) or 1, 2,
  *               4, 8, 16.
- *   workspace : fp32 device scratch of workspace_bytes >= the value of
- *               w4a16_gemm_batched_workspace_bytes_gs; overwritten.
- * Enqueues the per-row group sums of X, the tile kernel (weight group b =
- * problem b, its rows at b * M), and for SK > 1 the split-K reduce. Every
- * row of Y is written exactly once, no atomics: bitwise reproducible for a
- * given shape and split_k.
+ *   workspace : fp32 device scratch, overwritten, or NULL when SK is 1
+ *               (same layout and rules as for w4a16_gemm).
+ * Enqueues the tile kernel (weight group b = problem b, its rows at b * M),
+ * preceded by the row-sum pre-pass where the workspace has room for it (as
+ * for w4a16_gemm), and, for SK > 1, the split-K reduce. Every row of Y is written exactly
+ * once, no atomics: bitwise reproducible for a given shape and split_k.
  */
 w4a16_status w4a16_gemm_batched(const uint16_t* x, const uint8_t* w_packed,
                                 const uint16_t* scales, uint16_t* y,
@@ -230,111 +234,6 @@ w4a16_status w4a16_gemm_batched(const uint16_t* x, const uint8_t* w_packed,
 w4a16_status w4a16_splitk_reduce(const float* workspace, uint16_t* y,
                                  int32_t split_k, int64_t M, int64_t N,
                                  void* stream);
-
-/*
- * Explicit kernel selection, for tests and benchmarks that must exercise a
- * particular kernel at a shape where the automatic choice would pick another.
- * The result of a forced path still satisfies the same contract.
- *   path   : 0 = automatic, 1 = M == 1 GEMV (at most 64 groups per split-K
- *            slice),
- *            2 = M <= 48 MFMA 16x16x32 small-batch kernel (one row tile of
- *            16, two past 16 rows, three past 32; automatic for M <= 16,
- *            for M <= 32 while ceil(N/32) <= 3 x compute units, for M <= 48
- *            while ceil(N/16) <= compute units), 3 = MFMA tile kernel
- *            (LDS-staged; the only path of the grouped call)
- *   variant: -1 = default for the path; otherwise
- *            path 1: 1000 * layout + layout digits.
- *              layout 2 (default, MFMA diagonal contraction of 16 groups per
- *              instruction): 2000 + 100 * h + 10 * depth + blocks, with
- *              h = 4 * x_staged_in_lds + (waves_per_workgroup / 4 - 1)
- *              (waves 4, 8, 12, 16; x held in registers otherwise),
- *              depth 1..3 = weight blocks in flight per wave, blocks 1..9 =
- *              row blocks per wave (sets the grid), 0 = one workgroup per
- *              compute unit. Combinations that would not fit the register
- *              budget of their occupancy are not built (W4A16_ERR_LAUNCH).
- *              Slice lengths with no MFMA geometry run layout 1 variant 124.
- *              layout 0 (1 KiB weight runs per wave) and layout 1 (one row
- *              per half-wave, x in registers): 100 * nt + 10 * depth + rows,
- *              nt 1 = non-temporal weight loads, depth 1..3 (layout 0) or
- *              1..4 (layout 1) = loads in flight, rows 1..9 = rows or row
- *              blocks per wave;
- *            path 2: 10 * waves_per_workgroup +
- *            column_tiles_per_wave (41, 42, 44, 81, 82, 84; default 81 for
- *            M <= 8, 82 above): waves
- *            take a column block's groups in turn; or the streaming layout
- *            1000 * u + 100 * row_tiles + 10 * units_in_flight + waves / 4,
- *            units of 4 << (u - 1) groups (one workgroup per compute unit,
- *            X of the slice staged in LDS, each wave streaming blocks of
- *            16 * row_tiles weight rows): 1121, 1131, 1122, 1222, 2121,
- *            2122, 3121, 3112, 3131; with more than 32 groups per slice it
- *            runs the default of the first form; path 3: tile
- *            configuration index (0: 128x256 and 1: 128x128 with weights
- *            dequantised into LDS; 2: 128x256 with LDS-DMA staging, 8
- *            waves, 3 LDS stages; 3, 4, 5, 6, 7, 8: the same with 96x256,
- *            112x256, 80x256, 144x256, 64x256 and 48x256 tiles; group_size
- *            32 runs on 2 to 5 only, W4A16_ERR_GROUP_SIZE otherwise). By
- *            default the call picks among 2 to 8 (2 to 5 for group_size 32)
- *            the tile height and split with the least estimated time: the
- *            rounds of one workgroup per compute unit times rows per tile, weighted by
- *            each height's measured per-row rate (the grouped call
- *            estimates ceil(M_total/h) + G/2 row tiles per column).
- * An unavailable combination (e.g. path 1 with M != 1, path 2 with M > 48,
- * with M > 16 and a variant other than 81 or 82, or with M > 32 and a
- * variant other than 81)
- * returns W4A16_ERR_SHAPE; path 1 or 2 with group_size 32 returns
- * W4A16_ERR_GROUP_SIZE.
- */
-typedef struct {
-  int32_t path;
-  int32_t variant;
-} w4a16_config;
-
-/* w4a16_gemm_workspace_bytes for the kernel selected by cfg (NULL = auto). */
-size_t w4a16_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K,
-                                     int32_t split_k, const w4a16_config* cfg);
-
-/* w4a16_gemm with an explicit kernel selection (cfg NULL = automatic). */
-w4a16_status w4a16_gemm_ex(const uint16_t* x, const uint8_t* w_packed,
-                           const uint16_t* scales, uint16_t* y,
-                           int64_t M, int64_t N, int64_t K, int32_t group_size,
-                           int32_t split_k, float* workspace,
-                           size_t workspace_bytes, void* stream,
-                           const w4a16_config* cfg);
-
-/* w4a16_gemm_grouped with an explicit tile configuration (path must be 0 or 3). */
-w4a16_status w4a16_gemm_grouped_ex(const uint16_t* x, const uint8_t* w_packed,
-                                   const uint16_t* scales, const int32_t* m_sizes,
-                                   uint16_t* y, int32_t G, int64_t M_total,
-                                   int64_t N, int64_t K, int32_t group_size,
-                                   float* workspace, size_t workspace_bytes,
-                                   void* stream, const w4a16_config* cfg);
-
-/* w4a16_gemm_batched_workspace_bytes for an explicit tile configuration. */
-size_t w4a16_gemm_batched_workspace_bytes_ex(int32_t B, int64_t M, int64_t N, int64_t K,
-                                             int32_t split_k, const w4a16_config* cfg);
-
-/*
- * Workspace bytes for either group size (128 or 32; the functions above are
- * these with 128). With group_size 32 the tile kernel runs at every M and its
- * row sums take (K/32) * round_up(rows, 4) * 4 bytes. cfg NULL = automatic.
- * Return 0 for invalid arguments (including a group size the selected kernel
- * does not take) and when no workspace is needed.
- */
-size_t w4a16_gemm_workspace_bytes_gs(int64_t M, int64_t N, int64_t K, int32_t group_size,
-                                     int32_t split_k, const w4a16_config* cfg);
-size_t w4a16_gemm_grouped_workspace_bytes_gs(int32_t G, int64_t M_total, int64_t N, int64_t K,
-                                             int32_t group_size);
-size_t w4a16_gemm_batched_workspace_bytes_gs(int32_t B, int64_t M, int64_t N, int64_t K,
-                                             int32_t group_size, int32_t split_k,
-                                             const w4a16_config* cfg);
-
-/* w4a16_gemm_batched with an explicit tile configuration (path must be 0 or 3). */
-w4a16_status w4a16_gemm_batched_ex(const uint16_t* x, const uint8_t* w_packed,
-                                   const uint16_t* scales, uint16_t* y,
-                                   int32_t B, int64_t M, int64_t N, int64_t K,
-                                   int32_t group_size, int32_t split_k,
-                                   float* workspace, size_t workspace_bytes,
-                                   void* stream, const w4a16_config* cfg);
 
 #ifdef __cplusplus
 }

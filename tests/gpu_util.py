@@ -47,3 +47,22 @@ def check_gate(y_bits: np.ndarray, y_ref: np.ndarray, what: str):
     g = oracle.gate(y_bits, y_ref)
     assert g["ok"], f"{what}: {g}"
     return g
+
+
+BF16_NAN = 0x7FC0
+
+
+def nan_filled(shape) -> torch.Tensor:
+    """A bf16 device tensor filled with NaN: outputs that a kernel never
+    writes stay NaN, which the gate's finiteness check then catches."""
+    return torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev())
+
+
+def check_full(y: torch.Tensor, y_ref: np.ndarray, what: str):
+    """Every output element written (finite) and the whole output against the
+    oracle's."""
+    torch.cuda.synchronize()
+    yb = bits_host(y).reshape(y_ref.shape)
+    unwritten = int(np.count_nonzero((yb & 0x7FFF) > 0x7F80))
+    assert unwritten == 0, f"{what}: {unwritten} outputs left NaN (never written)"
+    return check_gate(yb, y_ref, what)

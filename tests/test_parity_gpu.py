@@ -13,7 +13,7 @@ import torch
 import bf16_activation_quantized_amd as w4
 import oracle
 from synth import make_config, make_inputs, make_workspace
-from gpu_util import DevCase, bf16_dev, bits_host, check_gate, u8_dev
+from gpu_util import DevCase, bf16_dev, bits_host, check_full, check_gate, nan_filled, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -45,22 +45,18 @@ def test_pack_bit_exact(rows, K):
 # ------------------------------------------------------------------ decode GEMV (M = 1)
 
 GEMV_CASES = [
-    # N, K, split_k, variant (1000 * layout [0 flat, 1 half-wave, 2 MFMA] + layout digits;
-    #   flat / half-wave: 100 * non-temporal + 10 * prefetch depth + row blocks (rows) per wave)
-    # None = the default (MFMA 2110 where the slice length has an MFMA geometry,
-    # otherwise half-wave 124)
+    # N, K, split_k, variant (None = the MFMA layout where the slice length has
+    # a tiling of 16 (row, group) pairs per instruction, else the half-wave
+    # layout; 1 = the half-wave layout forced)
     (256, 512, 0, None),      # the tiny workload (MFMA, 4-row blocks)
     (17408, 5120, 1, None),   # the decode workload (MFMA, 2-row blocks)
-    (1001, 5120, 1, 131),     # odd N: last 2-row block half outside
-    (999, 8192, 1, 22),       # flat, 1-row blocks, 4 runs of 1 KiB
-    (777, 4096, 1, 113),      # flat, 1-row blocks, 2 runs
-    (1003, 2560, 1, 24),      # flat, 4-row blocks, 5 runs
-    (1002, 1024, 1, 21),      # flat, 2-row blocks, 1 run
-    (1000, 1280, 1, 1011),    # half-wave layout (flat does not fit 40 chunks/row)
-    (1000, 1280, 1, 1022),
-    (1001, 1280, 1, 1134),
-    (999, 640, 1, 1149),
-    (1003, 5120, 1, 1037),    # half-wave layout forced
+    (1001, 5120, 1, None),    # odd N: last 2-row block half outside
+    (1003, 2560, 1, None),    # 4-row blocks, 5 instructions
+    (1002, 1024, 1, None),    # 2-row blocks, 1 instruction
+    (999, 8192, 1, None),     # 1-row blocks, 4 instructions
+    (777, 4096, 1, None),     # 1-row blocks, 2 instructions
+    (1000, 1280, 1, None),    # 10 groups: 8-row blocks, no MFMA tiling -> half-wave
+    (999, 640, 1, None),      # 5 groups: half-wave
     (37, 128, 1, None),
     (513, 2560, 2, None),
     (300, 9216, 0, None),     # 72 groups: auto split so that a slice holds <= 64
@@ -68,38 +64,20 @@ GEMV_CASES = [
     (64, 384, 4, None),       # 3 groups over 4 slices
     (1, 8192, 1, None),       # single row, 64 groups in one slice
     (3, 5120, 1, None),       # fewer rows than one wave's blocks
-    (40, 10240, 2, 24),       # flat with split-K: 40 groups per slice
+    (5, 5120, 1, None),
+    (256, 512, 1, None),      # fewer blocks than one workgroup per compute unit can take
     (41, 7680, 2, None),      # 30 groups per slice -> half-wave fallback
-    # MFMA layout: 2000 + 100 * (4 * x-in-LDS + waves / 4 - 1) + 10 * depth
-    #              + row blocks per wave (0: one workgroup per compute unit)
-    (17408, 5120, 1, 2024),   # 2-row blocks, 5 instructions, x in registers
-    (17408, 5120, 1, 2514),   # x in LDS, 8 waves
-    (17408, 5120, 1, 2610),   # x in LDS, 12 waves, one workgroup per CU
-    (17408, 5120, 1, 2620),
-    (17408, 5120, 1, 2710),   # 16 waves
-    (17408, 5120, 1, 2110),   # 8 waves, x in registers, one workgroup per CU
-    (17408, 5120, 1, 2120),
-    (1001, 5120, 1, 2115),
-    (1003, 2560, 1, 2110),    # 4-row blocks, 5 instructions
-    (1002, 1024, 1, 2210),    # 12 waves, x in registers (2-row blocks, 1 instruction)
-    (1001, 5120, 1, 2413),
-    (999, 8192, 1, 2022),     # 1-row blocks, 4 instructions
-    (777, 4096, 1, 2431),     # 1-row blocks, 2 instructions, depth 3
-    (1003, 2560, 1, 2424),    # 4-row blocks, 5 instructions
-    (1002, 1024, 1, 2012),    # 2-row blocks, 1 instruction
-    (1002, 1024, 1, 2610),
-    (256, 512, 1, 2421),      # 4-row blocks, 1 instruction (the tiny shape)
-    (256, 512, 1, 2610),      # fewer blocks than one workgroup per CU can take
-    (40, 10240, 2, 2524),     # with split-K
-    (40, 10240, 2, 2610),
-    (5, 5120, 1, 2011),       # fewer rows than one block per wave
-    (5, 5120, 1, 2710),
-    (33, 8192, 4, 2620),      # split-K, 16 groups per slice, 1-row blocks
-    (1001, 896, 2, 2410),     # N * G odd: the last scale is the low half of a word
-    (1001, 896, 2, 2110),     #   that ends past the tensor (4 + 3 groups per slice)
-    (1000, 640, 1, 2213),     # 5 groups per slice: no MFMA geometry -> half-wave 124
-    (17408, 5120, 1, 122),    # flat layout at the decode shape
-    (17408, 5120, 1, 1124),   # half-wave layout at the decode shape
+    (33, 8192, 4, None),      # split-K, 16 groups per slice, 1-row blocks
+    (1001, 896, 2, None),     # N * G odd: the last scale is the low half of a word
+                              #   that ends past the tensor (4 + 3 groups per slice)
+    (40, 10240, 2, None),     # with split-K: 40 groups per slice
+    # the half-wave layout forced
+    (17408, 5120, 1, 1),
+    (1000, 1280, 1, 1),
+    (1001, 1280, 1, 1),
+    (1003, 5120, 1, 1),
+    (999, 640, 2, 1),
+    (40, 10240, 2, 1),
 ]
 
 
@@ -115,51 +93,42 @@ def test_gemv_parity(N, K, sk, variant):
 # ------------------------------------------------------------------ skinny MFMA (M <= 16)
 
 SKINNY_CASES = [
-    # M, N, K, split_k, variant (10 * waves + column tiles per wave; or streaming)
-    (1, 256, 512, 1, 44),
-    (2, 1000, 1024, 1, 44),
-    (3, 17, 384, 1, 41),
-    (5, 64, 128, 1, 42),
-    (15, 1000, 1024, 2, 84),
-    (16, 513, 2048, 4, 81),
-    (16, 256, 1024, 8, 82),
-    (16, 100, 384, 16, 44),   # more slices than groups
-    (7, 300, 640, 1, 82),
+    # M, N, K, split_k, column tiles of 16 per wave (None = 1 up to 8 rows and
+    # past 32, 2 between)
+    (1, 256, 512, 1, 1),
+    (2, 1000, 1024, 1, 2),
+    (3, 17, 384, 1, 1),
+    (5, 64, 128, 1, 2),
+    (15, 1000, 1024, 2, 2),
+    (16, 513, 2048, 4, 1),
+    (16, 256, 1024, 8, 2),
+    (16, 100, 384, 16, 1),    # more slices than groups
+    (7, 300, 640, 1, 2),
     (16, 8192, 1024, 0, None),
     # X row quads loaded per group follow M (1: M <= 4, 2: <= 8, 3: <= 12, 4)
-    (4, 300, 640, 1, 82),
-    (8, 300, 640, 2, 82),
-    (9, 513, 1024, 1, 82),
-    (12, 300, 640, 1, 41),
-    (13, 257, 384, 1, 84),
-    (4, 100, 40960, 1, 82),       # a slice too long to stage its scales in LDS (320 groups)
-    # two row tiles of 16 (17 <= M <= 32; 6 or 8 row quads), 8 waves of 1 or 2 column tiles
-    (17, 300, 640, 1, 82),
-    (20, 257, 1024, 2, 81),
-    (24, 513, 2048, 4, 82),
-    (25, 100, 384, 16, 82),       # more slices than groups
-    (31, 1000, 1024, 1, 81),
-    (32, 8192, 1024, 0, 82),
-    (32, 300, 40960, 1, 82),      # a slice too long to stage its scales in LDS
-    # three row tiles (33 <= M <= 48; 10 or 12 row quads), 8 waves of 1 column tile
-    (33, 300, 640, 1, 81),
-    (40, 257, 1024, 2, 81),
-    (41, 513, 2048, 4, 81),
-    (48, 100, 384, 16, 81),       # more slices than groups
+    (4, 300, 640, 1, 2),
+    (8, 300, 640, 2, 2),
+    (9, 513, 1024, 1, 2),
+    (12, 300, 640, 1, 1),
+    (13, 257, 384, 1, 2),
+    (4, 100, 40960, 1, 2),        # a slice too long to stage its scales in LDS (320 groups)
+    # two row tiles of 16 (17 <= M <= 32; 6 or 8 row quads)
+    (17, 300, 640, 1, 2),
+    (20, 257, 1024, 2, 1),
+    (24, 513, 2048, 4, 2),
+    (25, 100, 384, 16, 2),        # more slices than groups
+    (31, 1000, 1024, 1, 1),
+    (32, 8192, 1024, 0, 2),
+    (32, 300, 40960, 1, 2),       # a slice too long to stage its scales in LDS
+    # three row tiles (33 <= M <= 48; 10 or 12 row quads), one column tile per wave
+    (33, 300, 640, 1, 1),
+    (40, 257, 1024, 2, 1),
+    (41, 513, 2048, 4, 1),
+    (48, 100, 384, 16, 1),        # more slices than groups
     (48, 1000, 1024, 0, None),    # forced path, default variant and split
-    (47, 300, 40960, 1, 81),      # a slice too long to stage its scales in LDS
-    # streaming layout: 1000 + 100 * row tiles + 10 * units in flight + waves / 4
-    (1, 256, 512, 1, 1131),
-    (3, 17, 384, 1, 1121),        # fewer rows than one 16-row block
-    (5, 100, 640, 1, 3131),       # ragged unit (5 groups in a 16-group unit)
-    (15, 1000, 1024, 2, 2121),
-    (16, 513, 2048, 4, 2122),
-    (16, 1000, 4096, 1, 3112),    # 32 groups in one slice (the LDS maximum)
-    (16, 777, 1280, 4, 1222),     # uneven slices (3, 3, 3, 1 groups)
-    (16, 100, 384, 16, 1131),     # more slices than groups (empty slices write zeros)
-    (16, 512, 8192, 1, 1131),     # slice too long for LDS: group-striped fallback
+    (47, 300, 40960, 1, 1),       # a slice too long to stage its scales in LDS
     (16, 8192, 8192, 0, None),    # small-batch decode workload, default split
-    (9, 2048, 8192, 2, 1122),
+    (9, 2048, 8192, 2, 2),
 ]
 
 
@@ -174,68 +143,64 @@ def test_skinny_parity(M, N, K, sk, variant):
 # ------------------------------------------------------------------ tile MFMA (prefill)
 
 TILE_CASES = [
-    # M, N, K, split_k, tile config
-    (17, 100, 128, 1, 0),
-    (130, 256, 256, 1, 0),
-    (300, 1000, 640, 1, 1),
-    (129, 513, 384, 2, 0),
-    (64, 64, 1024, 4, 1),
-    (257, 300, 256, 8, 1),    # more slices than groups
-    (1, 256, 256, 1, 0),      # one row through the tile kernel (M tail)
-    (255, 129, 512, 0, 0),
-    (600, 700, 1280, 0, 1),
-    # LDS-DMA kernel, 8 waves, 3 stages: 2 = 128 x 256 tiles, 3 = 96 x 256 tiles
-    (17, 100, 128, 1, 2),     # one group: no second stage in flight; M and N tails
-    (130, 256, 256, 1, 2),    # two groups
-    (300, 1000, 640, 1, 2),   # steady state, N tail of 232 columns
-    (129, 513, 384, 2, 2),    # split-K slices of 2 and 1 groups
-    (257, 300, 256, 8, 2),    # more slices than groups: empty slices write zeros
-    (1, 256, 256, 1, 2),
-    (255, 129, 512, 0, 2),
-    (1322, 512, 2560, 1, 2),  # the prefill row count and depth
-    (64, 64, 1024, 4, 2),
-    (600, 700, 1280, 0, 2),
-    (77, 257, 640, 1, 2),
-    (129, 511, 384, 1, 2),    # N * G odd, no split
-    (17, 100, 128, 1, 3),
-    (97, 256, 256, 1, 3),     # one row past a 96-row tile
-    (300, 1000, 640, 1, 3),
-    (129, 513, 384, 2, 3),
-    (257, 300, 256, 8, 3),
-    (1322, 512, 2560, 1, 3),
-    (95, 129, 512, 0, 3),
-    # 4 = 112 x 256 tiles (7 row tiles: the X stage is 28 DMA blocks over 8 waves)
-    (17, 100, 128, 1, 4),
-    (113, 256, 256, 1, 4),    # one row past a 112-row tile
-    (300, 1000, 640, 1, 4),
-    (129, 513, 384, 2, 4),
-    (257, 300, 256, 8, 4),
-    (1322, 512, 2560, 1, 4),
-    (111, 129, 512, 0, 4),
-    (224, 257, 384, 1, 4),    # exactly two tiles; N * G odd
-    # 6 = 144 x 256 tiles (36 X DMA blocks over 8 waves, 3 x 52.6 KiB stages)
-    (17, 100, 128, 1, 6),
-    (145, 256, 256, 1, 6),    # one row past a 144-row tile
-    (300, 1000, 640, 1, 6),
-    (129, 513, 384, 2, 6),
-    (257, 300, 256, 8, 6),
-    (1322, 512, 2560, 1, 6),
-    (143, 129, 512, 0, 6),
-    # 7 = 64 x 256 and 8 = 48 x 256 tiles (16 and 12 X DMA blocks over 8 waves)
-    (17, 100, 128, 1, 7),
-    (65, 256, 256, 1, 7),     # one row past a 64-row tile
-    (300, 1000, 640, 2, 7),
-    (1322, 512, 2560, 1, 7),
-    (17, 100, 128, 1, 8),
-    (49, 256, 256, 1, 8),     # one row past a 48-row tile
-    (300, 1000, 640, 8, 8),
-    (47, 129, 512, 0, 8),
-    # 5 = 80 x 256 tiles (20 X DMA blocks over 8 waves)
-    (17, 100, 128, 1, 5),
-    (81, 256, 256, 1, 5),
-    (300, 1000, 640, 1, 5),
-    (257, 300, 256, 8, 5),
-    (1322, 512, 2560, 1, 5),
+    # M, N, K, split_k, rows per tile (LDS-DMA kernel, 8 waves, 3 stages)
+    (17, 100, 128, 1, 128),   # one group: no second stage in flight; M and N tails
+    (130, 256, 256, 1, 128),  # two groups
+    (300, 1000, 640, 1, 128), # steady state, N tail of 232 columns
+    (129, 513, 384, 2, 128),  # split-K slices of 2 and 1 groups
+    (257, 300, 256, 8, 128),  # more slices than groups: empty slices write zeros
+    (1, 256, 256, 1, 128),
+    (255, 129, 512, 0, 128),
+    (1322, 512, 2560, 1, 128),  # the prefill row count and depth
+    (64, 64, 1024, 4, 128),
+    (600, 700, 1280, 0, 128),
+    (77, 257, 640, 1, 128),
+    (129, 511, 384, 1, 128),  # N * G odd, no split
+    (17, 100, 128, 1, 96),
+    (97, 256, 256, 1, 96),    # one row past a 96-row tile
+    (300, 1000, 640, 1, 96),
+    (129, 513, 384, 2, 96),
+    (257, 300, 256, 8, 96),
+    (1322, 512, 2560, 1, 96),
+    (95, 129, 512, 0, 96),
+    # 112-row tiles (7 row tiles: the X stage is 28 DMA blocks over 8 waves)
+    (17, 100, 128, 1, 112),
+    (113, 256, 256, 1, 112),  # one row past a 112-row tile
+    (300, 1000, 640, 1, 112),
+    (129, 513, 384, 2, 112),
+    (257, 300, 256, 8, 112),
+    (1322, 512, 2560, 1, 112),
+    (111, 129, 512, 0, 112),
+    (224, 257, 384, 1, 112),  # exactly two tiles; N * G odd
+    # 144-row tiles (36 X DMA blocks over 8 waves, 3 x 52.6 KiB stages; the
+    # ninth row tile's sums are taken by a different wave each group)
+    (17, 100, 128, 1, 144),
+    (145, 256, 256, 1, 144),  # one row past a 144-row tile
+    (300, 1000, 640, 1, 144),
+    (129, 513, 384, 2, 144),
+    (257, 300, 256, 8, 144),
+    (1322, 512, 2560, 1, 144),
+    (143, 129, 512, 0, 144),
+    (150, 300, 2048, 1, 144), # 16 groups: every wave takes the ninth row tile twice
+    # 64- and 48-row tiles (16 and 12 X DMA blocks over 8 waves; 4 and 3 of
+    # the 8 waves form the row sums)
+    (17, 100, 128, 1, 64),
+    (65, 256, 256, 1, 64),    # one row past a 64-row tile
+    (300, 1000, 640, 2, 64),
+    (1322, 512, 2560, 1, 64),
+    (17, 100, 128, 1, 48),
+    (49, 256, 256, 1, 48),    # one row past a 48-row tile
+    (300, 1000, 640, 8, 48),
+    (47, 129, 512, 0, 48),
+    # 80-row tiles (20 X DMA blocks over 8 waves)
+    (17, 100, 128, 1, 80),
+    (81, 256, 256, 1, 80),
+    (300, 1000, 640, 1, 80),
+    (257, 300, 256, 8, 80),
+    (1322, 512, 2560, 1, 80),
+    # automatic tile height and split
+    (200, 700, 1280, 0, None),
+    (1000, 300, 4096, 0, None),
 ]
 
 
@@ -243,39 +208,74 @@ TILE_CASES = [
 def test_tile_parity(M, N, K, sk, cfg):
     c = make_inputs(M, N, K, seed=M + N * 3 + K)
     d = DevCase(c)
-    y = _run(d, sk=sk, path=w4.PATH_TILE, variant=cfg)
-    check_gate(y, oracle.gemm(c.x, d.p_host, c.s), f"tile M={M} N={N} K={K} sk={sk} cfg={cfg}")
+    y = nan_filled((M, N))
+    w4.w4a16_gemm(d.x, d.w, d.s, y=y, split_k=sk, path=w4.PATH_TILE, variant=cfg)
+    check_full(y, oracle.gemm(c.x, d.p_host, c.s), f"tile M={M} N={N} K={K} sk={sk} rows={cfg}")
+
+
+# Row sums of X on the tile path: with a wide N (at least 32 column tiles) and
+# a workspace of w4a16_gemm_workspace_bytes, a pre-pass forms them into the
+# workspace; with no workspace (or too small a one) the tile kernel forms
+# them itself. Both ways, at the same shapes.
+ROWSUM_CASES = [
+    # M, N, K, split_k, rows per tile
+    (300, 8192, 640, 1, 128),
+    (129, 8448, 384, 2, 144),     # M tail, split-K; N = 33 column tiles
+    (97, 8193, 512, 1, 96),       # N tail in the 33rd column tile
+    (1, 8192, 256, 1, 48),
+    (200, 8192, 1280, 4, 80),
+]
+
+
+@pytest.mark.parametrize("prepass", [True, False])
+@pytest.mark.parametrize("M,N,K,sk,rows", ROWSUM_CASES)
+def test_tile_rowsum_paths(M, N, K, sk, rows, prepass):
+    c = make_inputs(M, N, K, seed=M + N + K + 5)
+    d = DevCase(c)
+    need = w4.w4a16_gemm_workspace_bytes(M, N, K, sk, path=w4.PATH_TILE, variant=rows)
+    split = sk * M * N * 4 if sk > 1 else 0
+    split = (split + 255) // 256 * 256
+    assert need > split                                   # the pre-pass row sums are part of it
+    nbytes = need if prepass else max(split, 16)          # room for the partials only: in-kernel sums
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    y = nan_filled((M, N))
+    w4.w4a16_gemm(d.x, d.w, d.s, y=y, split_k=sk, workspace=ws, path=w4.PATH_TILE, variant=rows)
+    check_full(y, oracle.gemm(c.x, d.p_host, c.s), f"tile M={M} N={N} K={K} sk={sk} rows={rows} pre-pass={prepass}")
+    if prepass:
+        # the row sums the pre-pass left in the workspace: -136 * sum of each 128-group, fp32
+        sx = ws[split // 4: split // 4 + (K // 128) * ((M + 3) // 4 * 4)].view(K // 128, -1)[:, :M].cpu().numpy()
+        ref = -136.0 * oracle.bf16_to_f64(c.x).reshape(M, K // 128, 128).sum(axis=2).T
+        assert np.allclose(sx, ref, rtol=1e-5, atol=1e-3)
 
 
 # ------------------------------------------------------------------ grouped
 
 GROUPED_CASES = [
-    # m_sizes, N, K, tile config
+    # m_sizes, N, K, rows per tile (None = automatic)
     ([37], 256, 384, None),
-    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 0),
-    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 1),
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, None),
     ([0, 0, 0, 50], 128, 128, None),
-    ([128, 128, 128], 256, 512, 1),
-    ([1, 1, 1, 1, 1], 64, 128, 0),
-    ([37], 256, 384, 2),
-    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 2),
-    ([1, 1, 1, 1, 1], 64, 128, 2),
-    ([128, 128, 128], 256, 512, 2),
-    ([0, 0, 0, 50], 128, 128, 2),
-    ([5, 70, 33], 257, 384, 2),   # N * G odd per weight group: unaligned group bases
-    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 3),   # 96-row tiles
-    ([96, 97, 95, 0, 1], 256, 640, 3),
-    ([37], 256, 384, 3),
-    ([0, 0, 0, 50], 128, 128, 3),
-    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 4),   # 112-row tiles
-    ([112, 113, 111, 0, 1], 256, 640, 4),
-    ([37], 256, 384, 4),
-    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 5),   # 80-row tiles
-    ([80, 81, 79, 0, 1], 256, 640, 5),
-    ([0, 0, 0, 0, 0, 0, 0, 700], 512, 256, 5),      # all rows in the last group
-    ([144, 145, 143, 0, 1], 256, 640, 6),           # 144-row tiles
-    ([64, 65, 63, 0, 1], 256, 640, 7),              # 64-row tiles
-    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 8),   # 48-row tiles
+    ([128, 128, 128], 256, 512, None),
+    ([1, 1, 1, 1, 1], 64, 128, None),
+    ([37], 256, 384, 128),
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 128),
+    ([1, 1, 1, 1, 1], 64, 128, 128),
+    ([128, 128, 128], 256, 512, 128),
+    ([0, 0, 0, 50], 128, 128, 128),
+    ([5, 70, 33], 257, 384, 128),   # N * G odd per weight group: unaligned group bases
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 96),
+    ([96, 97, 95, 0, 1], 256, 640, 96),
+    ([37], 256, 384, 96),
+    ([0, 0, 0, 50], 128, 128, 96),
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 112),
+    ([112, 113, 111, 0, 1], 256, 640, 112),
+    ([37], 256, 384, 112),
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 80),
+    ([80, 81, 79, 0, 1], 256, 640, 80),
+    ([0, 0, 0, 0, 0, 0, 0, 700], 512, 256, 80),      # all rows in the last group
+    ([144, 145, 143, 0, 1], 256, 640, 144),
+    ([64, 65, 63, 0, 1], 256, 640, 64),
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 48),
 ]
 
 
@@ -284,27 +284,27 @@ def test_grouped_parity(ms, N, K, cfg):
     c = make_inputs(sum(ms), N, K, seed=len(ms) * 31 + N + K, G=len(ms), m_sizes=ms)
     d = DevCase(c)
     assert d.packed_matches_oracle()
-    y = w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, variant=cfg)
-    torch.cuda.synchronize()
-    check_gate(bits_host(y), oracle.gemm_grouped(c.x, d.p_host, c.s, c.m_sizes), f"grouped {ms} N={N} K={K}")
+    y = nan_filled((sum(ms), N))
+    w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, y=y, variant=cfg)
+    check_full(y, oracle.gemm_grouped(c.x, d.p_host, c.s, c.m_sizes), f"grouped {ms} N={N} K={K} rows={cfg}")
 
 
 # ------------------------------------------------------------------ batched
 
 BATCHED_CASES = [
-    # B, M, N, K, split_k, tile configuration (None = automatic)
+    # B, M, N, K, split_k, rows per tile (None = automatic)
     (1, 17, 100, 128, 0, None),
     (3, 1, 256, 512, 0, None),      # one row per problem
     (4, 16, 300, 640, 2, None),     # N tail, split-K
     (2, 130, 513, 384, 0, None),    # M tail across tiles, N * G odd per problem
     (3, 97, 257, 256, 4, None),     # more slices than groups per slice of 1
     (5, 33, 129, 1280, 8, None),
-    (2, 64, 256, 2560, 16, 2),      # 16 slices of 20 groups
-    (2, 144, 256, 256, 1, 6),       # 144-row tiles: exactly one per problem
-    (3, 100, 300, 384, 1, 5),       # 80-row tiles: a problem spans two tiles
-    (2, 113, 300, 256, 2, 4),
-    (3, 50, 200, 256, 2, 0),        # the LDS-dequant tile kernel
-    (2, 70, 130, 384, 1, 1),
+    (2, 64, 256, 2560, 16, 128),    # 16 slices of 20 groups
+    (2, 144, 256, 256, 1, 144),     # exactly one tile per problem
+    (3, 100, 300, 384, 1, 80),      # a problem spans two tiles
+    (2, 113, 300, 256, 2, 112),
+    (3, 50, 200, 256, 2, 48),
+    (2, 70, 130, 384, 1, 64),
 ]
 
 
@@ -314,10 +314,10 @@ def test_batched_parity(B, M, N, K, sk, cfg):
     d = DevCase(c)
     assert d.packed_matches_oracle()
     x = d.x.view(B, M, K)
-    y = w4.w4a16_gemm_batched(x, d.w, d.s, split_k=sk, variant=cfg)
-    torch.cuda.synchronize()
+    y = nan_filled((B, M, N))
+    w4.w4a16_gemm_batched(x, d.w, d.s, y=y, split_k=sk, variant=cfg)
     ref = oracle.gemm_batched(c.x.reshape(B, M, K), d.p_host, c.s)
-    check_gate(bits_host(y.view(B * M, N)), ref.reshape(B * M, N), f"batched B={B} M={M} N={N} K={K} sk={sk}")
+    check_full(y, ref, f"batched B={B} M={M} N={N} K={K} sk={sk}")
     # every problem on its own gate too (a swapped problem would pass the joint gate only by luck)
     yb = bits_host(y.view(B * M, N)).reshape(B, M, N)
     for b in range(B):
@@ -335,91 +335,103 @@ def test_batched_repeat_bitwise():
     assert np.array_equal(y0, y1)
 
 
-# ------------------------------------------------------------------ full sizes, sampled outputs
+# ------------------------------------------------------------------ full sizes, whole outputs
+#
+# Each workload in the launch configuration bench.py times (same entry point,
+# same automatic or explicit split), its output pre-filled with NaN so that a
+# tile that is never written fails, and compared element by element with the
+# float64 oracle (about a second of host BLAS per workload).
 
-def _sample_entries(rng, M, N, n_random, row_edges=(), col_edges=()):
-    """Random (row, col) pairs plus the corners of the given row and column
-    boundaries (tile edges, last row and column)."""
-    rows = list(rng.integers(0, M, n_random))
-    cols = list(rng.integers(0, N, n_random))
-    for r in list(row_edges) + [0, M - 1]:
-        for c in list(col_edges) + [0, N - 1]:
-            if 0 <= r < M and 0 <= c < N:
-                rows.append(r)
-                cols.append(c)
-    return np.asarray(rows, dtype=np.int64), np.asarray(cols, dtype=np.int64)
-
-
-def _gate_sampled(y_bits, rows, cols, ref, what):
-    got = y_bits[rows, cols]
-    assert np.all(np.isfinite(oracle.bf16_to_f64(y_bits))), f"{what}: non-finite output"
-    check_gate(got, ref, what)
+def test_decode_gemv_full_size():
+    c = make_config("decode_gemv")
+    d = DevCase(c)
+    y = nan_filled((c.M, c.N))
+    w4.w4a16_gemm(d.x, d.w, d.s, y=y)
+    check_full(y, oracle.gemm(c.x, d.p_host, c.s), "decode 1x17408x5120")
 
 
-def test_prefill_full_size_sampled():
-    # the deep-prefill workload in the launch configuration bench.py times
-    # (default path and tile configuration), checked on sampled entries
+@pytest.mark.parametrize("sk", [0, 1, 2, 4, 8])
+def test_decode_splitk_full_size(sk):
+    # the small-batch decode workload at every split bench.py times; the
+    # final output is also the bit-exact reduce of the kernel's own partials
+    c = make_config("decode_splitk")
+    d = DevCase(c)
+    y = nan_filled((c.M, c.N))
+    need = w4.w4a16_gemm_workspace_bytes(c.M, c.N, c.K, sk)
+    ws = torch.full((max(need // 4, 1) + 4,), float("nan"), dtype=torch.float32, device="cuda")
+    w4.w4a16_gemm(d.x, d.w, d.s, y=y, split_k=sk, workspace=ws)
+    check_full(y, oracle.gemm(c.x, d.p_host, c.s), f"small-batch 16x8192x8192 sk={sk}")
+    eff = sk if sk else w4.w4a16_gemm_auto_split_k(c.M, c.N, c.K)
+    if eff > 1:
+        part = ws[: eff * c.M * c.N].view(eff, c.M, c.N).cpu().numpy()
+        assert np.array_equal(bits_host(y), oracle.splitk_reduce_bf16(part))
+
+
+@pytest.mark.parametrize("prepass", [True, False])
+def test_prefill_full_size(prepass):
+    # as benched: the default choice with its workspace (the row sums from the
+    # pre-pass); and with no workspace (the tile kernel forms them)
     c = make_config("prefill")
     d = DevCase(c)
-    y = bits_host(w4.w4a16_gemm(d.x, d.w, d.s))
-    torch.cuda.synchronize()
-    M, N = c.M, c.N
-    rng = np.random.default_rng(11)
-    rows, cols = _sample_entries(rng, M, N, 3000, row_edges=(111, 112, 127, 128, 143, 144, 1231, 1232, 1279, 1280, 1295, 1296, 1321),
-                                 col_edges=(255, 256, 19199, 19200, 19455))
-    ref = oracle.gemm_entries(c.x, d.p_host, c.s, rows, cols)
-    _gate_sampled(y, rows, cols, ref, "prefill 1322x19456x2560 sampled")
+    y = nan_filled((c.M, c.N))
+    ws = None if prepass else torch.empty(4, dtype=torch.float32, device="cuda")
+    w4.w4a16_gemm(d.x, d.w, d.s, y=y, workspace=ws)
+    check_full(y, oracle.gemm(c.x, d.p_host, c.s), f"prefill 1322x19456x2560 pre-pass={prepass}")
 
 
-def test_grouped_full_size_sampled():
+def test_grouped_full_size():
     c = make_config("grouped")
     d = DevCase(c)
-    y = bits_host(w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes))
-    torch.cuda.synchronize()
-    ms = c.m_sizes.astype(np.int64)
-    starts = oracle.group_starts(ms)
-    rng = np.random.default_rng(12)
-    all_rows, all_cols, all_ref = [], [], []
-    for g in range(ms.shape[0]):
-        if ms[g] == 0:
-            continue
-        r0 = int(starts[g])
-        rows, cols = _sample_entries(rng, int(ms[g]), c.N, 300, row_edges=(127, 128), col_edges=(255, 256))
-        ref = oracle.gemm_entries(c.x[r0:r0 + int(ms[g])], d.p_host[g], c.s[g], rows, cols)
-        all_rows.append(rows + r0)
-        all_cols.append(cols)
-        all_ref.append(ref)
-    _gate_sampled(y, np.concatenate(all_rows), np.concatenate(all_cols), np.concatenate(all_ref),
-                  f"grouped G=8 {list(ms)} sampled")
+    y = nan_filled((c.M, c.N))
+    w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, y=y)
+    ms = [int(v) for v in c.m_sizes]
+    ref = oracle.gemm_grouped(c.x, d.p_host, c.s, c.m_sizes)
+    check_full(y, ref, f"grouped G=8 {ms}")
+    # every non-empty group on its own gate too
+    starts = oracle.group_starts(c.m_sizes)
+    yb = bits_host(y)
+    for g, m in enumerate(ms):
+        if m:
+            r0 = int(starts[g])
+            check_gate(yb[r0:r0 + m], ref[r0:r0 + m], f"grouped group {g}")
 
 
-def test_batched_full_size_sampled():
-    # the batched workload in the launch configuration bench.py times
-    # (automatic tile height and split), checked on sampled entries per problem
+def test_batched_full_size():
     c = make_config("batched")
     B, M, N, K = c.G, c.M // c.G, c.N, c.K
     d = DevCase(c)
-    y = bits_host(w4.w4a16_gemm_batched(d.x.view(B, M, K), d.w, d.s).view(B * M, N))
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(13)
-    all_rows, all_cols, all_ref = [], [], []
+    y = nan_filled((B, M, N))
+    w4.w4a16_gemm_batched(d.x.view(B, M, K), d.w, d.s, y=y)
+    ref = oracle.gemm_batched(c.x.reshape(B, M, K), d.p_host, c.s)
+    check_full(y, ref, f"batched B={B} {M}x{N}x{K}")
+    yb = bits_host(y)
     for b in range(B):
-        r0 = b * M
-        rows, cols = _sample_entries(rng, M, N, 300, row_edges=(79, 80, 127, 128), col_edges=(255, 256))
-        ref = oracle.gemm_entries(c.x[r0:r0 + M], d.p_host[b], c.s[b], rows, cols)
-        all_rows.append(rows + r0)
-        all_cols.append(cols)
-        all_ref.append(ref)
-    _gate_sampled(y, np.concatenate(all_rows), np.concatenate(all_cols), np.concatenate(all_ref),
-                  f"batched B={B} {M}x{N}x{K} sampled")
+        check_gate(yb[b], ref[b], f"batched problem {b}")
 
 
-def test_grouped_empty_total_is_noop():
+def _guarded_empty_call(call, n_cols):
+    """Runs `call(y)` with y a (0, n_cols) view at the start of a NaN-filled
+    buffer and checks that nothing of the buffer was written."""
+    buf = nan_filled((64, n_cols))
+    before = bits_host(buf)
+    call(buf[:0])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_host(buf), before)
+
+
+def test_m0_writes_nothing():
+    c = make_inputs(1, 64, 256, seed=3)
+    d = DevCase(c)
+    _guarded_empty_call(lambda y: w4.w4a16_gemm(d.x[:0], d.w, d.s, y=y), 64)
+    _guarded_empty_call(lambda y: w4.w4a16_gemm(d.x[:0], d.w, d.s, y=y, split_k=4), 64)
+    _guarded_empty_call(lambda y: w4.w4a16_gemm(d.x[:0], d.w, d.s, y=y, group_size=128, path=w4.PATH_TILE,
+                                                 variant=128), 64)
+
+
+def test_grouped_empty_total_writes_nothing():
     c = make_inputs(0, 64, 128, seed=5, G=3, m_sizes=[0, 0, 0])
     d = DevCase(c)
-    y = torch.full((0, 64), 1.0, dtype=torch.bfloat16, device="cuda")
-    w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, y=y)
-    torch.cuda.synchronize()
+    _guarded_empty_call(lambda y: w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, y=y), 64)
 
 
 # ------------------------------------------------------------------ split-K partials and reduce
@@ -487,15 +499,6 @@ def test_n1_and_k128():
         check_gate(_run(d), oracle.gemm(c.x, d.p_host, c.s), f"N=1 M={M}")
 
 
-def test_m0_leaves_output_untouched():
-    c = make_inputs(1, 64, 256, seed=3)
-    d = DevCase(c)
-    x0 = d.x[:0]
-    y = torch.full((0, 64), 2.0, dtype=torch.bfloat16, device="cuda")
-    w4.w4a16_gemm(x0, d.w, d.s, y=y)
-    torch.cuda.synchronize()
-
-
 # ------------------------------------------------------------------ determinism and graphs
 
 @pytest.mark.parametrize("path,M,N,K,sk", [
@@ -537,9 +540,7 @@ def test_grouped_graph_replay():
     c = make_inputs(sum(ms), 300, 256, seed=12, G=len(ms), m_sizes=ms)
     d = DevCase(c)
     y = torch.empty((sum(ms), 300), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(w4.w4a16_gemm_grouped_workspace_bytes(len(ms), sum(ms), 300, 256) // 4,
-                     dtype=torch.float32, device="cuda")
-    w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, y=y, workspace=ws)
+    w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, y=y)
     torch.cuda.synchronize()
     ref = bits_host(y)
     s = torch.cuda.Stream()
@@ -547,7 +548,7 @@ def test_grouped_graph_replay():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, y=y, workspace=ws)
+            w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, y=y)
     torch.cuda.current_stream().wait_stream(s)
     for i in range(3):
         y.fill_(0)

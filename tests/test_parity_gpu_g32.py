@@ -15,7 +15,7 @@ import torch
 import bf16_activation_quantized_amd as w4
 import oracle
 from synth import make_inputs
-from gpu_util import DevCase, bits_host, check_gate
+from gpu_util import DevCase, bits_host, check_full, check_gate, nan_filled
 
 pytestmark = pytest.mark.gpu
 
@@ -36,28 +36,28 @@ def _gemm(d, **kw):
 
 
 TILE_CASES = [
-    # M, N, K, split_k, tile configuration (None = automatic)
+    # M, N, K, split_k, rows per tile (None = automatic)
     (1, 256, 128, 0, None),     # decode row count: the tile kernel at M = 1
     (16, 300, 512, 0, None),
-    (17, 100, 128, 1, 2),       # one 128-k stage (4 scale groups), M and N tails
-    (130, 256, 256, 1, 2),
-    (300, 1000, 640, 1, 2),     # steady state, N tail of 232 columns
-    (129, 513, 384, 2, 2),      # split-K slices of 2 and 1 stages, N * K/32 odd rows
-    (257, 300, 256, 8, 2),      # more slices than stages: empty slices write zeros
-    (1322, 512, 2560, 1, 2),    # the prefill row count and depth
-    (97, 256, 256, 1, 3),       # one row past a 96-row tile
-    (300, 1000, 640, 1, 3),
-    (95, 129, 512, 0, 3),
-    (113, 256, 256, 1, 4),      # one row past a 112-row tile
-    (1322, 512, 2560, 1, 4),
-    (224, 257, 384, 4, 4),
-    (81, 256, 256, 1, 5),       # one row past an 80-row tile
-    (300, 1000, 640, 2, 5),
-    (1322, 512, 2560, 1, 5),
+    (17, 100, 128, 1, 128),       # one 128-k stage (4 scale groups), M and N tails
+    (130, 256, 256, 1, 128),
+    (300, 1000, 640, 1, 128),     # steady state, N tail of 232 columns
+    (129, 513, 384, 2, 128),      # split-K slices of 2 and 1 stages, N * K/32 odd rows
+    (257, 300, 256, 8, 128),      # more slices than stages: empty slices write zeros
+    (1322, 512, 2560, 1, 128),    # the prefill row count and depth
+    (97, 256, 256, 1, 96),       # one row past a 96-row tile
+    (300, 1000, 640, 1, 96),
+    (95, 129, 512, 0, 96),
+    (113, 256, 256, 1, 112),      # one row past a 112-row tile
+    (1322, 512, 2560, 1, 112),
+    (224, 257, 384, 4, 112),
+    (81, 256, 256, 1, 80),       # one row past an 80-row tile
+    (300, 1000, 640, 2, 80),
+    (1322, 512, 2560, 1, 80),
     (600, 700, 1280, 0, None),
     (64, 64, 1024, 4, None),
     (130, 300, 16384, 0, None),   # 512 scale groups per row, automatic split
-    (40, 257, 16384, 16, 5),      # 16 slices of 8 stages, N * K/32 odd rows
+    (40, 257, 16384, 16, 80),      # 16 slices of 8 stages, N * K/32 odd rows
 ]
 
 
@@ -66,8 +66,26 @@ def test_g32_tile_parity(M, N, K, sk, cfg):
     c = make_inputs(M, N, K, seed=M + N * 3 + K + 32, group=G32)
     assert c.s.shape == (N, K // G32)
     d = DevCase(c)
-    y = _gemm(d, split_k=sk, path=w4.PATH_TILE if cfg is not None else None, variant=cfg)
-    check_gate(y, oracle.gemm(c.x, d.p_host, c.s, G32), f"g32 tile M={M} N={N} K={K} sk={sk} cfg={cfg}")
+    y = nan_filled((M, N))
+    w4.w4a16_gemm(d.x, d.w, d.s, y=y, group_size=G32, split_k=sk,
+                  path=w4.PATH_TILE if cfg is not None else None, variant=cfg)
+    check_full(y, oracle.gemm(c.x, d.p_host, c.s, G32), f"g32 tile M={M} N={N} K={K} sk={sk} rows={cfg}")
+
+
+@pytest.mark.parametrize("prepass", [True, False])
+@pytest.mark.parametrize("M,N,K,sk,rows", [(130, 2048, 512, 1, 128), (97, 2049, 384, 2, 80), (1, 2304, 256, 1, 96)])
+def test_g32_rowsum_paths(M, N, K, sk, rows, prepass):
+    # from 8 column tiles the 32-group row sums come from the pre-pass when the
+    # workspace has room for them, else the tile kernel forms them
+    c = make_inputs(M, N, K, seed=M + N + K + 320, group=G32)
+    d = DevCase(c)
+    need = w4.w4a16_gemm_workspace_bytes(M, N, K, sk, path=w4.PATH_TILE, variant=rows, group_size=G32)
+    split = (sk * M * N * 4 + 255) // 256 * 256 if sk > 1 else 0
+    assert need > split
+    ws = torch.full(((need if prepass else max(split, 16)) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    y = nan_filled((M, N))
+    w4.w4a16_gemm(d.x, d.w, d.s, y=y, split_k=sk, workspace=ws, path=w4.PATH_TILE, variant=rows, group_size=G32)
+    check_full(y, oracle.gemm(c.x, d.p_host, c.s, G32), f"g32 M={M} N={N} K={K} sk={sk} pre-pass={prepass}")
 
 
 def test_g32_scales_differ_within_a_stage():
@@ -80,7 +98,7 @@ def test_g32_scales_differ_within_a_stage():
     ex = 0x3D80 - (np.arange(K // G32) % 4) * 0x80     # bf16 2^-4, 2^-5, 2^-6, 2^-7
     c.s[:] = ex.astype(np.uint16)[None, :]
     d = DevCase(c)
-    for cfg in (2, 3, 4, 5):
+    for cfg in (128, 96, 112, 80):
         y = _gemm(d, split_k=1, path=w4.PATH_TILE, variant=cfg)
         ref = oracle.gemm(c.x, d.p_host, c.s, G32)
         check_gate(y, ref, f"g32 stepped scales cfg={cfg}")
@@ -109,23 +127,25 @@ def test_g32_n1_k128_and_m0():
         c = make_inputs(M, 1, 128, seed=M + 32, group=G32)
         d = DevCase(c)
         check_gate(_gemm(d), oracle.gemm(c.x, d.p_host, c.s, G32), f"g32 N=1 K=128 M={M}")
-    # M = 0: nothing is enqueued and the output is left as it was
+    # M = 0: nothing is enqueued and no byte of the buffer behind y is written
     c = make_inputs(1, 64, 256, seed=5, group=G32)
     d = DevCase(c)
-    y = torch.full((0, 64), 1.0, dtype=torch.bfloat16, device="cuda")
-    w4.w4a16_gemm(d.x[:0], d.w, d.s, y=y, group_size=G32)
+    buf = nan_filled((16, 64))
+    before = bits_host(buf)
+    w4.w4a16_gemm(d.x[:0], d.w, d.s, y=buf[:0], group_size=G32)
     torch.cuda.synchronize()
+    assert np.array_equal(bits_host(buf), before)
 
 
 GROUPED_CASES = [
-    # m_sizes, N, K, tile configuration (None = automatic)
+    # m_sizes, N, K, rows per tile (None = automatic)
     ([37], 256, 384, None),
     ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, None),
-    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 2),
-    ([96, 97, 95, 0, 1], 256, 640, 3),
-    ([112, 113, 111, 0, 1], 256, 640, 4),
-    ([80, 81, 79, 0, 1], 256, 640, 5),
-    ([5, 70, 33], 257, 384, 2),     # N * K/32 odd per weight group
+    ([3, 0, 129, 5, 0, 255, 1, 64], 300, 256, 128),
+    ([96, 97, 95, 0, 1], 256, 640, 96),
+    ([112, 113, 111, 0, 1], 256, 640, 112),
+    ([80, 81, 79, 0, 1], 256, 640, 80),
+    ([5, 70, 33], 257, 384, 128),     # N * K/32 odd per weight group
     ([0, 0, 0, 50], 128, 128, None),
 ]
 
@@ -134,20 +154,20 @@ GROUPED_CASES = [
 def test_g32_grouped_parity(ms, N, K, cfg):
     c = make_inputs(sum(ms), N, K, seed=len(ms) * 31 + N + K + 32, G=len(ms), m_sizes=ms, group=G32)
     d = DevCase(c)
-    y = w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, variant=cfg, group_size=G32)
-    torch.cuda.synchronize()
+    y = nan_filled((sum(ms), N))
+    w4.w4a16_gemm_grouped(d.x, d.w, d.s, d.m_sizes, y=y, variant=cfg, group_size=G32)
     ref = oracle.gemm_grouped(c.x, d.p_host, c.s, c.m_sizes, G32)
-    check_gate(bits_host(y), ref, f"g32 grouped {ms} N={N} K={K} cfg={cfg}")
+    check_full(y, ref, f"g32 grouped {ms} N={N} K={K} rows={cfg}")
 
 
 BATCHED_CASES = [
-    # B, M, N, K, split_k, tile configuration (None = automatic)
+    # B, M, N, K, split_k, rows per tile (None = automatic)
     (3, 1, 256, 512, 0, None),
     (4, 16, 300, 640, 2, None),
     (2, 130, 513, 384, 0, None),
-    (3, 97, 257, 256, 4, 3),
-    (2, 113, 300, 256, 2, 4),
-    (3, 100, 300, 384, 1, 5),
+    (3, 97, 257, 256, 4, 96),
+    (2, 113, 300, 256, 2, 112),
+    (3, 100, 300, 384, 1, 80),
 ]
 
 
@@ -155,9 +175,10 @@ BATCHED_CASES = [
 def test_g32_batched_parity(B, M, N, K, sk, cfg):
     c = make_inputs(B * M, N, K, seed=B * 1000 + M + N + K + 32, G=B, m_sizes=[M] * B, group=G32)
     d = DevCase(c)
-    y = w4.w4a16_gemm_batched(d.x.view(B, M, K), d.w, d.s, split_k=sk, variant=cfg, group_size=G32)
-    torch.cuda.synchronize()
+    y = nan_filled((B, M, N))
+    w4.w4a16_gemm_batched(d.x.view(B, M, K), d.w, d.s, y=y, split_k=sk, variant=cfg, group_size=G32)
     ref = oracle.gemm_batched(c.x.reshape(B, M, K), d.p_host, c.s, G32)
+    check_full(y, ref, f"g32 batched B={B} M={M} N={N} K={K} sk={sk}")
     yb = bits_host(y.view(B * M, N)).reshape(B, M, N)
     for b in range(B):
         check_gate(yb[b], ref[b], f"g32 batched B={B} M={M} N={N} K={K} sk={sk} problem {b}")
@@ -204,23 +225,14 @@ LAYER_GEMMS = [
 ]
 
 
+@pytest.mark.parametrize("group", [32, 128])
 @pytest.mark.parametrize("name,N,K", LAYER_GEMMS)
-def test_g32_layer_gemm_full_size_sampled(name, N, K):
-    # default path and tile choice (what the per-layer bench times), checked
-    # on sampled entries: random ones plus the corners of tile boundaries
+def test_layer_gemm_full_size(name, N, K, group):
+    # default path, tile choice and split (what the per-layer bench times),
+    # the whole output against the oracle, every element written
     M = 1322
-    c = make_inputs(M, N, K, seed=1322 + N + K, group=G32)
+    c = make_inputs(M, N, K, seed=1322 + N + K, group=group)
     d = DevCase(c)
-    y = _gemm(d)
-    assert np.all(np.isfinite(oracle.bf16_to_f64(y))), name
-    rng = np.random.default_rng(N + K)
-    rows = list(rng.integers(0, M, 1500))
-    cols = list(rng.integers(0, N, 1500))
-    for r in (0, 79, 80, 95, 96, 111, 112, 127, 128, 1279, 1280, M - 1):
-        for col in (0, 255, 256, N - 1):
-            rows.append(r)
-            cols.append(col)
-    rows = np.asarray(rows, dtype=np.int64)
-    cols = np.asarray(cols, dtype=np.int64)
-    ref = oracle.gemm_entries(c.x, d.p_host, c.s, rows, cols, G32)
-    check_gate(y[rows, cols], ref, f"g32 {name} {M}x{N}x{K} sampled")
+    y = nan_filled((M, N))
+    w4.w4a16_gemm(d.x, d.w, d.s, y=y, group_size=group)
+    check_full(y, oracle.gemm(c.x, d.p_host, c.s, group), f"g{group} {name} {M}x{N}x{K}")
