@@ -65,6 +65,7 @@ def _lib():
         "w4a16_gemm_batched_workspace_bytes": (SZ, [I32, I64, I64, I64, I32, I32]),
         "w4a16_gemm_batched": (ctypes.c_int, [P, P, P, P, I32, I64, I64, I64, I32, I32, P, SZ, P]),
         "w4a16_splitk_reduce": (ctypes.c_int, [P, P, I32, I64, I64, P]),
+        "w4a16_gemm_noalloc": (ctypes.c_int, [P, P, P, P, I64, I64, I64, I32, I32, P]),
         # internal entry points that force a kernel (tests, benchmarks)
         "w4a16_gemm_workspace_bytes_ex": (SZ, [I64, I64, I64, I32, I32, P]),
         "w4a16_gemm_ex": (ctypes.c_int, [P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P, P]),
@@ -195,6 +196,24 @@ def w4a16_gemm(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
         st = L.w4a16_gemm_ex(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(y), M, N, K, group_size, split_k,
                              _ptr(workspace), wbytes, _stream(stream), cfg)
     _raise(st, "w4a16_gemm")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def w4a16_gemm_noalloc(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor, y: torch.Tensor,
+                       split_k: int = 0, stream=None, group_size: int = GROUP_SIZE) -> torch.Tensor:
+    """w4a16_gemm with the library's own device scratch in place of a
+    workspace (the C entry point allocates nothing; y must be given)."""
+    _check(x, "x", torch.bfloat16)
+    M, K = x.shape
+    N = w_packed.shape[0]
+    _check(w_packed, "w_packed", torch.uint8, (N, K // 2))
+    _check(scales, "scales", torch.bfloat16, (N, K // group_size))
+    _check(y, "y", torch.bfloat16, (M, N))
+    _raise(_lib().w4a16_gemm_noalloc(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(y), M, N, K, group_size, split_k,
+                                     _stream(stream)), "w4a16_gemm_noalloc")
     return y
 
 

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include <stddef.h>
 #include <stdint.h>
@@ -420,6 +421,33 @@ size_t batched_workspace_bytes(int32_t B, int64_t M, int64_t N, int64_t K, int32
   return (size_t)(round_up(p.ws_split, 256) + p.ws_sx);
 }
 
+// ---------------------------------------------------------------- scratch of the no-allocation entry point
+// Device scratch for w4a16_gemm_noalloc: the split-K partials and the
+// pre-pass row sums live here instead of in a caller's workspace. Each GPU
+// holds its own copy (allocated with the library's code object) until the
+// process ends. In host code `scratch` names a host-side stand-in, so its
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)W4A16_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's scratch (nullptr on failure): looked up
+// with the device current, on the first call per device, and kept.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -473,6 +501,27 @@ w4a16_status w4a16_gemm(const uint16_t* x, const uint8_t* w_packed, const uint16
                         int64_t N, int64_t K, int32_t group_size, int32_t split_k, float* workspace,
                         size_t workspace_bytes, void* stream) {
   return run_gemm(x, w_packed, scales, y, M, N, K, group_size, split_k, workspace, workspace_bytes, stream, nullptr);
+}
+
+w4a16_status w4a16_gemm_noalloc(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales, uint16_t* y,
+                                int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t split_k, void* stream) {
+  Plan p;
+  bool empty = false;
+  w4a16_status st = plan_gemm(x, w_packed, scales, y, M, N, K, group_size, split_k, nullptr, &p, &empty);
+  if (st != W4A16_OK || empty) return st;
+  // the partials must fit the scratch; the row sums only where they fit too
+  // (otherwise the tile kernel forms them), as with a caller's workspace
+  if (round_up(p.ws_split, 256) > kScratchBytes) return W4A16_ERR_WORKSPACE;
+  float* ws = nullptr;
+  if (p.ws_split > 0 || p.ws_sx > 0) {
+    ws = reinterpret_cast<float*>(scratch_ptr());
+    if (ws == nullptr) return W4A16_ERR_LAUNCH;
+  }
+  float* rowsums = nullptr;
+  if (p.ws_sx > 0 && plan_bytes(p) <= kScratchBytes)
+    rowsums = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + round_up(p.ws_split, 256));
+  return launch_plan(p, x, w_packed, scales, y, M, N, K, group_size, ws, rowsums,
+                     reinterpret_cast<hipStream_t>(stream));
 }
 
 w4a16_status w4a16_gemm_ex(const uint16_t* x, const uint8_t* w_packed, const uint16_t* scales, uint16_t* y,

@@ -151,6 +151,32 @@ w4a16_status w4a16_gemm(const uint16_t* x, const uint8_t* w_packed,
                         size_t workspace_bytes, void* stream);
 
 /*
+ * w4a16_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels, with the workspace replaced by a scratch
+ * array inside the library, W4A16_NOALLOC_SCRATCH_BYTES bytes per GPU, held
+ * from the library's first use on that GPU until the process ends. The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   Arguments as for w4a16_gemm, without workspace and workspace_bytes.
+ *   The split-K partials (SK * M * N * 4 bytes, rounded up to 256, when the
+ *   effective SK is above 1) must fit the scratch, else W4A16_ERR_WORKSPACE
+ *   is returned before anything is enqueued; the pre-pass row sums are used
+ *   where they fit beside them (else the tile kernel forms them). Every byte
+ *   of scratch a call reads is first written by that call.
+ *   All calls on one GPU share its scratch: calls that overlap in time on one
+ *   GPU (different streams, or different host threads without ordering) race
+ *   and give undefined results; calls ordered on one stream are safe.
+ * The kernels are those w4a16_gemm runs with a workspace of
+ * w4a16_gemm_workspace_bytes_gs bytes (when that fits the scratch): the same
+ * results, bit for bit.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (16u << 20)
+w4a16_status w4a16_gemm_noalloc(const uint16_t* x, const uint8_t* w_packed,
+                                const uint16_t* scales, uint16_t* y,
+                                int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                int32_t split_k, void* stream);
+
+/*
  * Grouped GEMM in one launch ("Add Triton BF16xINT4 rowwise GEMM for ROCm
  * gfx942/gfx950", Implementation "Native fused grouped kernel"): for each
  * group g with
