@@ -38,9 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROTATE_BYTES = 512 << 20
 # GPU work run back to back before the timed replay (clock settling)
-SETTLE_S = 0.05
-# spin before the timed replay (GPU clock cycles, about a millisecond)
-PREROLL_CYCLES = 2_000_000
+SETTLE_S = 0.1
 # the decode GEMV at M=1, N=17408, K=5120, split_k 1 (40 groups per slice ->
 # 2-row blocks, 5 instructions per block; one block in flight; one 8-wave
 # workgroup per compute unit, x in registers)
@@ -88,10 +86,12 @@ def time_steps(step, steps, warmup, settle_s=SETTLE_S):
     HIP graph on a side stream (the library enqueues only kernels, so the
     capture is exact) and replayed untimed until at least `settle_s` seconds
     of GPU work have run back to back (however many replays that takes), so
-    that the clocks have left their idle state; the timed region is then one
-    replay of exactly K steps bracketed by synchronisations and HIP events on
-    that stream. The shader and memory clocks are sampled while the settling
-    replays run. Returns (total seconds, seconds per step, clock record)."""
+    that the clocks have left their idle state (under the decode GEMV's load
+    the shader clock climbs for tens of milliseconds); the timed region is
+    then one replay of exactly K steps, between HIP events on that stream,
+    behind two untimed replays, all bracketed by synchronisations. The
+    shader and memory clocks are sampled while the settling replays run.
+    Returns (total seconds, seconds per step, clock record)."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -120,10 +120,12 @@ def time_steps(step, steps, warmup, settle_s=SETTLE_S):
         settled_s = time.perf_counter() - t_settle
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
-        # a spin kernel of about a millisecond ahead of the first event keeps
-        # the host's submission of the graph out of the timed region: t0 .. t1
-        # then spans the K steps' GPU execution only
-        torch.cuda._sleep(PREROLL_CYCLES)
+        # two more untimed replays queued ahead of the first event keep the
+        # GPU under the same load (clocks as settled) and the host's
+        # submission of the timed graph out of the timed region: t0 .. t1
+        # spans exactly the K steps' GPU execution
+        g.replay()
+        g.replay()
         t0.record(s)
         g.replay()
         t1.record(s)
@@ -174,20 +176,26 @@ class _Clocks:
         return dict(sclk=self._current(os.path.join(d, "pp_dpm_sclk")),
                     mclk=self._current(os.path.join(d, "pp_dpm_mclk")))
 
-    def sample_while(self, event, every_s=0.004, most=12):
+    def sample_while(self, event, every_s=0.01, most=40):
         """Samples every few milliseconds until `event` has completed (the
-        GPU work queued before it is done); the samples' sclk values and the
-        last mclk."""
+        GPU work queued before it is done): the first, median and last sclk
+        (MHz) and the last mclk."""
         if not self._find():
             return None
         sclk, last = [], None
         while len(sclk) < most:
             last = self.sample()
-            sclk.append(last["sclk"])
+            try:
+                sclk.append(int(str(last["sclk"]).lower().replace("mhz", "")))
+            except ValueError:
+                pass
             if event.query():
                 break
             time.sleep(every_s)
-        return dict(sclk_samples=sclk, mclk=last["mclk"])
+        if not sclk:
+            return dict(mclk=last["mclk"] if last else None)
+        return dict(sclk_mhz_first=sclk[0], sclk_mhz_median=int(np.median(sclk)), sclk_mhz_last=sclk[-1],
+                    sclk_samples=len(sclk), mclk=last["mclk"])
 
 
 CLOCKS = _Clocks()

@@ -170,9 +170,11 @@ template <int R, int I, int D, int WAVES, bool XLDS>
 __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* __restrict__ x,
                                                                const uint8_t* __restrict__ w,
                                                                const uint16_t* __restrict__ s,
-                                                               uint16_t* __restrict__ y,
-                                                               float* __restrict__ ws,
-                                                               int N, int K, int gps) {
+                                                               void* __restrict__ out,
+                                                               int N, int K, int gps, int bper, int brem) {
+  // (13 dwords of arguments: all of them arrive preloaded in SGPRs where the
+  // code object asks for kernel-argument preloading, so the first address
+  // computations wait on no scalar load)
   constexpr int NTHR = 64 * WAVES;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -182,14 +184,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
   const int g0 = slice * gps;
   const int g1 = min(G, g0 + gps);
   const int Gs = g1 > g0 ? g1 - g0 : 0;        // groups per row in this slice
-  // the workgroup owns a contiguous, balanced range of row blocks; its waves
+  // the workgroup owns a contiguous, balanced range of row blocks (bper or,
+  // for the first brem workgroups, bper + 1; computed on the host); its waves
   // take them in turn (block b_lo + wq + WAVES * j)
-  // (the first nblk % grid workgroups take one block more)
-  const int nblk = (N + R - 1) / R;
-  const int bper = nblk / (int)gridDim.x, brem = nblk - bper * (int)gridDim.x;
   const int b_lo = (int)blockIdx.x * bper + min((int)blockIdx.x, brem);
-  const int b_hi = b_lo + bper + ((int)blockIdx.x < brem ? 1 : 0);
-  const int nb = wq < b_hi - b_lo ? (b_hi - b_lo - 1 - wq) / WAVES + 1 : 0;
+  const int nbw = bper + ((int)blockIdx.x < brem ? 1 : 0);
+  const int nb = wq < nbw ? (nbw - 1 - wq) / WAVES + 1 : 0;
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint32_t)((uint64_t)N * (uint32_t)K / 2u));
@@ -212,37 +212,41 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
   // the wave's x requests go out ahead of its first weight request
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- static per-lane mapping (identical for every block)
+  // ---- per-lane offsets of a block's loads (the same for every block; block
+  // b adds b * R rows). Lane (m, kb) of instruction i reads sub-chunk kb of
+  // block-group gi = 16 i + m, i.e. row gi / Gs, slice group gi % Gs. When the
+  // slice is the whole row (no split) the block is one contiguous run and
+  // block-group gi sits at 64 gi: a few instructions get the first request
+  // out; a slice needs the row / group split (by compares: R <= 4).
   const int m = lane & 15, kb = lane >> 4;
-  uint32_t woff[I], soff[I], xaddr[I], sshift[I];
-  float rmask[I][R];
-#pragma unroll
-  for (int i = 0; i < I; ++i) {
-    const int gi = 16 * i + m;                 // block-group of this lane's A row / B column
-    const bool ok = gi < R * Gs;
-    // row r and slice group gin of the block-group (by compares: R <= 4)
-    int r = 0, gin = gi;
+  auto block_group = [&](int gi, int& r, int& gin) {
+    r = 0;
+    gin = gi;
 #pragma unroll
     for (int rr = 1; rr < R; ++rr)
       if (gin >= Gs) { gin -= Gs; ++r; }
-    if (!ok) r = gin = 0;
-    // invalid lanes read past the extent (zeros); their products are masked by rmask
-    woff[i] = ok ? (uint32_t)r * rowb + (uint32_t)(g0 + gin) * 64u + (uint32_t)kb * 16u : 0xFFFFFFF0u;
-    soff[i] = ok ? ((uint32_t)r * (uint32_t)G + (uint32_t)(g0 + gin)) * 2u : 0xFFFFFFF0u;
-    // scales are read as the aligned 32-bit word that holds them (16-bit
-    // loads get packed in pairs by the compiler, which ties the wait of one
-    // block to the next one's loads); in block 0 the lane's scale is the low
-    // half (shift 16 into the bf16 position) when its offset is 4-aligned
-    sshift[i] = (soff[i] & 2u) ? 0u : 16u;
-    // LDS byte address of piece (gin, kb, j = 0); piece j is at xaddr ^ (16 j)
-    xaddr[i] = (uint32_t)gin * 256u + 16u * ((uint32_t)(4 * kb) ^ (uint32_t)(gin & 15));
+  };
+  uint32_t woff[I], soff[I];
+  if (Gs == G) {
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) rmask[i][rr] = (ok && r == rr) ? 1.0f : 0.0f;
+    for (int i = 0; i < I; ++i) {
+      const uint32_t gi = (uint32_t)(16 * i + m);
+      const bool ok = gi < (uint32_t)(R * G);
+      woff[i] = ok ? gi * 64u + (uint32_t)kb * 16u : 0xFFFFFFF0u;
+      soff[i] = ok ? gi * 2u : 0xFFFFFFF0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      const int gi = 16 * i + m;
+      const bool ok = gi < R * Gs;
+      int r, gin;
+      block_group(gi, r, gin);
+      // invalid lanes read past the extent (zeros); their products are masked by rmask
+      woff[i] = ok ? (uint32_t)r * rowb + (uint32_t)(g0 + gin) * 64u + (uint32_t)kb * 16u : 0xFFFFFFF0u;
+      soff[i] = ok ? ((uint32_t)r * (uint32_t)G + (uint32_t)(g0 + gin)) * 2u : 0xFFFFFFF0u;
+    }
   }
-  // one-hot of the diagonal register: lane (n + 16 q) holds D[4q + j][n]
-  float onehot[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) onehot[j] = (m == 4 * kb + j) ? 1.0f : 0.0f;
 
   // ---- weight ring. Every slot is refilled after it is consumed, also past
   // the wave's last block: such loads (and those of rows past N) use an
@@ -267,6 +271,31 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
   };
 #pragma unroll
   for (int jb = 0; jb < D; ++jb) issue(wbuf[jb], sbuf[jb], jb);
+
+  // ---- the rest of the per-lane mapping, needed only when a block is consumed
+  uint32_t xaddr[I], sshift[I];
+  float rmask[I][R];
+#pragma unroll
+  for (int i = 0; i < I; ++i) {
+    const int gi = 16 * i + m;
+    const bool ok = gi < R * Gs;
+    int r, gin;
+    block_group(gi, r, gin);
+    if (!ok) r = gin = 0;
+    // scales are read as the aligned 32-bit word that holds them (16-bit
+    // loads get packed in pairs by the compiler, which ties the wait of one
+    // block to the next one's loads); in block 0 the lane's scale is the low
+    // half (shift 16 into the bf16 position) when its offset is 4-aligned
+    sshift[i] = (soff[i] & 2u) ? 0u : 16u;
+    // LDS byte address of piece (gin, kb, j = 0); piece j is at xaddr ^ (16 j)
+    xaddr[i] = (uint32_t)gin * 256u + 16u * ((uint32_t)(4 * kb) ^ (uint32_t)(gin & 15));
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) rmask[i][rr] = (ok && r == rr) ? 1.0f : 0.0f;
+  }
+  // one-hot of the diagonal register: lane (n + 16 q) holds D[4q + j][n]
+  float onehot[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) onehot[j] = (m == 4 * kb + j) ? 1.0f : 0.0f;
 
   // ---- prepare x in LDS: pair-interleave, swizzle, per-group -136 * sum
   for (int e = tid; e < 16 * I; e += NTHR) clds[e] = 0.0f;
@@ -396,12 +425,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
     }
     wave_reduce_rows<R>(acc);
     if (lane == 63 && jb < nb) {
+      // one slice: bf16 y; several: fp32 partials of this slice
+      const bool partials = gridDim.y > 1;
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
         const int n = (b_lo + wq + jb * WAVES) * R + rr;
         if (n < N) {
-          if (ws == nullptr) y[n] = to_bf16(acc[rr]);
-          else ws[(size_t)slice * N + n] = acc[rr];
+          if (!partials) static_cast<uint16_t*>(out)[n] = to_bf16(acc[rr]);
+          else static_cast<float*>(out)[(size_t)slice * N + n] = acc[rr];
         }
       }
     }
@@ -446,8 +477,10 @@ static hipError_t launch_mfma_ri(const uint16_t* x, const uint8_t* w, const uint
   constexpr int kWaves = 8;
   const int nblk = (N + R - 1) / R;
   const int gx = std::max(1, std::min(cu_count(), (nblk + kWaves - 1) / kWaves));
+  const int bper = nblk / gx, brem = nblk - bper * gx;
+  void* out = sk > 1 ? static_cast<void*>(ws) : static_cast<void*>(y);
   hipLaunchKernelGGL((gemv_mfma_kernel<R, I, 1, kWaves, false>), dim3(gx, sk), dim3(64 * kWaves), 0, stream, x, w,
-                     s, y, ws, N, K, gps);
+                     s, out, N, K, gps, bper, brem);
   return hipGetLastError();
 }
 

@@ -71,6 +71,14 @@ GEMV_CASES = [
     (1001, 896, 2, None),     # N * G odd: the last scale is the low half of a word
                               #   that ends past the tensor (4 + 3 groups per slice)
     (40, 10240, 2, None),     # with split-K: 40 groups per slice
+    # blocks per workgroup not a multiple of the 8 waves: the leftover blocks'
+    # instructions are dealt to all waves (rem = 7, 7 with q = 0, 1, 0 .. 7)
+    (7680, 5120, 1, None),    # 15 two-row blocks per workgroup: 1 full step + 7 leftover blocks
+    (7680, 5120, 2, None),    # 20 groups per slice: 4-row blocks, 7 per workgroup, all leftover
+    (12310, 5120, 1, None),   # 24 or 25 blocks per workgroup (rem 0 or 1)
+    (6000, 8192, 1, None),    # 1-row blocks of 64 groups (I = 4), rem varies
+    (8192, 3584, 1, None),    # 28 groups: 4-row blocks of 7 instructions (one leftover per step)
+    (8200, 3584, 1, None),
     # the half-wave layout forced
     (17408, 5120, 1, 1),
     (1000, 1280, 1, 1),
