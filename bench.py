@@ -365,7 +365,11 @@ def bench_dispatch(N, K, Ms, steps=20):
         if M == 1:
             cands += [("gemv", w4.PATH_GEMV, None, sk) for sk in (1, 2, 4)]
         if M <= 48:
-            cands += [("small-batch", w4.PATH_SKINNY, None, sk) for sk in (1, 2, 4, 8)]
+            for tiles in ((1, 2) if M <= 32 else (1,)):
+                cands += [(f"small-batch{tiles}", w4.PATH_SKINNY, tiles, sk) for sk in (1, 2, 4, 8)]
+        if M <= 16:   # the LDS-staged small-batch kernel, stage geometries 0 and 3
+            for var in (3, 6):
+                cands += [(f"small-batch-lds{var - 3}", w4.PATH_SKINNY, var, sk) for sk in (1, 2, 4, 8)]
         if M > 1:
             for rows in (48, 64, 80, 96, 112, 128, 144):
                 for sk in ((1, 2, 4, 8) if M < 1024 else (1, 2)):

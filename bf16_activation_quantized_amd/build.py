@@ -20,13 +20,14 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
 
-SOURCES = ["api.cpp", "pack_reduce.hip", "gemv.hip", "skinny.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "pack_reduce.hip", "gemv.hip", "skinny.hip", "skinny_lds.hip", "prefill.hip"]
 # MFMA accumulators that the VALU reads (diagonal extraction, per-group
 # rescale) stay in VGPRs (the default heuristic moved them through AGPRs with
 # extra copies); the decode GEMV's kernel arguments arrive preloaded in SGPRs
 # (its first weight request waits on no scalar load)
 EXTRA_FLAGS = {"gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=13"],
-               "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+               "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "skinny_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 

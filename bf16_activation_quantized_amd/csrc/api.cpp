@@ -50,11 +50,19 @@ int device_cus() {
   return v;
 }
 
-// Small batch: one column tile of 16 per wave up to 8 rows and past 32, two
-// between (8 waves per workgroup; at 17408 x 5120 and 8192 x 8192, rotated
-// weights: M = 2-4 7-10 % faster with one tile, M >= 9 4-12 % faster with
-// two; past 32 rows the three row tiles leave registers for one only).
-int skinny_default_tiles(int64_t M) { return M <= 8 || M > 32 ? 1 : 2; }
+// Small batch: the register-streaming kernel with one column tile of 16 per
+// wave up to 8 rows and past 32, two between (8 waves per workgroup; at
+// 17408 x 5120 and 8192 x 8192: M = 2-4 7-10 % faster with one tile, M >= 9
+// 4-12 % faster with two; past 32 rows the three row tiles leave registers
+// for one only). At 9-16 rows the LDS-staged kernel (variant 6: stages of 4
+// groups, 4 in flight) instead: over N x K = 8192 x 8192, 17408 x 5120,
+// 7168 x 8192, 4096 x 4096, 2560 x 9728, 2048 x 5120 and 896 x 5120 it ran
+// 2-18 % faster at M = 16; at M = 8 it lost at four of the seven, at M <= 4
+// at five, by up to 33 % (its X stage is read in full whatever M is).
+int skinny_default_tiles(int64_t M) {
+  if (M > 8 && M <= 16) return 6;
+  return M <= 8 || M > 32 ? 1 : 2;
+}
 constexpr int kSkinnyWaves = 8;
 
 Path auto_path(int64_t M, int64_t N, int64_t K, int32_t sk) {
@@ -183,13 +191,17 @@ int32_t auto_split(Path path, int64_t M, int64_t N, int64_t K, int bm, int nt) {
       sk = pow2_at_least(ceil_div(Gk, 64));
       break;
     case kPathSkinny: {
-      // split only while fewer than half of the compute units have a
-      // workgroup: the reduce kernel and the partials cost more than the
-      // shorter slices save once the grid is half full (4096 x 4096, 128
-      // workgroups: SK 1 8-16 % faster than 2; 2560 x 9728, 80 workgroups:
-      // SK 2 20 % faster than 4), every wave keeping at least one group
-      const int64_t wgs = ceil_div(N, 16 * (int64_t)nt);
-      while (sk < 16 && wgs * sk < device_cus() / 2 && ceil_div(Gk, (int64_t)sk * 2) >= kSkinnyWaves) sk <<= 1;
+      // split only when fewer than half of the compute units have a
+      // workgroup, and then as far as one round of workgroups goes: the
+      // reduce kernel and the partials cost more than the shorter slices save
+      // once the grid is half full (4096 x 4096, 128 workgroups: SK 1 8-16 %
+      // faster than 2), while a grid a quarter full or less gains from
+      // filling the GPU (M = 16 at 2048 x 5120, 64 workgroups: SK 4 9.3 us,
+      // SK 2 10.3; at 896 x 5120, 28 workgroups: SK 8 8.7, SK 4 9.1;
+      // 2560 x 9728, 80 workgroups: SK 2 20 % faster than 4)
+      const int64_t wgs = ceil_div(N, 16 * (int64_t)nt), cus = device_cus();
+      if (2 * wgs < cus)
+        while (sk < 16 && 2 * sk <= Gk && wgs * sk * 2 <= cus) sk <<= 1;
       break;
     }
     case kPathTile:
@@ -247,8 +259,9 @@ w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w
       break;
     case kPathSkinny:
       if (variant <= 0) variant = skinny_default_tiles(M);
-      // past 32 rows (three row tiles) one column tile per wave only
-      if (variant > 2 || (M > 32 && variant != 1)) return W4A16_ERR_SHAPE;
+      // past 32 rows (three row tiles) one column tile per wave only; variants
+      // 3..6: the LDS-staged kernel (M <= 16), stage geometries 0..3
+      if (variant > 6 || (M > 32 && variant != 1) || (variant >= 3 && M > 16)) return W4A16_ERR_SHAPE;
       break;
     case kPathTile:
       if (variant <= 0) variant = default_tile_rows(M, N, K, split_k, gs);
@@ -259,7 +272,7 @@ w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w
     default:
       return W4A16_ERR_SHAPE;
   }
-  int32_t sk = split_k > 0 ? split_k : auto_split(path, M, N, K, variant, variant);
+  int32_t sk = split_k > 0 ? split_k : auto_split(path, M, N, K, variant, variant >= 3 ? 2 : variant);
   if (sk > Gk && split_k == 0) sk = 1;
   if (path == kPathGemv && ceil_div(Gk, sk) > 64) {
     if (split_k != 0) return W4A16_ERR_SPLIT_K;   // explicit split too small for the GEMV path
@@ -333,7 +346,11 @@ w4a16_status launch_plan(const Plan& p, const uint16_t* x, const uint8_t* w, con
       e = w4a16::launch_gemv_m1(x, w, s, y, ws_split, iN, iK, p.gps, p.sk, p.variant == 1, strm);
       break;
     case kPathSkinny:
-      e = w4a16::launch_skinny(x, w, s, y, ws_split, iM, iN, iK, p.gps, p.sk, p.variant, kSkinnyWaves, strm);
+      if (p.variant >= 3 && w4a16::skinny_lds_fits(iM, p.gps))
+        e = w4a16::launch_skinny_lds(x, w, s, y, ws_split, iM, iN, iK, p.gps, p.sk, p.variant - 3, strm);
+      else
+        e = w4a16::launch_skinny(x, w, s, y, ws_split, iM, iN, iK, p.gps, p.sk, p.variant >= 3 ? 1 : p.variant,
+                                 kSkinnyWaves, strm);
       break;
     case kPathTile: {
       const int ld = (int)round_up((uint64_t)M, 4);

@@ -36,6 +36,11 @@ hipError_t launch_gemv_m1(const uint16_t* x, const uint8_t* w, const uint16_t* s
 hipError_t launch_skinny(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws,
                          int M, int N, int K, int gps, int sk, int nt, int waves, hipStream_t stream);
 
+// 1 <= M <= 16 decode with X and the weights staged in LDS by DMA (skinny_lds.hip)
+bool skinny_lds_fits(int M, int gps);
+hipError_t launch_skinny_lds(const uint16_t* x, const uint8_t* w, const uint16_t* s, uint16_t* y, float* ws, int M,
+                             int N, int K, int gps, int sk, int geometry, hipStream_t stream);
+
 // slices of at most this many groups stage their scales in LDS (16 NT x gps x 2
 // bytes, at most 32 KiB)
 constexpr int kSkinnyMaxScaleGroups = 256;

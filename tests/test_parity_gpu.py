@@ -137,7 +137,20 @@ SKINNY_CASES = [
     (47, 300, 40960, 1, 1),       # a slice too long to stage its scales in LDS
     (16, 8192, 8192, 0, None),    # small-batch decode workload, default split
     (9, 2048, 8192, 2, 2),
-]
+    # 3..6: X and the weights staged in LDS by DMA (3 stages of 8 groups; 6,
+    # 5, 4 stages of 4 groups)
+] + [case[:4] + (v,) for v in (3, 4, 5, 6) for case in (
+    (16, 8192, 8192, 1),          # the small-batch decode workload
+    (16, 8192, 8192, 4),
+    (1, 256, 512, 1),             # one partial stage
+    (3, 17, 384, 1),              # N tail inside the first column tile; 3 groups
+    (5, 100, 1280, 2),            # slices of 5 groups
+    (16, 513, 2048, 4),           # N tail of one column; empty groups in the last stage
+    (16, 100, 384, 16),           # more slices than groups: empty slices write zeros
+    (8, 1000, 5120, 1),           # 40 groups
+    (12, 777, 3584, 1),           # 28 groups (odd scale words: N * G even, n * G odd rows)
+    (16, 2049, 9728, 2),          # 76 groups over 2 slices
+)]
 
 
 @pytest.mark.parametrize("M,N,K,sk,variant", SKINNY_CASES)
@@ -415,6 +428,25 @@ def test_batched_full_size():
     yb = bits_host(y)
     for b in range(B):
         check_gate(yb[b], ref[b], f"batched problem {b}")
+
+
+# The automatic path, tile height and split choice at the shape sets of the
+# MI350X Triton page's Performance tables ("Add Triton BF16xINT4 rowwise GEMM
+# for ROCm gfx942/gfx950"): decode rows M = 1, 16, 64, 128 at N x K = 896 x
+# 5120, 2048 x 5120, 8192 x 3584, 7168 x 8192; prefill M = 2048, 4096 at
+# 8192 x 3584 and 7168 x 8192. Whole outputs against the oracle.
+AUTO_SHAPES = [(M, N, K) for N, K in ((896, 5120), (2048, 5120), (8192, 3584), (7168, 8192))
+               for M in (1, 16, 64, 128)] + \
+              [(M, N, K) for N, K in ((8192, 3584), (7168, 8192)) for M in (2048, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", AUTO_SHAPES)
+def test_auto_choice_page_shapes(M, N, K):
+    c = make_inputs(M, N, K, seed=M + N + K + 7)
+    d = DevCase(c)
+    y = nan_filled((M, N))
+    w4.w4a16_gemm(d.x, d.w, d.s, y=y)     # split_k 0, automatic path, the workspace it asks for
+    check_full(y, oracle.gemm(c.x, d.p_host, c.s), f"auto {M}x{N}x{K} (sk {w4.w4a16_gemm_auto_split_k(M, N, K)})")
 
 
 def _guarded_empty_call(call, n_cols):
