@@ -60,6 +60,20 @@ __device__ __forceinline__ void st16(uint16_t v, __amdgpu_buffer_rsrc_t r, uint3
   __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
 }
 
+// ---------------------------------------------------------------- LDS
+// XOR swizzle of the 16-byte chunks of an LDS operand row, by row & 15: the
+// row's low two bits, and its 4-row block j = (row >> 2) & 3 mapped to
+// 0, 2, 3, 1. Chunk c of row r sits in slot c ^ xswz(r) (within its aligned
+// run of 16 chunks). A wave's 16-byte MFMA fragment read, lane (m, kb) at row
+// m and chunk 4 kb + st (or kb + 4 st), then takes the 4 cycles of a
+// conflict-free read on gfx950 by the LDS bank-conflict counter, for rows of
+// any multiple of 256 B; XOR by row & 7 or by row & 15 measured 2-way
+// conflicts (8 cycles). The block map is a permutation whose XOR with the
+// identity is one too.
+__device__ __forceinline__ uint32_t xswz(int r) {
+  return (uint32_t)((r & 3) | ((r >> 1) & 4) | ((((r >> 2) ^ (r >> 3)) & 1) << 3));
+}
+
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }

@@ -29,9 +29,10 @@
 //  * within a group the MFMA k order is permuted: lane (r, kb) of step st
 //    holds k = 32 kb + 8 st + 0..7 for both operands, so one lane's four steps
 //    of packed weights are one 16-byte LDS read;
-//  * LDS rows are XOR-swizzled in 16-byte chunks (X by row & 7, weights by
-//    (row >> 1) & 3): the DMA lanes fetch the chunk that belongs at their LDS
-//    slot, and the MFMA operand reads avoid bank conflicts;
+//  * LDS rows are XOR-swizzled in 16-byte chunks (X rows by xswz(row & 15),
+//    weights by (row >> 1) & 3): the DMA lanes fetch the chunk that belongs
+//    at their LDS slot, and the MFMA operand reads are free of bank
+//    conflicts (4 LDS cycles per 16-byte read of a wave; see xswz);
 //  * one barrier per group, after an explicit wait for the next group's DMA.
 // The M tail and N tail read zeros through the exact buffer extents; stores
 // past the last row are dropped and columns >= N are skipped.
@@ -145,13 +146,13 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   // ---- DMA lane offsets (constant over groups)
   // X instruction i of wave wv fills LDS block q = wv + 8 i (if q < 4 MS),
   // i.e. tile rows 4 q + (lane >> 4), slot lane & 15; the chunk stored in
-  // slot p of row r is p ^ (r & 7), and r & 7 = 4 (q & 1) + (lane >> 4): row
-  // offset 4 (q & ~1) KB plus xvo[q & 1].
+  // slot p of row r is p ^ xswz(r & 15), and r & 15 = 4 (q & 3) + (lane >> 4)
+  // with q & 3 = wv & 3 for every i: row offset 4 (q & ~3) KB plus xvo().
   // (recomputed from the lane id at each issue: a few VALU ops per group
   // instead of registers held across the main loop)
-  auto xvo = [&](int e) {
-    const int xr = lane >> 4, xp = lane & 15;
-    return (uint32_t)(4 * e + xr) * KB + 16u * (uint32_t)(xp ^ (4 * e + xr));
+  auto xvo = [&]() {
+    const int r = 4 * (wv & 3) + (lane >> 4), xp = lane & 15;
+    return (uint32_t)r * KB + 16u * ((uint32_t)xp ^ xswz(r));
   };
   // W instruction i fills block q = QW wv + i: tile rows 16 q + (lane >> 2),
   // slot lane & 3; the chunk stored in slot p of row r is p ^ ((r >> 1) & 3).
@@ -169,12 +170,11 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     // a waterfall loop around each load
     const uint32_t gx = __builtin_amdgcn_readfirstlane((uint32_t)g * 256u);
     const uint32_t gw = __builtin_amdgcn_readfirstlane((uint32_t)g * 64u);
-    const uint32_t xo0 = xvo(0), xo1 = xvo(1);
+    const uint32_t xo = xvo();
 #pragma unroll
     for (int i = 0; i < QX; ++i) {
       const int q = wv + kNW * i;   // wave-uniform
-      if (NQX % kNW == 0 || q < NQX)
-        dma16(rx, base + 1024 * q, ((q & 1) ? xo1 : xo0) + (uint32_t)(4 * (q & ~1)) * KB, gx);
+      if (NQX % kNW == 0 || q < NQX) dma16(rx, base + 1024 * q, xo + (uint32_t)(4 * (q & ~3)) * KB, gx);
     }
     const uint32_t wo = wvo();
 #pragma unroll
@@ -213,9 +213,9 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   };
 
   // ---- LDS operand offsets within a stage
-  // A (X): row 16 ms + m16, logical chunk 4 kb + st, slot chunk ^ (row & 7)
-  // (4 kb + st) ^ (m16 & 7) = ((4 kb) ^ (m16 & 7)) ^ st: one base register
-  const uint32_t aoff0 = (uint32_t)m16 * 256u + 16u * (uint32_t)((4 * kb) ^ (m16 & 7));
+  // A (X): row 16 ms + m16, logical chunk 4 kb + st, slot chunk ^ xswz(m16)
+  // (4 kb + st) ^ x = ((4 kb) ^ x) ^ st: one base register
+  const uint32_t aoff0 = (uint32_t)m16 * 256u + 16u * ((uint32_t)(4 * kb) ^ xswz(m16));
   // B (packed W): row TN wv + 16 ns + m16, logical chunk kb
   const uint32_t boff = ST::kX + (uint32_t)(TN * wv + m16) * 64u + 16u * (uint32_t)(kb ^ ((m16 >> 1) & 3));
   // C init: -136 * row sums of rows 16 ms + 4 kb + 0..3
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   SW sc_cur[SN], sc_nxt[SN];
 
   // GS = 32 operand offsets (natural k order, see below)
-  const uint32_t aoffN = (uint32_t)m16 * 256u + 16u * (uint32_t)(kb ^ (m16 & 7));
+  const uint32_t aoffN = (uint32_t)m16 * 256u + 16u * ((uint32_t)kb ^ xswz(m16));
   const uint32_t boffN = ST::kX + (uint32_t)(TN * wv + m16) * 64u + 4u * (uint32_t)kb + 16u * (uint32_t)((m16 >> 1) & 3);
   // ---- -136 * row sums of a landed stage, on the matrix core: MFMA steps of
   // the X fragments against a constant bf16(-136) operand give D[m][n] =
@@ -290,8 +290,8 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   // GS = 32: MFMA step st covers scale group st of the stage (natural k
   // order: lane (r, kb) of step st holds k = 32 st + 8 kb + 0..7 for both
   // operands), each step starts from its group's row sums and is rescaled on
-  // its own. A: chunk 4 st + kb of the row, slot (4 st + kb) ^ (row & 7) =
-  // ((kb ^ (row & 7)) ^ 4 st); B: dword kb of chunk st of the packed row, slot
+  // its own. A: chunk 4 st + kb of the row, slot (4 st + kb) ^ xswz(row) =
+  // ((kb ^ xswz(row)) ^ 4 st); B: dword kb of chunk st of the packed row, slot
   // st ^ ((row >> 1) & 3).
   auto compute32 = [&](int stage, int rstage, int j) {
     if constexpr (GS == 32) {

@@ -15,8 +15,8 @@
 //    layout of skinny.hip re-reads X per wave and group and reads 16 weight
 //    rows x 64 B per instruction);
 //  * 16-byte chunks are XOR-swizzled by row (chunk c of row r in slot
-//    c ^ (r & 15)) so that the MFMA operand reads of 16 rows hit all 64 banks;
-//    the DMA lanes fetch the chunk that belongs in their slot;
+//    c ^ xswz(r & 15)) so that the MFMA operand reads of 16 rows are free of
+//    bank conflicts; the DMA lanes fetch the chunk that belongs in their slot;
 //  * per stage the 2 column tiles x 8 groups are 16 units, two per wave; a
 //    unit is one group of one column tile: 4 MFMA steps whose k order is
 //    permuted alike on both sides (lane (r, kb) of step st holds k = 32 kb +
@@ -96,6 +96,7 @@ __global__ __launch_bounds__(64 * kSLWaves) void skinny_lds_kernel(const uint16_
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m16 = lane & 15, kb = lane >> 4;
+  const uint32_t xs = xswz(m16);   // this lane's row swizzle in both operands
   const int G = K / kGroup;
   const int slice = blockIdx.y;
   const int gb = slice * gps;
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(64 * kSLWaves) void skinny_lds_kernel(const uint16_
       const int q = wv + kSLWaves * i;
       const int row = q / (SG / 4), h = q % (SG / 4);
       const int slot = 64 * h + lane;
-      const int c = slot ^ row;                 // chunk held by this slot
+      const int c = slot ^ (int)xswz(row);      // chunk held by this slot
       const int g = glo + (c >> 4);
       const uint32_t off = g < ge ? (uint32_t)row * KB + (uint32_t)g * 256u + 16u * (uint32_t)(c & 15) : 0xFFFFFFF0u;
       sl_dma16(rx, base + row * (SG * 256) + h * 1024, off);
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(64 * kSLWaves) void skinny_lds_kernel(const uint16_
     for (int i = 0; i < ST::kWI; ++i) {
       const int q = wv + kSLWaves * i;
       const int row = (16 / SG) * q + lane / (4 * SG);
-      const int c = (lane % (4 * SG)) ^ (row & 15);
+      const int c = (lane % (4 * SG)) ^ (int)xswz(row);
       const int g = glo + (c >> 2);
       const uint32_t off = g < ge ? (uint32_t)row * K2 + (uint32_t)g * 64u + 16u * (uint32_t)(c & 3) : 0xFFFFFFF0u;
       sl_dma16(rw, base + ST::kX + q * 1024, off);
@@ -162,9 +163,9 @@ __global__ __launch_bounds__(64 * kSLWaves) void skinny_lds_kernel(const uint16_
     bf16x8 a[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st)
-      a[st] = *reinterpret_cast<const bf16x8*>(sb + m16 * (SG * 256) + 16 * ((16 * gl + 4 * kb + st) ^ m16));
+      a[st] = *reinterpret_cast<const bf16x8*>(sb + m16 * (SG * 256) + 16 * ((16 * gl + 4 * kb + st) ^ xs));
     const int r = 16 * ct + m16;
-    const u32x4 pk = *reinterpret_cast<const u32x4*>(sb + ST::kX + r * (SG * 64) + 16 * ((4 * gl + kb) ^ m16));
+    const u32x4 pk = *reinterpret_cast<const u32x4*>(sb + ST::kX + r * (SG * 64) + 16 * ((4 * gl + kb) ^ xs));
     const uint32_t sw = *reinterpret_cast<const uint32_t*>(sb + ST::kX + ST::kW + 4 * (r * SG + gl));
     const float sc = __uint_as_float((((uint32_t)(n0 + r) * (uint32_t)G + (uint32_t)g) & 1u) ? (sw & 0xFFFF0000u)
                                                                                                : (sw << 16));
