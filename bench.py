@@ -341,10 +341,13 @@ def bench_pack(steps, warmup):
 
 
 def bench_dispatch(N, K, Ms, steps=20):
-    """Path / tile height / split-K selection over M at one N x K: the
-    automatic choice (split_k=0, no path) against every explicit one, each
-    graph-timed over `steps` calls with rotated weight copies. One JSON line
-    per M: auto time, the best explicit (name, SK, time) and their ratio."""
+    """Path / tile height / split-K selection over M at one N x K: every
+    explicit choice and the automatic one (split_k=0, no path), each
+    graph-timed over `steps` calls with rotated weight copies, in two passes
+    (forward, then reverse order, so that the drift of the clocks under load
+    favours no candidate; the faster pass counts). One JSON line per M: the
+    automatic choice (path, variant, SK) and its time, the best explicit
+    choice and their ratio."""
     import torch
     import bf16_activation_quantized_amd as w4
     g = torch.Generator(device="cuda")
@@ -357,49 +360,56 @@ def bench_dispatch(N, K, Ms, steps=20):
     copies = max(1, math.ceil(ROTATE_BYTES / wb))
     ws_ = [w] + [w.clone() for _ in range(copies - 1)]
     ss_ = [s] + [s.clone() for _ in range(copies - 1)]
+    names = {w4.PATH_GEMV: "gemv", w4.PATH_SKINNY: "small-batch", w4.PATH_TILE: "tile"}
+    sks = (1, 2, 4, 8, 16)
     out = []
     for M in Ms:
         x = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
         y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
         cands = [("auto", None, None, 0)]
         if M == 1:
-            cands += [("gemv", w4.PATH_GEMV, None, sk) for sk in (1, 2, 4)]
+            cands += [("gemv", w4.PATH_GEMV, 0, sk) for sk in sks]
         if M <= 48:
             for tiles in ((1, 2) if M <= 32 else (1,)):
-                cands += [(f"small-batch{tiles}", w4.PATH_SKINNY, tiles, sk) for sk in (1, 2, 4, 8)]
+                cands += [(f"small-batch{tiles}", w4.PATH_SKINNY, tiles, sk) for sk in sks]
         if M <= 16:   # the LDS-staged small-batch kernel, stage geometries 0 and 3
             for var in (3, 6):
-                cands += [(f"small-batch-lds{var - 3}", w4.PATH_SKINNY, var, sk) for sk in (1, 2, 4, 8)]
+                cands += [(f"small-batch-lds{var - 3}", w4.PATH_SKINNY, var, sk) for sk in sks]
         if M > 1:
             for rows in (48, 64, 80, 96, 112, 128, 144):
-                for sk in ((1, 2, 4, 8) if M < 1024 else (1, 2)):
+                for sk in (sks if M < 1024 else (1, 2)):
                     cands.append((f"tile{rows}", w4.PATH_TILE, rows, sk))
-        res = []
-        for name, path, var, sk in cands:
-            need = w4.w4a16_gemm_workspace_bytes(M, N, K, sk, path=path, variant=var)
-            wsp = torch.empty(max(need // 4, 1) + 4, dtype=torch.float32, device="cuda")
+        apath, avar, ask = w4.w4a16_gemm_auto_config(M, N, K)
+        times = {}
+        for order in (cands, cands[::-1]):
+            for name, path, var, sk in order:
+                need = w4.w4a16_gemm_workspace_bytes(M, N, K, sk, path=path, variant=var)
+                wsp = torch.empty(max(need // 4, 1) + 4, dtype=torch.float32, device="cuda")
 
-            def step(i, path=path, var=var, sk=sk, wsp=wsp):
-                w4.w4a16_gemm(x, ws_[i % copies], ss_[i % copies], y=y, split_k=sk, workspace=wsp,
-                              path=path, variant=var)
-            try:
-                _, t, _ = time_steps(step, steps, 3)
-                res.append((t * 1e6, name, sk))
-            except RuntimeError as e:   # a combination the library refuses
-                log(f"dispatch M={M} {name} sk={sk}: {e}")
-            del wsp
-        # the automatic choice again, last (the first timing of a sweep can
-        # run before the GPU clocks have settled): the better of its two runs
-        def step_auto(i):
-            w4.w4a16_gemm(x, ws_[i % copies], ss_[i % copies], y=y, split_k=0, workspace=wsp_auto)
-        wsp_auto = torch.empty(max(w4.w4a16_gemm_workspace_bytes(M, N, K, 0) // 4, 1) + 4, dtype=torch.float32,
-                               device="cuda")
-        _, t, _ = time_steps(step_auto, steps, 3)
-        auto = min(res[0], (t * 1e6, "auto", 0))
-        best = min(res[1:] or res)
-        r = dict(N=N, K=K, M=M, auto_us=round(auto[0], 2), best=[best[1], best[2], round(best[0], 2)],
-                 auto_vs_best=round(auto[0] / best[0], 3), auto_sk=w4.w4a16_gemm_auto_split_k(M, N, K),
-                 auto_tflops=round(2.0 * M * N * K / auto[0] / 1e6, 1), auto_gbs=round(wb / auto[0] / 1e3, 1))
+                def step(i, path=path, var=var, sk=sk, wsp=wsp):
+                    w4.w4a16_gemm(x, ws_[i % copies], ss_[i % copies], y=y, split_k=sk, workspace=wsp,
+                                  path=path, variant=var)
+                try:
+                    _, t, _ = time_steps(step, steps, 3)
+                    key = (name, var, sk)
+                    times[key] = min(times.get(key, float("inf")), t * 1e6)
+                except RuntimeError as e:   # a combination the library refuses
+                    if order is cands:
+                        log(f"dispatch M={M} {name} sk={sk}: {e}")
+                del wsp
+        auto_us = times[("auto", None, 0)]
+        explicit = {k: v for k, v in times.items() if k[0] != "auto"}
+        best = min(explicit.items(), key=lambda kv: kv[1])
+        aname = f"{names[apath]}{'' if apath != w4.PATH_SKINNY else ('-lds' + str(avar - 3) if avar >= 3 else avar)}"
+        if apath == w4.PATH_TILE:
+            aname += str(avar)
+        twin = [v for (n, var, sk), v in explicit.items()
+                if sk == ask and var == avar and n.startswith(names[apath])]
+        r = dict(N=N, K=K, M=M, auto=[aname, ask], auto_us=round(auto_us, 2),
+                 auto_explicit_us=round(twin[0], 2) if twin else None,
+                 best=[best[0][0], best[0][2], round(best[1], 2)], auto_vs_best=round(auto_us / best[1], 3),
+                 auto_tflops=round(2.0 * M * N * K / auto_us / 1e6, 1), auto_gbs=round(wb / auto_us / 1e3, 1),
+                 candidates=len(explicit))
         print(json.dumps(r), flush=True)
         out.append(r)
         del x, y

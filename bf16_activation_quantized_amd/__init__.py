@@ -67,6 +67,7 @@ def _lib():
         "w4a16_splitk_reduce": (ctypes.c_int, [P, P, I32, I64, I64, P]),
         "w4a16_gemm_noalloc": (ctypes.c_int, [P, P, P, P, I64, I64, I64, I32, I32, P]),
         # internal entry points that force a kernel (tests, benchmarks)
+        "w4a16_gemm_auto_config": (ctypes.c_int, [I64, I64, I64, I32, P, P]),
         "w4a16_gemm_workspace_bytes_ex": (SZ, [I64, I64, I64, I32, I32, P]),
         "w4a16_gemm_ex": (ctypes.c_int, [P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P, P]),
         "w4a16_gemm_grouped_ex": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I64, I32, P, P]),
@@ -148,6 +149,15 @@ def w4a16_pack_int4(q: torch.Tensor, out: Optional[torch.Tensor] = None, stream=
 
 def w4a16_gemm_auto_split_k(M: int, N: int, K: int, group_size: int = GROUP_SIZE) -> int:
     return int(_lib().w4a16_gemm_auto_split_k(M, N, K, group_size))
+
+
+def w4a16_gemm_auto_config(M: int, N: int, K: int, group_size: int = GROUP_SIZE) -> tuple:
+    """The automatic choice of w4a16_gemm at these sizes (internal entry
+    point): (path, variant, split_k); path 0 when nothing would run (M = 0)."""
+    cfg, sk = _Config(), ctypes.c_int32(0)
+    _raise(_lib().w4a16_gemm_auto_config(M, N, K, group_size, ctypes.byref(cfg), ctypes.byref(sk)),
+           "w4a16_gemm_auto_config")
+    return int(cfg.path), int(cfg.variant), int(sk.value)
 
 
 def w4a16_gemm_workspace_bytes(M: int, N: int, K: int, split_k: int = 0,

@@ -256,6 +256,7 @@ w4a16_status make_plan(int64_t M, int64_t N, int64_t K, int32_t split_k, const w
   switch (path) {
     case kPathGemv:
       if (variant > 1) return W4A16_ERR_SHAPE;
+      if (variant < 0) variant = 0;   // the MFMA layout where it applies
       break;
     case kPathSkinny:
       if (variant <= 0) variant = skinny_default_tiles(M);
@@ -499,6 +500,23 @@ int32_t w4a16_gemm_auto_split_k(int64_t M, int64_t N, int64_t K, int32_t group_s
   Plan p;
   if (make_plan(M, N, K, 0, nullptr, group_size, &p) != W4A16_OK) return 0;
   return p.sk;
+}
+
+w4a16_status w4a16_gemm_auto_config(int64_t M, int64_t N, int64_t K, int32_t group_size, w4a16_config* cfg_out,
+                                    int32_t* split_k_out) {
+  if (cfg_out == nullptr || split_k_out == nullptr) return W4A16_ERR_NULL;
+  cfg_out->path = 0;
+  cfg_out->variant = -1;
+  *split_k_out = 0;
+  const w4a16_status st = check_dims(M, N, K, group_size);
+  if (st != W4A16_OK || M == 0) return st;
+  Plan p;
+  const w4a16_status sp = make_plan(M, N, K, 0, nullptr, group_size, &p);
+  if (sp != W4A16_OK) return sp;
+  cfg_out->path = (int32_t)p.path;
+  cfg_out->variant = p.variant;
+  *split_k_out = p.sk;
+  return W4A16_OK;
 }
 
 size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t split_k) {

@@ -26,7 +26,11 @@ extern "C" {
  *   variant: -1 = default for the path; otherwise
  *            path 1: 1 = the half-wave layout (the fallback for slice lengths
  *              with no MFMA tiling), 0 = the MFMA layout where it applies;
- *            path 2: column tiles of 16 per wave, 1 or 2 (1 only past 32 rows);
+ *            path 2: 1 or 2 = the register-streaming kernel with that many
+ *              column tiles of 16 per wave (1 only past 32 rows); 3 .. 6 =
+ *              the LDS-staged kernel (M <= 16) with stage geometry 0 .. 3
+ *              (groups per stage x stages in flight: 8 x 3, 4 x 6, 4 x 5,
+ *              4 x 4);
  *            path 3: rows per tile, 48 .. 144 in steps of 16 (80 .. 128 at
  *              group size 32).
  * An unavailable combination returns W4A16_ERR_SHAPE (W4A16_ERR_GROUP_SIZE
@@ -36,6 +40,13 @@ typedef struct {
   int32_t path;
   int32_t variant;
 } w4a16_config;
+
+/* The automatic choice of a plain GEMM (split_k = 0, no config): its path
+ * and variant (as above, variant resolved) and split-K. W4A16_OK, or the
+ * status the public call would return for these sizes (M = 0 gives
+ * W4A16_OK with path 0 and split-K 0: nothing would run). */
+w4a16_status w4a16_gemm_auto_config(int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                    w4a16_config* cfg_out, int32_t* split_k_out);
 
 size_t w4a16_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int32_t group_size,
                                      int32_t split_k, const w4a16_config* cfg);

@@ -203,6 +203,29 @@ def test_auto_split_rule():
     assert w4.w4a16_gemm_auto_split_k(1, 64, 100) == 0
 
 
+def test_auto_config_rule():
+    """The automatic path, variant and split at the documented regime
+    boundaries (256 compute units assumed on the host without a device)."""
+    ac = w4.w4a16_gemm_auto_config
+    assert ac(1, 17408, 5120) == (1, 0, 1)           # decode GEMV, MFMA layout, one slice
+    assert ac(16, 8192, 8192) == (2, 6, 1)           # 9-16 rows: LDS-staged small batch
+    assert ac(9, 8192, 8192)[:2] == (2, 6)
+    assert ac(8, 8192, 8192)[:2] == (2, 1)           # up to 8 rows: one column tile per wave
+    assert ac(24, 8192, 8192)[:2] == (2, 2)          # 17-32 rows: two column tiles per wave
+    assert ac(16, 896, 5120) == (2, 6, 8)            # 28 workgroups: split to fill the GPU
+    path, rows, sk = ac(1322, 19456, 2560)
+    assert (path, rows, sk) == (3, 144, 1)            # prefill: 144-row tiles, 3 rounds
+    assert ac(1322, 19456, 2560, 32)[0] == 3
+    assert ac(1, 256, 512, 32)[0] == 3               # group 32 always on the tile kernel
+    assert ac(0, 64, 128) == (0, -1, 0)              # nothing would run
+    with pytest.raises(RuntimeError):
+        ac(1, 64, 100)                               # K not a multiple of 128
+    for M in (1, 2, 16, 17, 48, 49, 100, 1322):
+        path, var, sk = ac(M, 4096, 4096)
+        assert path in (1, 2, 3) and sk in (1, 2, 4, 8, 16)
+        assert sk == w4.w4a16_gemm_auto_split_k(M, 4096, 4096)
+
+
 def test_workspace_sizes():
     # the split-K partials [SK, M, N] fp32 (rounded up to 256 bytes) when the
     # effective split is above 1; on the tile path with a wide N (at least 32
