@@ -39,6 +39,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROTATE_BYTES = 512 << 20
 # GPU work run back to back before the timed replay (clock settling)
 SETTLE_S = 0.1
+SETTLE_MAX_S = 1.0
 # the decode GEMV at M=1, N=17408, K=5120, split_k 1 (40 groups per slice ->
 # 2-row blocks, 5 instructions per block; one block in flight; one 8-wave
 # workgroup per compute unit, x in registers)
@@ -84,13 +85,15 @@ class Dev:
 def time_steps(step, steps, warmup, settle_s=SETTLE_S):
     """W untimed eager warmup steps; then the K steps are captured once in a
     HIP graph on a side stream (the library enqueues only kernels, so the
-    capture is exact) and replayed untimed until at least `settle_s` seconds
-    of GPU work have run back to back (however many replays that takes), so
-    that the clocks have left their idle state (under the decode GEMV's load
-    the shader clock climbs for tens of milliseconds); the timed region is
-    then one replay of exactly K steps, between HIP events on that stream,
-    behind two untimed replays, all bracketed by synchronisations. The
-    shader and memory clocks are sampled while the settling replays run.
+    capture is exact) and replayed untimed, in chunks of about 20 ms of GPU
+    work, until at least `settle_s` seconds have run back to back and the
+    shader clock has settled: it has reached 95 % of its highest DPM level,
+    or stopped rising from one chunk to the next (under the decode GEMV's
+    load it climbs from idle for a few hundred milliseconds; under prefill's
+    it sinks to a power-limited level), at most SETTLE_MAX_S. The timed
+    region is then one replay of exactly K steps, between HIP events on that
+    stream, behind two untimed replays, all bracketed by synchronisations.
+    The shader and memory clocks are sampled while the settling replays run.
     Returns (total seconds, seconds per step, clock record)."""
     import torch
     s = torch.cuda.Stream()
@@ -109,15 +112,41 @@ def time_steps(step, steps, warmup, settle_s=SETTLE_S):
         g.replay()
         torch.cuda.synchronize()
         one = max(time.perf_counter() - w0, 1e-6)
-        n = max(2, int(math.ceil(settle_s / one)))
+        chunk = max(1, int(math.ceil(0.02 / one)))
+        top = CLOCKS.top_sclk()
+
+        def queue():
+            for _ in range(chunk):
+                g.replay()
+            e = torch.cuda.Event()
+            e.record(s)
+            return e
+        # one chunk always queued behind the one being waited for, so that the
+        # GPU never idles between chunks
         t_settle = time.perf_counter()
-        for _ in range(n):
-            g.replay()
-        done = torch.cuda.Event()
-        done.record(s)
-        clocks = CLOCKS.sample_while(done)          # while the replays run
-        torch.cuda.synchronize()
+        pending = [queue(), queue()]
+        n, samples, prev = 2 * chunk, [], None
+        while True:
+            e = pending.pop(0)
+            rec = CLOCKS.sample_while(e)          # while the replays run
+            e.synchronize()
+            elapsed = time.perf_counter() - t_settle
+            last = rec.get("sclk_mhz_last") if rec else None
+            if rec and "sclk_mhz_first" in rec:
+                samples.append(rec)
+            if elapsed >= SETTLE_MAX_S or (elapsed >= settle_s and (
+                    last is None or (top and last >= 0.95 * top) or (prev is not None and last <= prev))):
+                break
+            prev = last
+            pending.append(queue())
+            n += chunk
         settled_s = time.perf_counter() - t_settle
+        clocks = None
+        if samples:
+            clocks = dict(sclk_mhz_settle_first=samples[0]["sclk_mhz_first"],
+                          sclk_mhz_median=samples[-1]["sclk_mhz_median"],
+                          sclk_mhz_last=samples[-1]["sclk_mhz_last"], sclk_mhz_top=top,
+                          sclk_samples=sum(r["sclk_samples"] for r in samples), mclk=samples[-1]["mclk"])
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         # two more untimed replays queued ahead of the first event keep the
@@ -175,6 +204,18 @@ class _Clocks:
             return None
         return dict(sclk=self._current(os.path.join(d, "pp_dpm_sclk")),
                     mclk=self._current(os.path.join(d, "pp_dpm_mclk")))
+
+    def top_sclk(self):
+        """The highest shader clock DPM level (MHz), or None."""
+        d = self._find()
+        if not d:
+            return None
+        try:
+            with open(os.path.join(d, "pp_dpm_sclk")) as f:
+                lv = [int(l.split(":", 1)[1].strip(" *\n").lower().replace("mhz", "")) for l in f if ":" in l]
+            return max(lv) if lv else None
+        except (OSError, ValueError):
+            return None
 
     def sample_while(self, event, every_s=0.01, most=40):
         """Samples every few milliseconds until `event` has completed (the
