@@ -53,6 +53,13 @@ struct SLStage {
 __device__ __forceinline__ void sl_dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, 0, 0, 0);
 }
+// the same with the non-temporal hint, for the weights: read once, streamed
+// past the caches (16 x 8192 x 8192: 12.36 -> 12.07 us; the tile kernel,
+// whose weight columns are re-read by other row tiles from L2, ran 3-17 %
+// slower with it)
+__device__ __forceinline__ void sl_dma16nt(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, 0, 0, 2);
+}
 __device__ __forceinline__ void sl_dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 4, voff, 0, 0, 0);
 }
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(64 * kSLWaves) void skinny_lds_kernel(const uint16_
       const int c = (lane % (4 * SG)) ^ (int)xswz(row);
       const int g = glo + (c >> 2);
       const uint32_t off = g < ge ? (uint32_t)row * K2 + (uint32_t)g * 64u + 16u * (uint32_t)(c & 3) : 0xFFFFFFF0u;
-      sl_dma16(rw, base + ST::kX + q * 1024, off);
+      sl_dma16nt(rw, base + ST::kX + q * 1024, off);
     }
     // scales: lane i of instruction t (waves t < SG / 2) fetches the word
     // holding the scale of column (64 t + i) / SG, group (64 t + i) % SG
