@@ -166,7 +166,7 @@ constexpr int kMaxChunks = 256;   // 32-k chunks per row-slice (64 groups)
 // (group g, sub-chunk kb, dword j) in the pair order of the dequant, slot
 // (4 kb + j) XOR-swizzled by (g & 15) so that the 16 lanes of a B read (16
 // consecutive groups, same slot) hit 16 different bank groups.
-template <int R, int I, int D, int WAVES, bool XLDS>
+template <int R, int I, int D, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* __restrict__ x,
                                                                const uint8_t* __restrict__ w,
                                                                const uint16_t* __restrict__ s,
@@ -330,28 +330,26 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
   const uint32_t magic = vgpr_const(kMagicPair);
   const uint32_t mask = __builtin_amdgcn_readfirstlane(vgpr_const(kNibblePairMask));
 
-  // x in registers (XLDS false): every lane reads its B operands and initial
-  // C once from LDS; the empty asm makes them opaque, so the compiler keeps
-  // them live across blocks instead of re-reading LDS per block
-  constexpr int IR = XLDS ? 1 : I;
-  u32x4 xr[IR][4];
-  f32x4 cr[IR];
-  if constexpr (!XLDS) {
+  // x in registers: every lane reads its B operands and initial C once from
+  // LDS; the empty asm makes them opaque, so the compiler keeps them live
+  // across blocks instead of re-reading LDS per block (x re-read from LDS per
+  // block ran 12.9 against 11.2 us)
+  u32x4 xr[I][4];
+  f32x4 cr[I];
 #pragma unroll
-    for (int i = 0; i < I; ++i) {
-      cr[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(clds) +
-                                              4u * (uint32_t)(16 * i + 4 * kb));
+  for (int i = 0; i < I; ++i) {
+    cr[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(clds) +
+                                            4u * (uint32_t)(16 * i + 4 * kb));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xr[i][j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(xlds) +
-                                                   (xaddr[i] ^ (16u * (uint32_t)j)));
-    }
+    for (int j = 0; j < 4; ++j)
+      xr[i][j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(xlds) +
+                                                 (xaddr[i] ^ (16u * (uint32_t)j)));
+  }
 #pragma unroll
-    for (int i = 0; i < I; ++i) {
-      asm volatile("" : "+v"(cr[i]));
+  for (int i = 0; i < I; ++i) {
+    asm volatile("" : "+v"(cr[i]));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(xr[i][j]));
-    }
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(xr[i][j]));
   }
 
   auto consume = [&](const u32x4 (&wb)[I], const uint32_t (&sb)[I], int jb) {
@@ -361,41 +359,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
     float acc[R];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) acc[rr] = 0.0f;
-    // x in LDS: an opaque copy of the base keeps the compiler from hoisting
-    // these block-invariant reads into ~20 * I registers
-    uint32_t xbase = 0;
-    if (XLDS) asm volatile("v_mov_b32 %0, 0" : "=v"(xbase));
-    // B operands (x) and initial C (-136 * sum(x) of block-groups 16 i + 4 q
-    // + 0..3, the rows of D in this lane) of instruction group i; with x in
-    // LDS, group i + 1's reads are issued before group i's MFMAs
-    bf16x8 bq[2][4];
-    f32x4 cq[2];
-    auto lds_operands = [&](int i, bf16x8 (&bb)[4], f32x4& cc) {
-      if constexpr (XLDS) {
-        cc = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(clds) + xbase +
-                                             4u * (uint32_t)(16 * i + 4 * kb));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bb[j] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(xlds) + xbase +
-                                                   (xaddr[i] ^ (16u * (uint32_t)j)));
-      } else {
-        cc = cr[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bb[j] = __builtin_bit_cast(bf16x8, xr[i][j]);
-      }
-    };
-    lds_operands(0, bq[0], cq[0]);
+    // instruction group i: B operands (x) and initial C (-136 * sum(x) of
+    // block-groups 16 i + 4 q + 0..3, the rows of D in this lane) from the
+    // registers above
 #pragma unroll
     for (int i = 0; i < I; ++i) {
-      if (i + 1 < I) {
-        lds_operands(i + 1, bq[(i + 1) & 1], cq[(i + 1) & 1]);
-        if (XLDS) __builtin_amdgcn_sched_barrier(0);
-      }
-      f32x4 c = cq[i & 1];
+      f32x4 c = cr[i];
+      bf16x8 bq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bq[j] = __builtin_bit_cast(bf16x8, xr[i][j]);
       const uint32_t wd[4] = {wb[i].x, wb[i].y, wb[i].z, wb[i].w};
-      if constexpr (WAVES <= 8) {
-        // two dwords per 64-bit shift where the register budget has room for
-        // the aligned pairs (up to 8 waves)
+      {
+        // two dwords per 64-bit shift
         uint32_t w4[4], w8[4], w12[4];
         shr64_pair<4>(wd[0], wd[1], w4[0], w4[1]);
         shr64_pair<4>(wd[2], wd[3], w4[2], w4[3]);
@@ -407,15 +382,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_mfma_kernel(const uint16_t* _
         for (int j = 0; j < 4; ++j) {
           const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{(wd[j] & mask) | magic, (w4[j] & mask) | magic,
                                                             (w8[j] & mask) | magic, (w12[j] & mask) | magic});
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[i & 1][j], c, 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w0 = wd[j], w1 = wd[j] >> 4, w2 = wd[j] >> 8, w3 = wd[j] >> 12;
-          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{(w0 & mask) | magic, (w1 & mask) | magic,
-                                                            (w2 & mask) | magic, (w3 & mask) | magic});
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[i & 1][j], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[j], c, 0, 0, 0);
         }
       }
       const float v = (c.x * onehot[0] + c.y * onehot[1]) + (c.z * onehot[2] + c.w * onehot[3]);
@@ -479,7 +446,7 @@ static hipError_t launch_mfma_ri(const uint16_t* x, const uint8_t* w, const uint
   const int gx = std::max(1, std::min(cu_count(), (nblk + kWaves - 1) / kWaves));
   const int bper = nblk / gx, brem = nblk - bper * gx;
   void* out = sk > 1 ? static_cast<void*>(ws) : static_cast<void*>(y);
-  hipLaunchKernelGGL((gemv_mfma_kernel<R, I, 1, kWaves, false>), dim3(gx, sk), dim3(64 * kWaves), 0, stream, x, w,
+  hipLaunchKernelGGL((gemv_mfma_kernel<R, I, 1, kWaves>), dim3(gx, sk), dim3(64 * kWaves), 0, stream, x, w,
                      s, out, N, K, gps, bper, brem);
   return hipGetLastError();
 }
