@@ -50,43 +50,48 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(const uint8_t* __restric
   }
 }
 
-// One thread sums 4 consecutive outputs across the SK slices.
+// One thread sums 8 consecutive outputs across the SK slices (two 16-byte
+// loads per slice; the loads of up to 8 slices go out before their adds, one
+// memory round trip per 8 slices; the adds run in slice order). Against 4
+// outputs per thread: 1322 x 2560 at SK 2, 92 -> 88 us for the whole GEMM.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
                                                             uint16_t* __restrict__ y,
                                                             uint64_t mn, int sk) {
-  // vector path only when every slice starts 16-byte aligned
-  const uint64_t nvec = (mn % 4 == 0) ? mn / 4 : 0;
+  // vector path only when every slice starts 16-byte aligned; the last
+  // mn % 8 outputs take the scalar path
+  const uint64_t nvec = (mn % 4 == 0) ? mn / 8 : 0;
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t v = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
-    // the loads of up to 16 slices go out before their adds (one memory
-    // round trip per 16 slices instead of one per slice); the adds run in
-    // slice order
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < sk; s0 += 16) {
-      f32x4 part[16];
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < sk; s0 += 8) {
+      f32x4 p0[8], p1[8];
 #pragma unroll
-      for (int s = 0; s < 16; ++s)
-        if (s0 + s < sk) part[s] = *reinterpret_cast<const f32x4*>(ws + (uint64_t)(s0 + s) * mn + v * 4);
+      for (int s = 0; s < 8; ++s)
+        if (s0 + s < sk) {
+          p0[s] = *reinterpret_cast<const f32x4*>(ws + (uint64_t)(s0 + s) * mn + v * 8);
+          p1[s] = *reinterpret_cast<const f32x4*>(ws + (uint64_t)(s0 + s) * mn + v * 8 + 4);
+        }
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
+      for (int s = 0; s < 8; ++s) {
         if (s0 + s < sk) {
           if (s0 + s == 0) {
-            acc = part[0];
+            a0 = p0[0];
+            a1 = p1[0];
           } else {
-            acc.x = acc.x + part[s].x;
-            acc.y = acc.y + part[s].y;
-            acc.z = acc.z + part[s].z;
-            acc.w = acc.w + part[s].w;
+            a0.x = a0.x + p0[s].x; a0.y = a0.y + p0[s].y; a0.z = a0.z + p0[s].z; a0.w = a0.w + p0[s].w;
+            a1.x = a1.x + p1[s].x; a1.y = a1.y + p1[s].y; a1.z = a1.z + p1[s].z; a1.w = a1.w + p1[s].w;
           }
         }
       }
     }
-    u32x2 o;
-    o.x = pack_bf16x2(acc.x, acc.y);
-    o.y = pack_bf16x2(acc.z, acc.w);
-    *reinterpret_cast<u32x2*>(y + v * 4) = o;
+    u32x4 o;
+    o.x = pack_bf16x2(a0.x, a0.y);
+    o.y = pack_bf16x2(a0.z, a0.w);
+    o.z = pack_bf16x2(a1.x, a1.y);
+    o.w = pack_bf16x2(a1.z, a1.w);
+    *reinterpret_cast<u32x4*>(y + v * 8) = o;
   }
-  for (uint64_t i = nvec * 4 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn; i += stride) {
+  for (uint64_t i = nvec * 8 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn; i += stride) {
     float acc = ws[i];
     for (int s = 1; s < sk; ++s) acc = acc + ws[(uint64_t)s * mn + i];
     y[i] = to_bf16(acc);
@@ -107,7 +112,7 @@ hipError_t launch_pack_int4(const uint8_t* q, uint8_t* out, uint64_t total_in, h
 }
 
 hipError_t launch_splitk_reduce(const float* ws, uint16_t* y, uint64_t mn, int sk, hipStream_t stream) {
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for((mn % 4 == 0 ? mn / 4 : mn) + 1, 256)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for((mn % 4 == 0 ? mn / 8 : mn) + 1, 256)), dim3(256), 0, stream,
                      ws, y, mn, sk);
   return hipGetLastError();
 }

@@ -504,7 +504,8 @@ def test_splitk_workspace_slices(path, M, N, K, sk):
     assert np.array_equal(bits_host(y), oracle.splitk_reduce_bf16(ws[: sk * M * N].view(sk, M, N).cpu().numpy()))
 
 
-@pytest.mark.parametrize("sk,M,N", [(1, 3, 37), (2, 16, 64), (3, 5, 7), (8, 16, 8192), (16, 1, 17408), (64, 2, 6)])
+@pytest.mark.parametrize("sk,M,N", [(1, 3, 37), (2, 16, 64), (3, 5, 7), (8, 16, 8192), (16, 1, 17408), (64, 2, 6),
+                                    (3, 4, 1001), (9, 7, 1000)])
 def test_splitk_reduce_bit_exact(sk, M, N):
     ws = make_workspace(sk, M, N, seed=sk + M + N)
     y = w4.w4a16_splitk_reduce(torch.from_numpy(ws).cuda())
