@@ -469,7 +469,34 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(args.y + (size_t)row0 * args.N, (uint32_t)rows * (uint32_t)args.N * 2u);
   const __amdgpu_buffer_rsrc_t rws =
       make_rsrc(args.ws + ((size_t)slice * args.M_total + row0) * args.N, (uint32_t)rows * (uint32_t)args.N * 4u);
-  if (args.ws == nullptr) {
+  // bf16 output of a full column tile with N % 8 == 0 (16-byte aligned rows
+  // of 8 columns): through LDS, so that every lane stores 16 bytes (8
+  // columns of one row) with 9x fewer store instructions than 2-byte stores
+  // of the 4 rows of one column a lane holds (1322 x 19456 x 2560: 140.5 ->
+  // 140.0 us; 8 x 256 x 2048 x 4096 batched: 46.9 -> 46.3 us). The wave's
+  // tile goes row-major into its own LDS region (the stages are free once
+  // every wave is past its last group), then back out as 16-byte rows.
+  if (args.ws == nullptr && ncols == kPN && args.N % 8 == 0) {
+    static_assert(kNW * BM * TN * 2 <= NSTAGE * ST::kBytes, "epilogue tile fits the stages' LDS");
+    __syncthreads();
+    uint8_t* wreg = lds + wv * (BM * TN * 2);
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+      for (int ns = 0; ns < SN; ++ns)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<uint16_t*>(wreg + (16 * ms + 4 * kb + i) * (TN * 2) + (16 * ns + m16) * 2) =
+              to_bf16(acc[ms][ns][i]);
+    // lane: row lane / 4 + 16 t, columns 8 (lane % 4) .. + 7 of the wave's 32;
+    // rows past the tile's last are past the buffer extent (dropped)
+#pragma unroll
+    for (int tt = 0; tt < MS; ++tt) {
+      const int r = (lane >> 2) + 16 * tt, c8 = lane & 3;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(wreg + r * (TN * 2) + c8 * 16);
+      st128(v, ry, ((uint32_t)r * (uint32_t)args.N + (uint32_t)(n0 + TN * wv + 8 * c8)) * 2u);
+    }
+  } else if (args.ws == nullptr) {
 #pragma unroll
     for (int ns = 0; ns < SN; ++ns) {
       const int ncol = TN * wv + 16 * ns + m16;
