@@ -79,6 +79,17 @@ GEMV_CASES = [
     (6000, 8192, 1, None),    # 1-row blocks of 64 groups (I = 4), rem varies
     (8192, 3584, 1, None),    # 28 groups: 4-row blocks of 7 instructions (one leftover per step)
     (8200, 3584, 1, None),
+    # two or more blocks per wave on average: the two-deep ring of register
+    # sets (one instance per block shape below 7 instructions)
+    (8192, 5120, 1, None),    # 2-row blocks, exactly 16 per workgroup (2 per wave)
+    (20000, 2560, 1, None),   # 4-row blocks of 5 instructions, 19 or 20 per workgroup
+    (17000, 1536, 1, None),   # 4-row blocks of 3 instructions
+    (16500, 512, 1, None),    # 4-row blocks of 1 instruction
+    (9000, 3072, 1, None),    # 2-row blocks of 3 instructions
+    (8400, 1024, 1, None),    # 2-row blocks of 1 instruction
+    (4400, 6144, 1, None),    # 1-row blocks of 3 instructions
+    (4500, 4096, 1, None),    # 1-row blocks of 2 instructions
+    (4200, 2048, 1, None),    # 1-row blocks of 1 instruction
     # the half-wave layout forced
     (17408, 5120, 1, 1),
     (1000, 1280, 1, 1),
