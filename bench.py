@@ -7,8 +7,10 @@ fp32 accumulation, bf16 output), reported as effective weight bandwidth:
 (N*K/2 packed bytes + N*K/128*2 scale bytes) per step / time per step.
 
 All inputs are synthetic (seeded, see synth/gen.py) and resident in HBM
-before the timed region, which is one graph replay of exactly K steps after
-W eager warm-up steps and untimed replays that let the GPU clocks settle. Weights and scales are rotated over enough copies
+before the timed region: W eager warm-up steps, then untimed graph replays
+of the K steps that let the GPU clocks settle, then exactly K eager steps
+between HIP events, enqueued behind enough untimed replays that the GPU runs
+them back to back. Weights and scales are rotated over enough copies
 (>= 512 MB) that the 256 MB Infinity Cache cannot serve them from one step
 to the next. The other workloads (small-batch split-K decode, deep prefill,
 grouped, batched, the four decoder GEMMs of a layer at M=1322 with group
@@ -40,6 +42,10 @@ ROTATE_BYTES = 512 << 20
 # GPU work run back to back before the timed replay (clock settling)
 SETTLE_S = 0.1
 SETTLE_MAX_S = 1.0
+# GPU work queued ahead of the timed eager steps, at least (see time_steps)
+LEAD_S = 0.02
+# host enqueue time per step assumed when there is no warmup to measure it
+HOST_STEP_GUESS_S = 100e-6
 # the decode GEMV at M=1, N=17408, K=5120, split_k 1 (40 groups per slice ->
 # 2-row blocks, 5 instructions per block; a two-deep ring of weight blocks per
 # wave; one 8-wave workgroup per compute unit, x in registers)
@@ -83,24 +89,33 @@ class Dev:
 
 
 def time_steps(step, steps, warmup, settle_s=SETTLE_S):
-    """W untimed eager warmup steps; then the K steps are captured once in a
-    HIP graph on a side stream (the library enqueues only kernels, so the
-    capture is exact) and replayed untimed, in chunks of about 20 ms of GPU
-    work, until at least `settle_s` seconds have run back to back and the
-    shader clock has settled: it has reached 95 % of its highest DPM level,
-    or stopped rising from one chunk to the next (under the decode GEMV's
-    load it climbs from idle for a few hundred milliseconds; under prefill's
-    it sinks to a power-limited level), at most SETTLE_MAX_S. The timed
-    region is then one replay of exactly K steps, between HIP events on that
-    stream, behind two untimed replays, all bracketed by synchronisations.
-    The shader and memory clocks are sampled while the settling replays run.
-    Returns (total seconds, seconds per step, clock record)."""
+    """W untimed eager warmup steps (their host enqueue time is measured);
+    then the K steps are captured once in a HIP graph on a side stream (the
+    library enqueues only kernels, so the capture is exact) and replayed
+    untimed, in chunks of about 20 ms of GPU work, until at least `settle_s`
+    seconds have run back to back and the shader clock has settled: it has
+    reached 95 % of its highest DPM level, or stopped rising from one chunk to
+    the next (under the decode GEMV's load it climbs from idle for a few
+    hundred milliseconds; under prefill's it sinks to a power-limited level),
+    at most SETTLE_MAX_S. The timed region is then exactly K eager calls of
+    the step, enqueued between two HIP events on that stream behind untimed
+    replays that keep the GPU busy for longer than the host takes to enqueue
+    them (at least LEAD_S, and three times the warmup's host enqueue time for
+    K steps): t0 .. t1 spans the K steps' GPU execution back to back, with no
+    host gap and no graph-launch boundary inside (a replay of a 20-step graph
+    carries several microseconds of launch cost of its own). All of it is
+    bracketed by synchronisations. The shader and memory clocks are sampled
+    while the settling replays run. Returns (total seconds, seconds per step,
+    record of clocks and of the lead)."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
+        h0 = time.perf_counter()
         for i in range(warmup):
             step(i)
+        # host enqueue time per step (first calls included: an overestimate)
+        h_step = (time.perf_counter() - h0) / warmup if warmup > 0 else HOST_STEP_GUESS_S
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
@@ -149,18 +164,26 @@ def time_steps(step, steps, warmup, settle_s=SETTLE_S):
                           sclk_samples=sum(r["sclk_samples"] for r in samples), mclk=samples[-1]["mclk"])
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
-        # two more untimed replays queued ahead of the first event keep the
-        # GPU under the same load (clocks as settled) and the host's
-        # submission of the timed graph out of the timed region: t0 .. t1
-        # spans exactly the K steps' GPU execution
-        g.replay()
-        g.replay()
+        # the lead: untimed replays queued ahead of the first event keep the
+        # GPU under the same load (clocks as settled) while the host enqueues
+        # the K timed calls
+        n_lead = max(1, int(math.ceil(max(LEAD_S, 3.0 * h_step * steps) / one)))
+        h1 = time.perf_counter()
+        for _ in range(n_lead):
+            g.replay()
         t0.record(s)
-        g.replay()
+        for i in range(steps):
+            step(i)
         t1.record(s)
+        host_s = time.perf_counter() - h1
         torch.cuda.synchronize()
     total = t0.elapsed_time(t1) / 1e3
-    clocks = dict(clocks or {}, settle_replays=n, settle_ms=round(settled_s * 1e3, 2))
+    clocks = dict(clocks or {}, settle_replays=n, settle_ms=round(settled_s * 1e3, 2),
+                  lead_ms=round(n_lead * one * 1e3, 2), host_enqueue_ms=round(host_s * 1e3, 2),
+                  host_ahead=bool(host_s < n_lead * one))
+    if not clocks["host_ahead"]:
+        log(f"time_steps: the host took {host_s * 1e3:.2f} ms to enqueue the lead and the {steps} timed steps, "
+            f"longer than the lead's {n_lead * one * 1e3:.2f} ms of GPU work: the GPU may have idled")
     return total, total / steps, clocks
 
 
@@ -384,7 +407,7 @@ def bench_pack(steps, warmup):
 def bench_dispatch(N, K, Ms, steps=20):
     """Path / tile height / split-K selection over M at one N x K: every
     explicit choice and the automatic one (split_k=0, no path), each
-    graph-timed over `steps` calls with rotated weight copies, in two passes
+    timed over `steps` calls (time_steps) with rotated weight copies, in two passes
     (forward, then reverse order, so that the drift of the clocks under load
     favours no candidate; the faster pass counts). One JSON line per M: the
     automatic choice (path, variant, SK) and its time, the best explicit
