@@ -44,6 +44,8 @@ SETTLE_S = 0.1
 SETTLE_MAX_S = 1.0
 # GPU work queued ahead of the timed eager steps, at least (see time_steps)
 LEAD_S = 0.02
+# untimed eager steps between the lead's replays and the timed steps
+LEAD_EAGER = 4
 # host enqueue time per step assumed when there is no warmup to measure it
 HOST_STEP_GUESS_S = 100e-6
 # the decode GEMV at M=1, N=17408, K=5120, split_k 1 (40 groups per slice ->
@@ -101,7 +103,7 @@ def time_steps(step, steps, warmup, settle_s=SETTLE_S):
     the step, enqueued between two HIP events on that stream behind untimed
     replays that keep the GPU busy for longer than the host takes to enqueue
     them (at least LEAD_S, and three times the warmup's host enqueue time for
-    K steps): t0 .. t1 spans the K steps' GPU execution back to back, with no
+    K steps), and behind LEAD_EAGER untimed eager steps: t0 .. t1 spans the K steps' GPU execution back to back, with no
     host gap and no graph-launch boundary inside (a replay of a 20-step graph
     carries several microseconds of launch cost of its own). All of it is
     bracketed by synchronisations. The shader and memory clocks are sampled
@@ -167,10 +169,14 @@ def time_steps(step, steps, warmup, settle_s=SETTLE_S):
         # the lead: untimed replays queued ahead of the first event keep the
         # GPU under the same load (clocks as settled) while the host enqueues
         # the K timed calls
-        n_lead = max(1, int(math.ceil(max(LEAD_S, 3.0 * h_step * steps) / one)))
+        n_lead = max(1, int(math.ceil(max(LEAD_S, 3.0 * h_step * (steps + LEAD_EAGER)) / one)))
         h1 = time.perf_counter()
         for _ in range(n_lead):
             g.replay()
+        # a few untimed eager steps after the replays: the switch from graph
+        # replays to eager launches stays out of the timed region
+        for i in range(LEAD_EAGER):
+            step(i)
         t0.record(s)
         for i in range(steps):
             step(i)
