@@ -479,7 +479,8 @@ def bench_dispatch(N, K, Ms, steps=20):
                  auto_explicit_us=round(twin[0], 2) if twin else None,
                  best=[best[0][0], best[0][2], round(best[1], 2)], auto_vs_best=round(auto_us / best[1], 3),
                  auto_tflops=round(2.0 * M * N * K / auto_us / 1e6, 1), auto_gbs=round(wb / auto_us / 1e3, 1),
-                 candidates=len(explicit))
+                 candidates=len(explicit),
+                 times={f"{n}:{sk}": round(v, 2) for (n, var, sk), v in sorted(explicit.items(), key=lambda kv: kv[1])})
         print(json.dumps(r), flush=True)
         out.append(r)
         del x, y

@@ -90,15 +90,26 @@ Path auto_path(int64_t M, int64_t N, int64_t K, int32_t sk) {
 // 144-row tile runs 20 groups in 48.7 us). One workgroup per compute unit:
 // a launch takes ceil(tiles x SK / CUs) rounds of (rows / rate) x groups per
 // slice. A split adds its fp32 partials, written by the tile kernel and read
-// by the reduce (8 x SK x M x N bytes at ≈5 TB/s) and the reduce launch
-// (≈2 us). Splits only where tiles x SK fit one round (a second, mostly idle
-// round of slices never pays: at M = 96..384, N x K = 17408 x 5120 doubling
-// past it cost 24-52 %).
-constexpr double kUnitUs = 0.0162, kReduceBytesPerUs = 5.0e6, kReduceLaunchUs = 2.0;
+// by the reduce (8 x SK x M x N bytes at ≈4 TB/s), the reduce launch (≈1 us)
+// and ≈1.5 us per 8 slices (the reduce has the loads of up to 8 slices in
+// flight before it adds them, so every 8 slices are one more round trip).
+// Splits only where tiles x SK fit one round (a second, mostly idle round of
+// slices never pays: at M = 96..384, N x K = 17408 x 5120 doubling past it
+// cost 24-52 %). The three split costs and the rates of the 48- to 80-row
+// tiles below were fitted to every explicit choice timed at 42 shapes (M
+// 64..4096; N x K 896..17408 x 2560..8192): the automatic choice is within
+// 1 % of the fastest at 41 of them and 5.6 % at the last (with the partials
+// at 5 TB/s, a 2 us launch and no per-8-slices term: 1.7 % on average, 10 %
+// at worst, by choosing SK 16 where 8 was faster), and the deep prefill,
+// grouped and batched workloads keep their choices.
+constexpr double kUnitUs = 0.0162, kReduceBytesPerUs = 4.0e6, kReduceLaunchUs = 1.0, kReduceBatchUs = 1.5;
 
 double tile_cost(int64_t M, int64_t N, int64_t Gk, int64_t tiles, int bm, double rate, int64_t sk, int64_t cus) {
   double c = (double)ceil_div(tiles * sk, cus) * bm / rate * (double)ceil_div(Gk, sk);
-  if (sk > 1) c += (8.0 * (double)sk * (double)M * (double)N / kReduceBytesPerUs + kReduceLaunchUs) / kUnitUs;
+  if (sk > 1)
+    c += (8.0 * (double)sk * (double)M * (double)N / kReduceBytesPerUs + kReduceLaunchUs +
+          (double)ceil_div(sk, 8) * kReduceBatchUs) /
+         kUnitUs;
   return c;
 }
 
@@ -122,11 +133,11 @@ int32_t tile_split_rate(int64_t M, int64_t N, int64_t Gk, int64_t tiles, int bm,
 // Per-row rates of the tile heights, relative to the 128-row tile (shorter
 // tiles amortise the per-group dequantisation and barrier over fewer rows;
 // at 1322 x 19456 x 2560 on one box: 4 rounds of 128 rows 166 us, 4 of 112
-// rows 161 us, 3 of 144 rows 146 us, 5 of 96 rows 176 us; 64 and 48 rows
-// measured at 40-64 rows of 17408 x 5120 and 8192 x 8192 against 80).
+// rows 161 us, 3 of 144 rows 146 us, 5 of 96 rows 176 us; the 80-, 64- and
+// 48-row rates fitted with the split costs above).
 struct TileCand { int bm; double rate; };
 constexpr TileCand kTileCands[] = {{128, 1.0}, {144, 0.96}, {112, 0.91}, {96, 0.907},
-                                   {80, 0.85}, {64, 0.70},  {48, 0.55}};
+                                   {80, 0.80}, {64, 0.66},  {48, 0.58}};
 
 double tile_rate(int bm) {
   for (const TileCand& c : kTileCands)

@@ -215,6 +215,11 @@ def test_auto_config_rule():
     assert ac(16, 896, 5120) == (2, 6, 8)            # 28 workgroups: split to fill the GPU
     path, rows, sk = ac(1322, 19456, 2560)
     assert (path, rows, sk) == (3, 144, 1)            # prefill: 144-row tiles, 3 rounds
+    # tile path at small M (measured against every explicit choice): 48-row
+    # tiles, SK 16 only while 16 slices' partials stay small
+    assert ac(64, 896, 5120) == (3, 48, 16)
+    assert ac(128, 896, 5120) == (3, 48, 8)
+    assert ac(64, 2048, 5120) == (3, 48, 8)
     assert ac(1322, 19456, 2560, 32)[0] == 3
     assert ac(1, 256, 512, 32)[0] == 3               # group 32 always on the tile kernel
     assert ac(0, 64, 128) == (0, -1, 0)              # nothing would run
