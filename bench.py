@@ -617,9 +617,9 @@ def main():
     wb = head["eff_weight_bytes"]
     ms_per_step = head["us_per_step"] / 1e3
     # dominant kernel of the step: the decode GEMV, one launch per step at
-    # split_k 1; its average launch duration is the graph replay time / K
-    # (HIP events on the launch stream), so it includes the dispatch gap
-    # between consecutive graph nodes
+    # split_k 1; its average launch duration is the timed region / K (HIP
+    # events on the launch stream around K back-to-back launches), so it
+    # includes the dispatch gap between consecutive launches
     kern_s = head["us_per_step"] / 1e6
     achieved = wb / kern_s / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
