@@ -161,12 +161,12 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
     return (uint32_t)(16 * QW * wv + wr) * K2 + 16u * (uint32_t)(wp ^ ((wr >> 1) & 3));
   };
 
-  // Row offsets always go into the vector offset, which the hardware range
-  // checks against the buffer extent (rows past the tile read zeros); the
-  // scalar offset only carries the group's k offset, which stays inside a row.
   // byte offset of a stage, kept in a scalar register: every LDS address of
   // the stage is then one add of it to a loop-invariant lane offset
   auto stage_off = [&](int stage) { return __builtin_amdgcn_readfirstlane((uint32_t)stage * (uint32_t)ST::kBytes); };
+  // Row offsets always go into the vector offset, which the hardware range
+  // checks against the buffer extent (rows past the tile read zeros); the
+  // scalar offset only carries the group's k offset, which stays inside a row.
   auto issue = [&](int g, int stage) {
     uint8_t* base = lds + stage_off(stage);
     // the group is the same in every lane; keeping its offsets scalar avoids
