@@ -70,6 +70,14 @@ __device__ __forceinline__ void st16(uint16_t v, __amdgpu_buffer_rsrc_t r, uint3
 // any multiple of 256 B; XOR by row & 7 or by row & 15 measured 2-way
 // conflicts (8 cycles). The block map is a permutation whose XOR with the
 // identity is one too.
+// Lanes of one wave exchanging data through LDS (each lane reads what other
+// lanes of its wave wrote): one wave's LDS instructions are executed in
+// program order, but the compiler, reasoning per lane, may move a lane's
+// reads above writes it can tell go elsewhere (and, across a loop, its next
+// writes above its reads). An empty asm with a memory clobber between the two
+// sides keeps them in program order.
+__device__ __forceinline__ void wave_lds_exchange() { asm volatile("" ::: "memory"); }
+
 __device__ __forceinline__ uint32_t xswz(int r) {
   return (uint32_t)((r & 3) | ((r >> 1) & 4) | ((((r >> 2) ^ (r >> 3)) & 1) << 3));
 }

@@ -503,6 +503,7 @@ __global__ __launch_bounds__(64 * kNW) void prefill_kernel(const PrefillArgs arg
         for (int i = 0; i < 4; ++i)
           *reinterpret_cast<uint16_t*>(wreg + (16 * ms + 4 * kb + i) * (TN * 2) + (16 * ns + m16) * 2) =
               to_bf16(acc[ms][ns][i]);
+    wave_lds_exchange();   // the rows below were written by other lanes
     // lane: row lane / 4 + 16 t, columns 8 (lane % 4) .. + 7 of the wave's 32;
     // rows past the tile's last are past the buffer extent (dropped)
 #pragma unroll

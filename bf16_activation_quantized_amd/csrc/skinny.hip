@@ -116,11 +116,13 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(const uint16_t* __re
   };
   auto compute = [&](const u32x4 (&xb)[XR], const u32x4 (&wb)[NT], const uint16_t (&sb)[NT]) {
     u32x4* xw = xst[wave];
+    wave_lds_exchange();   // after the previous group's reads of the tile
 #pragma unroll
     for (int j = 0; j < XR; ++j) {
       const int r = 4 * j + (lane >> 4), pc = lane & 15;
       xw[16 * r + (pc ^ (r & 15))] = xb[j];
     }
+    wave_lds_exchange();   // the pieces read below were written by other lanes
     if constexpr (MT == 1) {
       bf16x8 a[4];
 #pragma unroll
